@@ -1,0 +1,332 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of one sparse MoE layer's forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP path, and the HIP path never calls it.
+ *
+ * What it computes, token by token (every token is independent):
+ *   1. logits a[e] = sum_h x[h] * Wg[e][h], accumulated in double, rounded to
+ *      fp32 (the gate is computed in FP32: page "MAX 中 Step-3.5-Flash
+ *      架构解析…", section "MoE：共享专家、sigmoid 路由与激活裁剪", the
+ *      Step3p5MoEGate paragraph).
+ *   2. scores s[e] = sigmoid(a[e]) in fp32; corrected c[e] = s[e] + bias[e]
+ *      (fp32 add; the bias is a learnable fp32 per-expert vector, same
+ *      paragraph).
+ *   3. the k experts with the largest corrected score are selected, ordered
+ *      by (c descending, index ascending); NaN ranks below every number;
+ *      indices are clamped to [0, E-1] (same paragraph: top-k on corrected
+ *      scores, index clamp as a NaN/Inf guard).
+ *   4. the weight of a selected expert is its *raw* score s (not c); if
+ *      norm_expert_weight, the k weights are divided by their sum; they are
+ *      always multiplied by router_scaling_factor (same paragraph; the
+ *      config table gives norm_expert_weight and the 3.0 factor).
+ *   5. each selected expert e: g = W13[e][0:I] x, u = W13[e][I:2I] x,
+ *      h = act(g, u, L), y = W2[e] h (clipped SwiGLU on the concatenated
+ *      gate|up projection, same section; gate rows first is this oracle's
+ *      reading of "concatenated").
+ *   6. shared expert: y_sh = Ws2 act(Ws13 x, L_shared) (always-on MLP of
+ *      width share_expert_dim, same section).
+ *   7. out = sum_j w_j y_j + y_sh.
+ *
+ * act(g, u, L) = silu(g) * u when L == 0 (config table: limit 0 means no
+ * clipping); otherwise min(silu(g), L) * clamp(u, -L, L).  The pages only say
+ * the SwiGLU is "clipped" with a per-layer limit; clamping each factor is this
+ * oracle's reading.
+ *
+ * FP8 mode (routed experts stored as OCP E4M3FN codes with one fp32 scale per
+ * 128x128 weight block: miles page "Step-5-Preview", section 1 Model
+ * Introduction): the true weight is decode(q) * scale (the trainer's
+ * dequantisation on load).  The inputs of both routed projections (x, and h)
+ * are quantised per (row, 128-column group): s_a = amax / 448 (1 if amax is
+ * 0), q_a = E4M3FN_RNE_saturating(a / s_a), a' = decode(q_a) * s_a.  The pages
+ * do not say how activations meet FP8 weights; this dynamic per-group
+ * quantisation is the oracle's reading.  Router and shared expert stay bf16.
+ *
+ * Precision: inputs are bf16 (or E4M3 codes) / fp32; every dot product is
+ * accumulated in double and each intermediate tensor is rounded to fp32.
+ * Parity of this file is pinned by the CPU tests (closed forms, brute force,
+ * textbook special cases); see the test suite.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int32_t H, E, k, I, Is;
+    float scale;
+    int32_t norm;
+    float limit, limit_shared;
+    int32_t fp8;
+} orc_cfg;
+
+/* ---- scalar helpers --------------------------------------------------- */
+
+static float bf16_val(uint16_t v) {
+    uint32_t u = ((uint32_t)v) << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* OCP 8-bit floating point, E4M3FN flavour: 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+ * (m/8 * 2^-6); S.1111.111 is NaN; there are no infinities; largest finite
+ * magnitude is 1.75 * 2^8 = 448. */
+double orc_e4m3_decode(uint8_t code) {
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even, saturating encode: the finite code nearest to v;
+ * on an exact tie the code with an even mantissa (even code) wins; anything
+ * beyond 448 in magnitude becomes +-448; NaN maps to the NaN code. */
+uint8_t orc_e4m3_encode(float v) {
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7E;
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 0x7F; ++c) {          /* all non-negative finite codes */
+        double d = fabs(orc_e4m3_decode((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+double orc_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* clipped SwiGLU, see the header comment */
+double orc_act(double g, double u, double L) {
+    double sg = orc_silu(g);
+    if (L == 0.0) return sg * u;
+    if (sg > L) sg = L;
+    if (u > L) u = L;
+    if (u < -L) u = -L;
+    return sg * u;
+}
+
+/* per (row, 128-group) dynamic E4M3 quantise-dequantise of a fp32 row, in place */
+static void quant_row_fp8(float* a, int n) {
+    for (int g0 = 0; g0 < n; g0 += 128) {
+        float amax = 0.f;
+        for (int i = g0; i < g0 + 128 && i < n; ++i) {
+            float m = fabsf(a[i]);
+            if (m > amax) amax = m;
+        }
+        float sa = amax > 0.f ? amax / 448.0f : 1.0f;
+        for (int i = g0; i < g0 + 128 && i < n; ++i) {
+            float r = a[i] / sa;
+            a[i] = (float)orc_e4m3_decode(orc_e4m3_encode(r)) * sa;
+        }
+    }
+}
+
+/* "a ranks above b" for the top-k order: larger value first, NaN last,
+ * equal values -> lower index first */
+static int ranks_above(float ca, int ia, float cb, int ib) {
+    int na = isnan(ca), nb = isnan(cb);
+    if (na && nb) return ia < ib;
+    if (na) return 0;
+    if (nb) return 1;
+    if (ca > cb) return 1;
+    if (ca < cb) return 0;
+    return ia < ib;
+}
+
+/* ---- routing ------------------------------------------------------------ */
+
+static void route_token(const orc_cfg* c, const uint16_t* xt, const uint16_t* wg,
+                        const float* bias, int32_t* ids, float* w,
+                        float* logits_out, float* corr_out, float* s_buf, float* c_buf) {
+    const int H = c->H, E = c->E, k = c->k;
+    for (int e = 0; e < E; ++e) {
+        double acc = 0.0;
+        const uint16_t* we = wg + (size_t)e * H;
+        for (int h = 0; h < H; ++h) acc += (double)bf16_val(xt[h]) * (double)bf16_val(we[h]);
+        float a = (float)acc;
+        float s = (float)(1.0 / (1.0 + exp(-(double)a)));
+        s_buf[e] = s;
+        c_buf[e] = s + bias[e];
+        if (logits_out) logits_out[e] = a;
+        if (corr_out) corr_out[e] = c_buf[e];
+    }
+    /* selection: k rounds, each picks the best not yet chosen */
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || ranks_above(c_buf[e], e, c_buf[best], best)) best = e;
+        }
+        if (best < 0) best = 0;
+        if (best > E - 1) best = E - 1;
+        taken[best] = 1;
+        ids[j] = best;
+    }
+    free(taken);
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += (double)s_buf[ids[j]];
+    for (int j = 0; j < k; ++j) {
+        double v = (double)s_buf[ids[j]];
+        if (c->norm) v = (double)(float)(v / sum);
+        w[j] = (float)(v * (double)c->scale);
+    }
+}
+
+/* Route T tokens.  x [T,H] bf16, wg [E,H] bf16, bias [E] fp32 ->
+ * ids [T,k] int32, w [T,k] fp32; logits/corrected [T,E] fp32 if non-NULL. */
+int orc_route(const orc_cfg* c, int64_t T, const uint16_t* x, const uint16_t* wg,
+              const float* bias, int32_t* ids, float* w, float* logits, float* corrected) {
+    if (!c || c->k < 1 || c->k > c->E) return 1;
+#pragma omp parallel
+    {
+        float* s_buf = (float*)malloc(sizeof(float) * (size_t)c->E);
+        float* c_buf = (float*)malloc(sizeof(float) * (size_t)c->E);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < T; ++t)
+            route_token(c, x + t * c->H, wg, bias, ids + t * c->k, w + t * c->k,
+                        logits ? logits + t * c->E : NULL, corrected ? corrected + t * c->E : NULL,
+                        s_buf, c_buf);
+        free(s_buf);
+        free(c_buf);
+    }
+    return 0;
+}
+
+/* ---- expert MLPs --------------------------------------------------------- */
+
+/* weight element (row n, column kk) of a [N,K] matrix: bf16, or FP8 code x
+ * the fp32 scale of its 128x128 block */
+static float wval(const void* W, const float* Ws, int K, int n, int kk, int fp8) {
+    if (!fp8) return bf16_val(((const uint16_t*)W)[(size_t)n * K + kk]);
+    uint8_t q = ((const uint8_t*)W)[(size_t)n * K + kk];
+    float s = Ws[(size_t)(n / 128) * (K / 128) + kk / 128];
+    return (float)orc_e4m3_decode(q) * s;
+}
+
+/* y[H] = W2 act(W13 xin, L), xin fp32 [H]; W13 [2N,H], W2 [H,N] */
+static void mlp(const orc_cfg* c, int N, const float* xin, const void* W13, const float* S13,
+                const void* W2, const float* S2, float L, int fp8, float* hbuf, float* y) {
+    const int H = c->H;
+    for (int i = 0; i < N; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int h = 0; h < H; ++h) {
+            g += (double)wval(W13, S13, H, i, h, fp8) * (double)xin[h];
+            u += (double)wval(W13, S13, H, N + i, h, fp8) * (double)xin[h];
+        }
+        float gf = (float)g, uf = (float)u;
+        hbuf[i] = (float)orc_act((double)gf, (double)uf, (double)L);
+    }
+    if (fp8) quant_row_fp8(hbuf, N);
+    for (int o = 0; o < H; ++o) {
+        double acc = 0.0;
+        for (int i = 0; i < N; ++i) acc += (double)wval(W2, S2, N, o, i, fp8) * (double)hbuf[i];
+        y[o] = (float)acc;
+    }
+}
+
+/*
+ * Full layer for n tokens (rows tok[0..n-1] of x, or 0..n-1 if tok is NULL).
+ * out [n,H] fp32; ids [n,k]; w [n,k]; y_routed [n,k,H] and y_shared [n,H]
+ * (fp32, optional) expose the per-expert outputs for the tests.
+ * w13: [E,2I,H] bf16 or E4M3 codes; w13s [E,2I/128,H/128] (FP8 only);
+ * w2: [E,H,I]; w2s [E,H/128,I/128]; ws13 [2Is,H] bf16; ws2 [H,Is] bf16.
+ */
+int orc_layer(const orc_cfg* c, int64_t n, const int64_t* tok, const uint16_t* x,
+              const uint16_t* wg, const float* bias, const void* w13, const float* w13s,
+              const void* w2, const float* w2s, const uint16_t* ws13, const uint16_t* ws2,
+              float* out, int32_t* ids, float* w, float* y_routed, float* y_shared) {
+    if (!c || c->k < 1 || c->k > c->E) return 1;
+    const int H = c->H, E = c->E, k = c->k, I = c->I, Is = c->Is;
+    const size_t esz = c->fp8 ? 1 : 2;
+    int err = 0;
+#pragma omp parallel
+    {
+        float* s_buf = (float*)malloc(sizeof(float) * (size_t)E);
+        float* c_buf = (float*)malloc(sizeof(float) * (size_t)E);
+        float* xin = (float*)malloc(sizeof(float) * (size_t)H);
+        float* xq = (float*)malloc(sizeof(float) * (size_t)H);
+        int hmax = I > Is ? I : Is;
+        float* hbuf = (float*)malloc(sizeof(float) * (size_t)(hmax > 0 ? hmax : 1));
+        float* y = (float*)malloc(sizeof(float) * (size_t)H);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t t = tok ? tok[r] : r;
+            const uint16_t* xt = x + t * H;
+            int32_t* id = ids + r * k;
+            float* wt = w + r * k;
+            route_token(c, xt, wg, bias, id, wt, NULL, NULL, s_buf, c_buf);
+            for (int h = 0; h < H; ++h) xin[h] = bf16_val(xt[h]);
+            memcpy(xq, xin, sizeof(float) * (size_t)H);
+            if (c->fp8) quant_row_fp8(xq, H);
+            for (int h = 0; h < H; ++h) acc[h] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                int e = id[j];
+                const char* W13e = (const char*)w13 + (size_t)e * 2 * I * H * esz;
+                const char* W2e = (const char*)w2 + (size_t)e * H * I * esz;
+                const float* S13 = c->fp8 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : NULL;
+                const float* S2 = c->fp8 ? w2s + (size_t)e * (H / 128) * (I / 128) : NULL;
+                mlp(c, I, xq, W13e, S13, W2e, S2, c->limit, c->fp8, hbuf, y);
+                if (y_routed) memcpy(y_routed + (r * k + j) * H, y, sizeof(float) * (size_t)H);
+                for (int h = 0; h < H; ++h) acc[h] += (double)wt[j] * (double)y[h];
+            }
+            if (Is > 0) {
+                mlp(c, Is, xin, ws13, NULL, ws2, NULL, c->limit_shared, 0, hbuf, y);
+                if (y_shared) memcpy(y_shared + r * H, y, sizeof(float) * (size_t)H);
+                for (int h = 0; h < H; ++h) acc[h] += (double)y[h];
+            } else if (y_shared) {
+                memset(y_shared + r * H, 0, sizeof(float) * (size_t)H);
+            }
+            for (int h = 0; h < H; ++h) out[r * H + h] = (float)acc[h];
+        }
+        free(s_buf); free(c_buf); free(xin); free(xq); free(hbuf); free(y); free(acc);
+    }
+    return err;
+}
+
+/* Per-expert token counts and the expert-major, token-ascending row order of
+ * the (token, slot) pairs: the plain definition of the permutation.
+ * ids [T,k] -> counts [E], offsets [E+1] (exclusive prefix sum),
+ * row_to_pair [T*k] (row r holds pair p = t*k + j), pair_to_row [T*k]. */
+int orc_permute(int64_t T, int32_t k, int32_t E, const int32_t* ids, int32_t* counts,
+                int32_t* offsets, int32_t* row_to_pair, int32_t* pair_to_row) {
+    const int64_t P = T * k;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        if (ids[p] < 0 || ids[p] >= E) return 1;
+        counts[ids[p]]++;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    for (int64_t p = 0; p < P; ++p) {      /* pairs in ascending order -> stable */
+        int e = ids[p];
+        int32_t r = offsets[e] + fill[e]++;
+        row_to_pair[r] = (int32_t)p;
+        pair_to_row[p] = r;
+    }
+    free(fill);
+    return 0;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

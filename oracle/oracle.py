@@ -1,0 +1,176 @@
+"""Python access to the CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the HIP path.  The functions take numpy
+arrays or CPU torch tensors (bf16 tensors are passed as their raw 16-bit
+patterns) and return numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("Is", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("norm", ctypes.c_int32), ("limit", ctypes.c_float),
+                ("limit_shared", ctypes.c_float), ("fp8", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        L.orc_route.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P]
+        L.orc_layer.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P,
+                                P, P, P, P, P, P, P]
+        L.orc_permute.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_act.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        L.orc_act.restype = ctypes.c_double
+        L.orc_silu.argtypes = [ctypes.c_double]
+        L.orc_silu.restype = ctypes.c_double
+        L.orc_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _cfg(cfg) -> _Cfg:
+    return _Cfg(cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size,
+                cfg.share_expert_dim, float(cfg.router_scaling_factor), int(bool(cfg.norm_expert_weight)),
+                float(cfg.swiglu_limit), float(cfg.swiglu_limit_shared),
+                int(cfg.expert_dtype == "fp8"))
+
+
+def _np(a, dtype=None):
+    """CPU numpy view of a tensor/array; bf16 becomes its uint16 bit pattern."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous()
+            if a.dtype == torch.bfloat16:
+                a = a.view(torch.int16)
+            a = a.numpy()
+            if a.dtype == np.int16:
+                a = a.view(np.uint16)
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(a)
+    if dtype is not None:
+        assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def route(cfg, x, w_router, router_bias, want_scores=False):
+    """Routing of every token: ids [T,k] int32, weights [T,k] fp32
+    (+ logits, corrected scores [T,E] fp32 when want_scores)."""
+    x = _np(x, np.uint16)
+    wg = _np(w_router, np.uint16)
+    b = _np(router_bias, np.float32)
+    T = x.shape[0]
+    E, k = cfg.num_experts, cfg.top_k
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float32)
+    lg = np.zeros((T, E), np.float32) if want_scores else None
+    cs = np.zeros((T, E), np.float32) if want_scores else None
+    c = _cfg(cfg)
+    rc = lib().orc_route(ctypes.byref(c), T, _p(x), _p(wg), _p(b), _p(ids), _p(w), _p(lg), _p(cs))
+    assert rc == 0, rc
+    if want_scores:
+        return ids, w, lg, cs
+    return ids, w
+
+
+def layer(cfg, inp, tokens=None, want_parts=False):
+    """Layer output for the given token rows (all rows if tokens is None).
+
+    inp holds the tensors of ``moe_inputs.make_inputs``.  Returns a dict with
+    out [n,H] fp32, ids [n,k], w [n,k] and, if want_parts, y_routed [n,k,H]
+    and y_shared [n,H]."""
+    x = _np(inp["x"], np.uint16)
+    T = x.shape[0]
+    tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    n = T if tok is None else tok.shape[0]
+    fp8 = cfg.expert_dtype == "fp8"
+    H, k, Is = cfg.hidden_size, cfg.top_k, cfg.share_expert_dim
+    wg = _np(inp["w_router"], np.uint16)
+    b = _np(inp["router_bias"], np.float32)
+    w13 = _np(inp["w13"], np.uint8 if fp8 else np.uint16)
+    w2 = _np(inp["w2"], np.uint8 if fp8 else np.uint16)
+    w13s = _np(inp["w13_scale"], np.float32) if fp8 else None
+    w2s = _np(inp["w2_scale"], np.float32) if fp8 else None
+    ws13 = _np(inp["ws13"], np.uint16) if Is > 0 else None
+    ws2 = _np(inp["ws2"], np.uint16) if Is > 0 else None
+    out = np.zeros((n, H), np.float32)
+    ids = np.zeros((n, k), np.int32)
+    w = np.zeros((n, k), np.float32)
+    yr = np.zeros((n, k, H), np.float32) if want_parts else None
+    ys = np.zeros((n, H), np.float32) if want_parts else None
+    c = _cfg(cfg)
+    rc = lib().orc_layer(ctypes.byref(c), n, _p(tok), _p(x), _p(wg), _p(b), _p(w13), _p(w13s),
+                         _p(w2), _p(w2s), _p(ws13), _p(ws2), _p(out), _p(ids), _p(w), _p(yr), _p(ys))
+    assert rc == 0, rc
+    res = {"out": out, "ids": ids, "w": w}
+    if want_parts:
+        res["y_routed"], res["y_shared"] = yr, ys
+    return res
+
+
+def permute(ids, num_experts):
+    """Counts, offsets, row_to_pair and pair_to_row for the given routing."""
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    T, k = ids.shape
+    counts = np.zeros(num_experts, np.int32)
+    offs = np.zeros(num_experts + 1, np.int32)
+    r2p = np.zeros(T * k, np.int32)
+    p2r = np.zeros(T * k, np.int32)
+    rc = lib().orc_permute(T, k, num_experts, _p(ids), _p(counts), _p(offs), _p(r2p), _p(p2r))
+    assert rc == 0, rc
+    return counts, offs, r2p, p2r
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(v)
+
+
+def act(g: float, u: float, limit: float) -> float:
+    return lib().orc_act(g, u, limit)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()

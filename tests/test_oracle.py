@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test pins one part of the layer (routing, activation, expert MLP, combine,
+permutation, FP8 codec) to a closed form, a page-printed number, a brute-force
+second implementation, or a library routine (torch.nn.functional, torch's
+float8 cast, numpy's stable sort) that reduces to the same definition.
+"""
+import dataclasses
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import moe_inputs as mi
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf(a):
+    return torch.as_tensor(a, dtype=torch.float32).to(torch.bfloat16)
+
+
+def tiny(**over):
+    return mi.workload("tiny", **over)
+
+
+# --------------------------------------------------------------------------
+# page-printed facts
+
+
+def test_page_facts_fix_the_configs():
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    s35 = facts["step35_config"]
+    c1 = mi.WORKLOADS["step35_prefill"].cfg
+    assert (c1.num_experts, c1.top_k, c1.moe_intermediate_size, c1.share_expert_dim) == (
+        s35["moe_num_experts"], s35["moe_top_k"], s35["moe_intermediate_size"], s35["share_expert_dim"])
+    assert c1.router_scaling_factor == s35["moe_router_scaling_factor"]
+    assert c1.norm_expert_weight == s35["norm_expert_weight"]
+    s5 = facts["step5_architecture"]
+    for name in ("step5_prefill", "step5_decode", "step5_fp8_prefill"):
+        c = mi.WORKLOADS[name].cfg
+        assert (c.hidden_size, c.num_experts, c.top_k, c.moe_intermediate_size, c.share_expert_dim) == (
+            s5["hidden_size"], s5["routed_experts"], s5["top_k"], s5["expert_intermediate_size"],
+            s5["shared_intermediate_size"])
+        assert c.router_scaling_factor == facts["step5_routing"]["router_scaling_factor"]
+
+
+def test_step35_hidden_size_follows_from_parameter_counts():
+    """Expert parameters = (total - per_rank) * ep / (ep - 1); they are
+    n_moe_layers * E * 3 * H * I, which fixes H = 4096 exactly."""
+    f = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    pc, cfg, lay = f["step35_param_counts"], f["step35_config"], f["step35_layers"]
+    ep = pc["ep"]
+    diff = pc["total_parameters"] - pc["per_rank_parameters_ep8"]
+    assert diff * ep % (ep - 1) == 0
+    expert_params = diff * ep // (ep - 1)
+    n_layers = lay["moe_layer_last"] - lay["moe_layer_first"] + 1
+    per_h = n_layers * cfg["moe_num_experts"] * 3 * cfg["moe_intermediate_size"]
+    assert expert_params % per_h == 0
+    assert expert_params // per_h == 4096 == mi.WORKLOADS["step35_prefill"].cfg.hidden_size
+
+
+def test_step5_expert_tensor_sizes_match_fused_layout():
+    """The 12 and 24 MiB bf16 expert tensors are one expert's [H, I] down
+    projection and fused [2I, H] gate|up projection."""
+    f = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    H, I = f["step5_architecture"]["hidden_size"], f["step5_architecture"]["expert_intermediate_size"]
+    assert sorted(f["step5_routing"]["fp8_expert_tensor_mib"]) == [H * I * 2 // 2**20, 2 * I * H * 2 // 2**20]
+
+
+# --------------------------------------------------------------------------
+# activation: closed-form scalars
+
+
+@pytest.mark.parametrize("g,u,L,want", [
+    (10.0, 10.0, 7.0, 49.0),                       # both factors clip
+    (10.0, -10.0, 7.0, -49.0),                     # up clips from below
+    (-10.0, 100.0, 7.0, 7.0 * -4.539786870243442e-04),  # silu(-10) * 7
+    (1.0, 2.0, 7.0, 2.0 * 0.7310585786300049),    # nothing clips: 2 * silu(1)
+    (1.0, 2.0, 0.0, 2.0 * 0.7310585786300049),
+    (0.0, 5.0, 7.0, 0.0),
+    (20.0, 3.0, 0.0, 60.0 * 0.9999999979388463),   # L = 0: no clip at all
+])
+def test_act_closed_forms(orc, g, u, L, want):
+    assert orc.act(g, u, L) == pytest.approx(want, rel=1e-12, abs=1e-15)
+
+
+def test_silu_closed_forms(orc):
+    assert orc.lib().orc_silu(0.0) == 0.0
+    assert orc.lib().orc_silu(1.0) == pytest.approx(0.7310585786300049, rel=1e-15)
+    assert orc.lib().orc_silu(-1.0) == pytest.approx(-0.2689414213699951, rel=1e-15)
+
+
+def test_act_limit_zero_is_unclipped(orc):
+    rng = np.random.default_rng(0)
+    for g, u in rng.normal(0, 30, (200, 2)):
+        want = float(F.silu(torch.tensor(g, dtype=torch.float64)) * u)
+        assert orc.act(g, u, 0.0) == pytest.approx(want, rel=1e-13, abs=1e-13)
+
+
+# --------------------------------------------------------------------------
+# routing
+
+
+def _inputs(wl, seed=0):
+    return mi.make_inputs(wl, "cpu", seed)
+
+
+def test_route_zero_input_picks_largest_bias(orc):
+    """x = 0 -> logits 0 -> s = 0.5 -> c = 0.5 + b: the ids are the k largest
+    biases; weights are scale/k with normalisation, scale*0.5 without."""
+    wl = tiny()
+    inp = _inputs(wl)
+    x = torch.zeros_like(inp["x"])
+    b = inp["router_bias"]
+    ids, w = orc.route(wl.cfg, x, inp["w_router"], b)
+    k = wl.cfg.top_k
+    want = sorted(range(wl.cfg.num_experts), key=lambda e: (-float(b[e]), e))[:k]
+    assert (ids == np.array(want, np.int32)[None, :]).all()
+    assert np.allclose(w, 3.0 / k, rtol=0, atol=1e-7)
+    cfg_nonorm = dataclasses.replace(wl.cfg, norm_expert_weight=False)
+    _, w2 = orc.route(cfg_nonorm, x, inp["w_router"], b)
+    assert np.allclose(w2, 1.5, rtol=0, atol=0)
+
+
+def test_route_ties_go_to_lower_index(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    x = torch.zeros_like(inp["x"])
+    ids, _ = orc.route(wl.cfg, x, inp["w_router"], torch.zeros(wl.cfg.num_experts))
+    assert (ids == np.arange(wl.cfg.top_k, dtype=np.int32)[None, :]).all()
+    # duplicate router rows give exactly equal scores: the lower index wins
+    wg = inp["w_router"].clone()
+    wg[9] = wg[3]
+    b = torch.zeros(wl.cfg.num_experts)
+    b[3] = b[9] = 5.0
+    ids, _ = orc.route(wl.cfg, inp["x"], wg, b)
+    assert (ids[:, 0] == 3).all() and (ids[:, 1] == 9).all()
+
+
+def test_route_weights_sum_to_scale(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    ids, w = orc.route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"])
+    assert np.abs(w.astype(np.float64).sum(1) - 3.0).max() < 1e-6
+    assert all(len(set(r)) == wl.cfg.top_k for r in ids.tolist())
+
+
+def test_route_matches_full_sort_of_fp64_scores(orc):
+    """Brute force: score every expert in double precision with torch, sort
+    all E of them, keep the first k (ties to the lower index)."""
+    wl = tiny()
+    inp = _inputs(wl)
+    ids, w, lg, cs = orc.route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"], want_scores=True)
+    logits = inp["x"].double() @ inp["w_router"].double().T
+    s = torch.sigmoid(logits)
+    c = s + inp["router_bias"].double()
+    assert np.allclose(lg, logits.numpy(), rtol=1e-6, atol=1e-6)
+    for t in range(wl.T):
+        order = sorted(range(wl.cfg.num_experts), key=lambda e: (-float(c[t, e]), e))
+        srt = sorted(float(v) for v in c[t])[::-1]
+        gap = srt[wl.cfg.top_k - 1] - srt[wl.cfg.top_k]
+        if gap > 1e-6:
+            assert sorted(ids[t].tolist()) == sorted(order[:wl.cfg.top_k])
+            assert ids[t].tolist() == order[:wl.cfg.top_k]       # descending order too
+        sw = s[t, ids[t]]
+        assert np.allclose(w[t], (3.0 * sw / sw.sum()).numpy(), rtol=1e-6)
+
+
+def test_route_nan_inf_guard(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    x = inp["x"].clone()
+    x[0] = float("nan")
+    x[1, 5] = float("inf")
+    x[2, :] = float("-inf")
+    wg = inp["w_router"].clone()
+    wg[7, 3] = float("nan")
+    ids, _ = orc.route(wl.cfg, x, wg, inp["router_bias"])
+    assert ids.min() >= 0 and ids.max() < wl.cfg.num_experts
+    assert ids[0].tolist() == list(range(wl.cfg.top_k))      # every score NaN -> lowest indices
+    for r in ids.tolist():
+        assert len(set(r)) == wl.cfg.top_k
+
+
+# --------------------------------------------------------------------------
+# expert MLPs and combine against torch library routines
+
+
+def _torch_mlp(x, w13, w2, L):
+    """Textbook SwiGLU MLP in float64 with torch: F.linear + F.silu."""
+    I = w2.shape[1]
+    gu = F.linear(x.double(), w13.double())
+    g, u = gu[..., :I], gu[..., I:]
+    sg = F.silu(g)
+    if L:
+        sg = sg.clamp(max=L)
+        u = u.clamp(-L, L)
+    return F.linear(sg * u, w2.double())
+
+
+def test_single_expert_is_textbook_swiglu(orc):
+    wl = tiny(num_experts=1, top_k=1, share_expert_dim=0, router_scaling_factor=1.0, swiglu_limit=0.0)
+    inp = _inputs(wl)
+    res = orc.layer(wl.cfg, inp)
+    want = _torch_mlp(inp["x"], inp["w13"][0], inp["w2"][0], 0.0).numpy()
+    assert (res["ids"] == 0).all() and np.allclose(res["w"], 1.0)
+    assert np.abs(res["out"] - want).max() <= 1e-5 * np.abs(want).max()
+
+
+def test_identical_experts_give_scaled_mlp_plus_shared(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    inp["w13"][:] = inp["w13"][0]
+    inp["w2"][:] = inp["w2"][0]
+    res = orc.layer(wl.cfg, inp)
+    want = 3.0 * _torch_mlp(inp["x"], inp["w13"][0], inp["w2"][0], wl.cfg.swiglu_limit) + \
+        _torch_mlp(inp["x"], inp["ws13"], inp["ws2"], wl.cfg.swiglu_limit_shared)
+    assert np.abs(res["out"] - want.numpy()).max() <= 1e-5 * np.abs(want.numpy()).max()
+
+
+def test_output_is_the_explicit_sum_over_chosen_experts(orc):
+    wl = tiny(x_scale=40.0)      # clip stress: many SwiGLU inputs beyond the limit
+    inp = _inputs(wl)
+    res = orc.layer(wl.cfg, inp, want_parts=True)
+    x = inp["x"]
+    ref = _torch_mlp(x, inp["ws13"], inp["ws2"], wl.cfg.swiglu_limit_shared)
+    assert np.abs(res["y_shared"] - ref.numpy()).max() <= 1e-5 * ref.abs().max().item()
+    out = ref.clone()
+    for t in range(wl.T):
+        for j, e in enumerate(res["ids"][t].tolist()):
+            y = _torch_mlp(x[t], inp["w13"][e], inp["w2"][e], wl.cfg.swiglu_limit)
+            assert np.abs(res["y_routed"][t, j] - y.numpy()).max() <= 1e-5 * y.abs().max().item()
+            out[t] += float(res["w"][t, j]) * y
+    assert np.abs(res["out"] - out.numpy()).max() <= 1e-5 * out.abs().max().item()
+
+
+def test_clip_stress_actually_clips(orc):
+    """At limit 7 with activations x40 a large share of gate/up values is
+    beyond the limit, so the stress case exercises the clip branch."""
+    wl = tiny(x_scale=40.0)
+    inp = _inputs(wl)
+    gu = F.linear(inp["x"].double(), inp["w13"][0].double())
+    frac = (gu.abs() > wl.cfg.swiglu_limit).double().mean().item()
+    assert frac > 0.2
+
+
+def test_output_linear_in_scaling_factor(orc):
+    wl3 = tiny(share_expert_dim=0)
+    wl1 = tiny(share_expert_dim=0, router_scaling_factor=1.0)
+    inp = _inputs(wl3)
+    o3 = orc.layer(wl3.cfg, inp)["out"].astype(np.float64)
+    o1 = orc.layer(wl1.cfg, inp)["out"].astype(np.float64)
+    assert np.abs(o3 - 3.0 * o1).max() <= 1e-6 * np.abs(o3).max()
+
+
+def test_token_subset_equals_full_rows(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    full = orc.layer(wl.cfg, inp)
+    sub = orc.layer(wl.cfg, inp, tokens=[5, 17, 63])
+    assert np.array_equal(sub["out"], full["out"][[5, 17, 63]])
+    assert np.array_equal(sub["ids"], full["ids"][[5, 17, 63]])
+
+
+@pytest.mark.parametrize("x_scale", [1.0, 40.0])
+def test_oracle_matches_brute_force(orc, x_scale):
+    wl = tiny(x_scale=x_scale)
+    inp = _inputs(wl)
+    toks = [0, 1, 2, 31, 62, 63]
+    res = orc.layer(wl.cfg, inp, tokens=toks)
+    f = lambda t: t.double().tolist()
+    x = f(inp["x"])
+    args = (f(inp["w_router"]), f(inp["router_bias"]), f(inp["w13"]), f(inp["w2"]), f(inp["ws13"]), f(inp["ws2"]))
+    for r, t in enumerate(toks):
+        ids, w, out, c = brute.token_forward(wl.cfg, x[t], *args)
+        srt = sorted(c, reverse=True)
+        if srt[wl.cfg.top_k - 1] - srt[wl.cfg.top_k] > 1e-6:
+            assert res["ids"][r].tolist() == ids
+        out = np.array(out)
+        assert np.abs(res["out"][r] - out).max() <= 1e-5 * np.abs(out).max()
+        assert np.allclose(res["w"][r], w, rtol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# permutation
+
+
+def test_permute_matches_stable_sort(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    ids, _ = orc.route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"])
+    E = wl.cfg.num_experts
+    counts, offs, r2p, p2r = orc.permute(ids, E)
+    flat = ids.reshape(-1)
+    assert counts.sum() == flat.size
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert offs[0] == 0 and np.array_equal(np.diff(offs), counts)
+    assert np.array_equal(r2p, np.argsort(flat, kind="stable"))      # library stable sort
+    assert np.array_equal(p2r[r2p], np.arange(flat.size))
+    for e in range(E):
+        seg = r2p[offs[e]:offs[e + 1]]
+        assert (flat[seg] == e).all() and (np.diff(seg) > 0).all()
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3FN codec and the FP8 layer
+
+
+def test_e4m3_decode_all_codes_against_torch(orc):
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double()
+    for code in range(256):
+        v = orc.e4m3_decode(code)
+        if math.isnan(ref[code]):
+            assert math.isnan(v) and code in (0x7F, 0xFF)
+        else:
+            assert v == ref[code].item(), code
+    assert orc.e4m3_decode(0x7E) == 448.0 and orc.e4m3_decode(0x01) == 2.0 ** -9
+
+
+def test_e4m3_encode_rne_against_torch(orc):
+    finite = sorted({orc.e4m3_decode(c) for c in range(0x7F)})
+    mids = [(a + b) / 2 for a, b in zip(finite[:-1], finite[1:])]
+    rng = np.random.default_rng(1)
+    vals = finite + mids + list(rng.uniform(-448, 448, 3000)) + list(rng.normal(0, 0.01, 1000))
+    vals = [float(np.float32(v)) for v in vals]
+    vals += [-v for v in vals]
+    ref = torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+    got = [orc.e4m3_encode(v) for v in vals]
+    assert got == ref.tolist()
+    # saturation beyond the finite range (torch's cast gives NaN there)
+    assert orc.e4m3_encode(500.0) == 0x7E and orc.e4m3_encode(-1e9) == 0xFE
+    assert orc.e4m3_encode(float("nan")) == 0x7F
+
+
+def _torch_fp8_reference(cfg, inp, ids, w):
+    """The FP8-mode layer with torch's own float8 cast and matmuls."""
+    def deq_w(codes, scale):
+        v = codes.view(torch.float8_e4m3fn).double()
+        return v * scale.double().repeat_interleave(128, 0).repeat_interleave(128, 1)
+
+    def quant_act(a):
+        a = a.float()
+        g = a.reshape(*a.shape[:-1], -1, 128)
+        amax = g.abs().amax(-1, keepdim=True)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (g / s).to(torch.float8_e4m3fn).float()
+        return (q * s).reshape(a.shape)
+
+    I, L = cfg.moe_intermediate_size, cfg.swiglu_limit
+    xq = quant_act(inp["x"].float()).double()
+    out = _torch_mlp(inp["x"], inp["ws13"], inp["ws2"], cfg.swiglu_limit_shared)
+    for t in range(xq.shape[0]):
+        for j, e in enumerate(ids[t].tolist()):
+            gu = F.linear(xq[t], deq_w(inp["w13"][e], inp["w13_scale"][e]))
+            gu = gu.float().double()
+            sg, u = F.silu(gu[:I]), gu[I:]
+            if L:
+                sg, u = sg.clamp(max=L), u.clamp(-L, L)
+            h = quant_act((sg * u).float()).double()
+            out[t] += float(w[t, j]) * F.linear(h, deq_w(inp["w2"][e], inp["w2_scale"][e]))
+    return out
+
+
+def test_fp8_layer_matches_torch_float8_reference(orc):
+    wl = mi.workload("tiny", hidden_size=256, moe_intermediate_size=128, expert_dtype="fp8", T=8)
+    inp = _inputs(wl)
+    res = orc.layer(wl.cfg, inp)
+    want = _torch_fp8_reference(wl.cfg, inp, res["ids"], res["w"]).numpy()
+    # activation codes can differ by one step where fp32 and fp64 disagree on
+    # a rounding midpoint; the bound covers a handful of such flips
+    assert np.abs(res["out"] - want).max() <= 1e-3 * np.abs(want).max()
+    assert np.sqrt(((res["out"] - want) ** 2).mean()) <= 1e-5 * np.abs(want).max()
+
+
+def test_fp8_exact_values_equal_bf16_path(orc):
+    """With unit block scales, integer weights and activations that quantise
+    exactly (x = 1, gate/up rows of ones so that with limit 1 every h is
+    exactly 1), the FP8 layer equals the bf16 layer up to the fp32 rounding
+    of 1/448 in the activation scale."""
+    base = dict(num_experts=1, top_k=1, share_expert_dim=0, router_scaling_factor=1.0,
+                swiglu_limit=1.0, hidden_size=256, moe_intermediate_size=128, T=4)
+    wl16 = mi.workload("tiny", **base)
+    wl8 = mi.workload("tiny", expert_dtype="fp8", **base)
+    inp = _inputs(wl16)
+    rng = np.random.default_rng(3)
+    x = torch.ones(4, 256)
+    w13 = torch.ones(1, 256, 256)
+    w2 = torch.tensor(rng.integers(-1, 2, (1, 256, 128)), dtype=torch.float32)
+    r16 = orc.layer(wl16.cfg, dict(inp, x=x.bfloat16(), w13=w13.bfloat16(), w2=w2.bfloat16()))
+    f8 = lambda t: t.to(torch.float8_e4m3fn).view(torch.uint8)
+    r8 = orc.layer(wl8.cfg, dict(inp, x=x.bfloat16(), w13=f8(w13), w2=f8(w2),
+                                 w13_scale=torch.ones(1, 2, 2), w2_scale=torch.ones(1, 2, 1)))
+    want = w2[0].sum(-1).numpy()[None, :].repeat(4, 0)
+    assert np.array_equal(r16["out"], want)
+    assert np.abs(r8["out"] - want).max() <= 1e-6 * np.abs(want).max()
