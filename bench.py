@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+One step = the whole hot path (route -> permute -> routed experts' up and
+down projections -> shared expert -> combine) over one batch of synthetic
+tokens whose inputs are already resident in HBM.  The default workload is the
+Step-5-Preview-shaped prefill: 8192 tokens, hidden 4096, 352 routed experts,
+top-8, expert and shared intermediate 1536, clipped SwiGLU at 7.0, bf16.
+
+Prints one JSON line with tokens/s, the whole-layer TFLOP/s and bytes/s, the
+roofline of the dominant kernel (routed experts' first projection + SwiGLU,
+timed with HIP events on the stream it runs on), the oracle timed on the
+host cores on a bounded token sample, and the 64-token decode shape's
+bandwidth.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer fwd tokens/s + % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5166e15      # dense bf16 MFMA FLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="step5_prefill")
+    ap.add_argument("--decode-workload", default="step5_decode")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+def layer_flops(wl, touched):
+    c = wl.cfg
+    T, H, E, k, I, Is = wl.T, c.hidden_size, c.num_experts, c.top_k, c.moe_intermediate_size, c.share_expert_dim
+    return 2 * T * E * H + 6 * T * k * H * I + 6 * T * H * Is
+
+
+def layer_bytes(wl, touched):
+    """Algorithmic HBM bytes of one layer forward: the weights of the experts
+    the routing touches, the shared expert and router weights, the bias, the
+    input once and the fp32 output once."""
+    c = wl.cfg
+    T, H, E, I, Is = wl.T, c.hidden_size, c.num_experts, c.moe_intermediate_size, c.share_expert_dim
+    bpw = 1 if c.expert_dtype == "fp8" else 2
+    b = touched * 3 * H * I * bpw + 3 * H * Is * 2 + 2 * E * H + 4 * E + 2 * T * H
+    b += (2 if c.out_dtype == "bf16" else 4) * T * H
+    return b
+
+
+def up_kernel_bytes(wl, touched):
+    """Algorithmic bytes of the routed experts' first projection: W13 of every
+    touched expert once, x once, h written once."""
+    c = wl.cfg
+    T, H, k, I = wl.T, c.hidden_size, c.top_k, c.moe_intermediate_size
+    return touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+
+
+def note(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this MoE-layer forward runs on a single MI355X and has no "
+              "multi-GPU path (expert-parallel sharding is a design note only); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs as mi
+    import sparse_moe_layer_route_amd as moe
+
+    dev = "cuda"
+    moe.load()
+    wl = mi.WORKLOADS[args.workload]
+    cfg, T, k, E, H, I = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size, \
+        wl.cfg.moe_intermediate_size
+    note(f"generating {wl.name} inputs")
+    inp = mi.make_inputs(wl, dev, seed=0)
+    ws = moe.workspace(cfg, T)
+    stream = torch.cuda.current_stream()
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    h = torch.empty(moe.moe_hidden_bytes(cfg, T), dtype=torch.uint8, device=dev)
+    y_rows = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ids, w, ws=ws, stream=stream)
+        counts, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], h=h, ws=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], y_rows=y_rows, ws=ws, stream=stream)
+        moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], y_shared=y_sh, ws=ws, stream=stream)
+        moe.moe_combine(cfg, y_rows, p2r, w, y_sh, out=out, stream=stream)
+        return counts
+
+    note(f"warmup {args.warmup} + timed {args.steps} steps")
+    for _ in range(args.warmup):
+        counts = step()
+    torch.cuda.synchronize()
+    touched = int((counts > 0).sum().item())
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    up_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+
+    # the single-call entry point does the same launches; time it too
+    lw = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    lw[0].record(stream)
+    for _ in range(args.steps):
+        moe.moe_layer_forward(cfg, inp, out=out, ws=ws, stream=stream)
+    lw[1].record(stream)
+    torch.cuda.synchronize()
+    layer_fwd_ms = lw[0].elapsed_time(lw[1]) / args.steps
+
+    tok_s = T / (ms_step * 1e-3)
+    fl = layer_flops(wl, touched)
+    by = layer_bytes(wl, touched)
+    up_bytes = up_kernel_bytes(wl, touched)
+    up_achieved = up_bytes / (up_ms * 1e-3)
+    res = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "hidden_size": H, "num_experts": E, "top_k": k,
+                   "moe_intermediate_size": I, "share_expert_dim": cfg.share_expert_dim,
+                   "swiglu_limit": cfg.swiglu_limit, "swiglu_limit_shared": cfg.swiglu_limit_shared,
+                   "router_scaling_factor": cfg.router_scaling_factor, "experts_touched": touched,
+                   "parallelism": "single GPU"},
+        "tflops": fl / (ms_step * 1e-3) / 1e12,
+        "mfma_frac": fl / (ms_step * 1e-3) / BF16_PEAK,
+        "layer_gbs": by / (ms_step * 1e-3) / 1e9,
+        "hbm_frac": by / (ms_step * 1e-3) / HBM_PEAK,
+        "layer_roofline_frac": max(fl / BF16_PEAK, by / HBM_PEAK) / (ms_step * 1e-3),
+        "layer_forward_ms": layer_fwd_ms,
+        "roofline": {"kernel": "routed experts: first projection + clipped SwiGLU (moe_expert_up)",
+                     "bound": "hbm", "achieved": up_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": up_achieved / HBM_PEAK, "traffic": None, "avg_ms": up_ms,
+                     "algorithmic_bytes": up_bytes},
+    }
+
+    if not args.no_decode:
+        del inp, ws, h, y_rows, y_sh, out
+        torch.cuda.empty_cache()
+        note(f"decode workload {args.decode_workload}")
+        res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
+
+    if not args.no_cpu_baseline:
+        note("CPU baseline (oracle on a token sample)")
+        res["cpu_baseline"] = cpu_baseline(args, wl, mi)
+
+    print(json.dumps(res), flush=True)
+
+
+def bench_decode(args, wl, moe, torch):
+    import moe_inputs as mi
+    inp = mi.make_inputs(wl, "cuda", seed=0)
+    T, k, E, H = wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size
+    ws = moe.workspace(wl.cfg, T)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(max(args.warmup, 3)):
+        moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, expert_counts=counts, stream=stream)
+    torch.cuda.synchronize()
+    touched = int((counts > 0).sum().item())
+    n = max(args.steps, 20)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(n):
+        moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, stream=stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / n
+    by = layer_bytes(wl, touched)
+    del inp, ws
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "tokens": T, "experts_touched": touched, "us_per_step": us,
+            "tokens_per_s": T / (us * 1e-6), "gbs": by / (us * 1e-6) / 1e9, "hbm_frac": by / (us * 1e-6) / HBM_PEAK,
+            "algorithmic_bytes": by}
+
+
+def cpu_baseline(args, wl, mi):
+    """The oracle, as it stands, on the host cores over a bounded token sample
+    of the same workload (rows are independent, so tokens/s scales)."""
+    import numpy as np
+    from oracle import oracle as orc
+    inp = mi.make_inputs(wl, "cuda", seed=0)
+    host = {k: v.cpu() for k, v in inp.items()}
+    del inp
+    rng = np.random.default_rng(0)
+    n = 8
+    t0 = time.perf_counter()
+    orc.layer(wl.cfg, host, tokens=rng.choice(wl.T, n, replace=False))
+    dt = time.perf_counter() - t0
+    n2 = int(min(wl.T, max(n, n * args.cpu_seconds / max(dt, 1e-3))))
+    toks = rng.choice(wl.T, n2, replace=False)
+    t0 = time.perf_counter()
+    orc.layer(wl.cfg, host, tokens=toks)
+    dt2 = time.perf_counter() - t0
+    return {"value": n2 / dt2, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{n2} of {wl.T} tokens of {wl.name} (seeded), full layer per token, {dt2:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

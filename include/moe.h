@@ -1,0 +1,175 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse MoE-layer forward.
+ *
+ * One MoE layer of the Step-3.5-Flash / Step-5-Preview decoders:
+ *   out = routed_moe(x) + shared_expert(x)
+ * with sigmoid router scores, a per-expert routing bias used only for the
+ * top-k choice, expert weights taken from the raw scores, optional
+ * renormalisation, a router scaling factor, clipped-SwiGLU experts and an
+ * always-on shared expert (page "MAX 中 Step-3.5-Flash 架构解析：混合注意力、MoE
+ * 与 TP/EP/DP 并行实现指南", section "MoE：共享专家、sigmoid 路由与激活裁剪";
+ * configuration fields from its section "Step3p5Config配置项全解").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every tensor pointer is a DEVICE pointer, row-major, contiguous,
+ *   16-byte aligned, owned by the caller.  The library never allocates or
+ *   frees device memory; scratch memory comes in through (ws, ws_bytes),
+ *   sized by moe_workspace_size().
+ * bf16: raw IEEE bfloat16 (uint16 storage).  FP8: OCP E4M3FN codes (uint8).
+ * Weights use the [out_features, in_features] layout of the stacked
+ *   checkpoint tensors (layers.{i}.moe.{proj}.weight [num_experts, ...]).
+ *   The fused first projection holds the gate rows 0..I-1, then the up rows
+ *   I..2I-1.
+ * Streams: all work is enqueued on `stream`; no call waits for the device.
+ * Errors: arguments are checked before anything is launched; on an argument
+ *   error nothing is written.  MOE_ERR_HIP reports a launch failure;
+ *   faults inside kernels surface on the stream.
+ * Threads: no global mutable state; calls are thread-safe.  Calls that share
+ *   a workspace must be ordered on one stream.
+ * Shapes: H % 64 == 0, I % 64 == 0, Is % 64 == 0 (or Is == 0), 1 <= k <= 32,
+ *   k <= E <= 1024, T >= 0 (T == 0 is a no-op), T * k < 2^31.  FP8 experts
+ *   also need H % 128 == 0 and I % 128 == 0.  Other shapes return
+ *   MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, bad enum, k > E, negative limit */
+    MOE_ERR_UNSUPPORTED = 2,       /* a shape or dtype combination the kernels do not cover */
+    MOE_ERR_WORKSPACE = 3,         /* ws_bytes smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 4                /* a HIP launch or runtime call failed */
+} moe_status_t;
+
+typedef enum {
+    MOE_BF16 = 0,
+    MOE_FP32 = 1,
+    MOE_FP8_E4M3_B128 = 2          /* E4M3FN codes + one fp32 scale per 128x128 block */
+} moe_dtype_t;
+
+/* One layer's configuration.  Field meanings follow Step3p5Config (config
+ * table of the MAX page): moe_num_experts, moe_top_k, moe_intermediate_size,
+ * share_expert_dim, moe_router_scaling_factor, norm_expert_weight, and one
+ * layer's entries of swiglu_limits / swiglu_limits_shared (0 = no clipping). */
+typedef struct {
+    int32_t hidden_size;            /* H */
+    int32_t num_experts;            /* E, routed experts */
+    int32_t top_k;                  /* k, experts per token */
+    int32_t moe_intermediate_size;  /* I, routed expert width */
+    int32_t share_expert_dim;       /* Is, shared expert width; 0 = no shared expert */
+    float   router_scaling_factor;  /* multiplies the k weights (3.0 on both models) */
+    int32_t norm_expert_weight;     /* 1: divide the k raw scores by their sum first */
+    float   swiglu_limit;           /* routed experts' clip; 0 = none; < 0 invalid */
+    float   swiglu_limit_shared;    /* shared expert's clip; 0 = none; < 0 invalid */
+    int32_t expert_dtype;           /* moe_dtype_t: MOE_BF16 or MOE_FP8_E4M3_B128 (routed experts) */
+    int32_t out_dtype;              /* moe_dtype_t: MOE_FP32 or MOE_BF16 (layer output) */
+} moe_config_t;
+
+/* Bytes of scratch memory moe_layer_forward needs for T tokens (it also
+ * covers each step's own entry point).  Writes *bytes; pure host function. */
+moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes);
+
+/* Router (MAX page, MoE section, Step3p5MoEGate paragraph): logits in fp32
+ * from bf16 x [T,H] and w_router [E,H]; s = sigmoid(logit); the k experts
+ * with the largest s + router_bias (fp32 [E]) are chosen, ordered by
+ * corrected score descending, ties to the lower index, NaN last; every id is
+ * in [0, E-1] even for NaN/Inf inputs.  topk_w [T,k] fp32 = raw s of the
+ * chosen experts, divided by their sum if norm_expert_weight, times
+ * router_scaling_factor.  topk_ids [T,k] int32.  Uses ws for the logits. */
+moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                       const float* router_bias, int32_t* topk_ids, float* topk_w,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permutation of the T*k (token, slot) pairs by expert (the grouping the
+ * routed experts run on; pages describe it only through EP dispatch).
+ * expert_counts [E]: pairs per expert.  expert_offsets [E+1]: exclusive
+ * prefix sum.  row_to_pair [T*k]: rows are expert-major and ascending in
+ * token inside an expert; row r holds pair p = t*k + j.  pair_to_row [T*k]:
+ * the inverse.  All int32; results are deterministic. */
+moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk_ids,
+                         int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* row_to_pair, int32_t* pair_to_row,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Routed experts (MAX page, MoE section: clipped SwiGLU built on the
+ * concatenated gate|up projection, limit = swiglu_limit): for every row r of
+ * expert e (rows expert_offsets[e] .. expert_offsets[e+1]-1), with
+ * t = row_to_pair[r] / k:
+ *   [g|u] = W13[e] x[t];  h = act(g, u, L);  y_rows[r] = W2[e] h
+ * act = silu(g)*u if L == 0, else min(silu(g), L) * clamp(u, -L, L).
+ * w13 [E,2I,H], w2 [E,H,I]: bf16, or E4M3FN codes with w13_scale
+ * [E,2I/128,H/128] and w2_scale [E,H/128,I/128] fp32 (multiplying) when
+ * expert_dtype is MOE_FP8_E4M3_B128 (miles page "Step-5-Preview", section
+ * 1 Model Introduction); scales must be NULL for bf16.  In FP8 mode x and h
+ * are quantised per (row, 128 columns) to E4M3FN with scale amax/448.
+ * y_rows [T*k, H] bf16, unweighted, in row order. */
+moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* x,
+                                const int32_t* expert_offsets, const int32_t* row_to_pair,
+                                const void* w13, const float* w13_scale,
+                                const void* w2, const float* w2_scale,
+                                void* y_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The two halves of moe_grouped_swiglu, for callers that schedule them
+ * apart (and for timing the first projection on its own).
+ * moe_expert_up: h = act(W13[e] x[row_to_pair[r] / k], L) for every row r.
+ *   h is [T*k, I] bf16 for bf16 experts; for FP8 experts it is [T*k, I]
+ *   E4M3FN codes followed by [T*k, I/128] fp32 scales (moe_hidden_bytes()).
+ * moe_expert_down: y_rows[r] = W2[e] h[r] (h dequantised in FP8 mode). */
+moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t T, const void* x,
+                           const int32_t* expert_offsets, const int32_t* row_to_pair,
+                           const void* w13, const float* w13_scale, void* h,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t T, const void* h,
+                             const int32_t* expert_offsets, const void* w2, const float* w2_scale,
+                             void* y_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Bytes of the h buffer moe_expert_up writes for T tokens. */
+moe_status_t moe_hidden_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes);
+
+/* Shared expert (MAX page, MoE section: always-on MLP of width
+ * share_expert_dim, clipped with swiglu_limit_shared):
+ *   y_shared[t] = Ws2 act(Ws13 x[t], L_shared)
+ * ws13 [2Is,H] bf16 (gate rows first), ws2 [H,Is] bf16, y_shared [T,H] fp32.
+ * Requires share_expert_dim > 0. */
+moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x,
+                            const void* ws13, const void* ws2, float* y_shared,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted combine (MAX page, MoE section: routed output plus the shared
+ * expert's): out[t] = sum_j topk_w[t,j] * y_rows[pair_to_row[t*k+j]] + y_shared[t]
+ * accumulated in fp32; y_shared may be NULL (no shared term).  out [T,H] in
+ * out_dtype (fp32 or bf16). */
+moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows,
+                         const int32_t* pair_to_row, const float* topk_w,
+                         const float* y_shared, void* out, hipStream_t stream);
+
+/* The whole layer: route, permute, routed experts, shared expert, combine.
+ * Inputs as above (ws13/ws2 may be NULL when share_expert_dim == 0).
+ * out [T,H] in out_dtype.  Optional outputs (NULL to skip): topk_ids_out
+ * [T,k], topk_w_out [T,k], expert_counts_out [E]. */
+moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x,
+                               const void* w_router, const float* router_bias,
+                               const void* w13, const float* w13_scale,
+                               const void* w2, const float* w2_scale,
+                               const void* ws13, const void* ws2, void* out,
+                               int32_t* topk_ids_out, float* topk_w_out,
+                               int32_t* expert_counts_out,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -312,7 +312,7 @@ int orc_permute(int64_t T, int32_t k, int32_t E, const int32_t* ids, int32_t* co
     }
     offsets[0] = 0;
     for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
-    int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    int32_t* fill = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
     for (int64_t p = 0; p < P; ++p) {      /* pairs in ascending order -> stable */
         int e = ids[p];
         int32_t r = offsets[e] + fill[e]++;

@@ -1,0 +1,72 @@
+// combine.hip -- weighted un-permute of the routed experts' rows plus the
+// shared expert (page "MAX 中 Step-3.5-Flash 架构解析…", section
+// "MoE：共享专家、sigmoid 路由与激活裁剪": the layer output is the routed
+// mixture plus the shared expert's output):
+//   out[t, :] = sum_j w[t, j] * y_rows[pair_to_row[t*k + j], :] + y_shared[t, :]
+// fp32 accumulation, in slot order j = 0..k-1, so results are deterministic.
+// One block of 256 threads per (token, 2048-column slice); each thread moves
+// 8 contiguous columns (16-byte bf16 loads of each of the k rows).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_rows,
+                                                      const int32_t* __restrict__ pair_to_row,
+                                                      const float* __restrict__ topk_w,
+                                                      const float* __restrict__ y_shared,
+                                                      void* __restrict__ out, int H, int k) {
+    const int t = blockIdx.x;
+    const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
+    if (col >= H) return;
+    float acc[8];
+    if (y_shared) {
+        const float4* ys = (const float4*)(y_shared + (int64_t)t * H + col);
+        float4 a = ys[0], b = ys[1];
+        acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
+        acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    for (int j = 0; j < k; ++j) {
+        const int64_t r = pair_to_row[(int64_t)t * k + j];
+        const float w = topk_w[(int64_t)t * k + j];
+        uint4 v = *(const uint4*)(y_rows + r * H + col);
+        uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += w * __uint_as_float(u[i] << 16);
+            acc[2 * i + 1] += w * __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+    if (OUT_BF16) {
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        *(uint4*)((uint16_t*)out + (int64_t)t * H + col) = o;
+    } else {
+        float4* o = (float4*)((float*)out + (int64_t)t * H + col);
+        o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
+hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
+                          const float* y_shared, void* out, bool out_bf16, int T, int H, int k,
+                          hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    dim3 grid(T, (H + 2047) / 2048);
+    if (out_bf16)
+        combine_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)y_rows, pair_to_row, topk_w, y_shared,
+                                                  out, H, k);
+    else
+        combine_kernel<false><<<grid, 256, 0, s>>>((const uint16_t*)y_rows, pair_to_row, topk_w, y_shared,
+                                                   out, H, k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

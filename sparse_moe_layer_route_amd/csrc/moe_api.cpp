@@ -1,0 +1,286 @@
+// moe_api.cpp -- the C ABI declared in include/moe.h: argument checks,
+// workspace layout and the order of launches.  No call allocates, frees or
+// synchronises; everything is enqueued on the caller's stream.
+#include "moe.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+    int64_t T, P;
+    int H, E, k, I, Is;
+};
+
+moe_status_t check_config(const moe_config_t* c, int64_t T) {
+    if (!c || T < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->hidden_size <= 0 || c->num_experts <= 0 || c->top_k <= 0 || c->moe_intermediate_size <= 0 ||
+        c->share_expert_dim < 0)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (c->top_k > c->num_experts) return MOE_ERR_INVALID_ARGUMENT;
+    if (!isfinite(c->router_scaling_factor)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(c->swiglu_limit >= 0.0f) || !isfinite(c->swiglu_limit)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(c->swiglu_limit_shared >= 0.0f) || !isfinite(c->swiglu_limit_shared))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (c->norm_expert_weight != 0 && c->norm_expert_weight != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_FP8_E4M3_B128) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->out_dtype != MOE_FP32 && c->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->hidden_size % 64 || c->moe_intermediate_size % 64 || c->share_expert_dim % 64)
+        return MOE_ERR_UNSUPPORTED;
+    if (c->top_k > 32 || c->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
+    if (T * (int64_t)c->top_k >= ((int64_t)1 << 31) || T >= ((int64_t)1 << 31) / 8)
+        return MOE_ERR_UNSUPPORTED;
+    if (c->expert_dtype == MOE_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;   // not built yet
+    return MOE_OK;
+}
+
+Dims dims(const moe_config_t* c, int64_t T) {
+    return Dims{T, T * c->top_k, c->hidden_size, c->num_experts, c->top_k, c->moe_intermediate_size,
+                c->share_expert_dim};
+}
+
+// scratch each step needs at the start of the workspace it is handed
+size_t route_ws(const Dims& d) { return align_up((size_t)d.T * d.E * 4); }
+size_t permute_ws(const Dims& d) { return align_up(moe::permute_scratch_bytes(d.P, d.E)); }
+size_t plan_ws(const Dims& d) { return align_up((size_t)(d.E + 1) * 4); }
+size_t grouped_ws(const Dims& d) { return plan_ws(d) + align_up((size_t)d.P * d.I * 2); }
+size_t shared_ws(const Dims& d) { return align_up((size_t)d.T * d.Is * 2); }
+
+// the whole layer: its own buffers followed by each step's scratch
+struct LayerWs {
+    size_t ids, w, counts, offsets, r2p, p2r, y_rows, y_sh, step, total;
+};
+
+LayerWs layer_ws(const Dims& d) {
+    LayerWs L;
+    size_t o = 0;
+    L.ids = o;     o += align_up((size_t)d.P * 4);
+    L.w = o;       o += align_up((size_t)d.P * 4);
+    L.counts = o;  o += align_up((size_t)d.E * 4);
+    L.offsets = o; o += align_up((size_t)(d.E + 1) * 4);
+    L.r2p = o;     o += align_up((size_t)d.P * 4);
+    L.p2r = o;     o += align_up((size_t)d.P * 4);
+    L.y_rows = o;  o += align_up((size_t)d.P * d.H * 2);
+    L.y_sh = o;    o += d.Is > 0 ? align_up((size_t)d.T * d.H * 4) : 0;
+    L.step = o;
+    o += std::max(std::max(route_ws(d), permute_ws(d)), std::max(grouped_ws(d), shared_ws(d)));
+    L.total = o;
+    return L;
+}
+
+inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                              \
+    do {                                           \
+        moe_status_t _st = (expr);                 \
+        if (_st != MOE_OK) return _st;             \
+    } while (0)
+#define HIP_TRY(expr) MOE_TRY(hip_status(expr))
+
+// ---- the steps, without argument checks ----------------------------------
+
+moe_status_t do_route(const moe_config_t* c, const Dims& d, const void* x, const void* wr, const float* b,
+                      int32_t* ids, float* w, char* ws, hipStream_t s) {
+    float* logits = (float*)ws;
+    HIP_TRY(moe::launch_router_logits(x, wr, logits, (int)d.T, d.E, d.H, s));
+    HIP_TRY(moe::launch_topk(logits, b, (int)d.T, d.E, d.k, c->router_scaling_factor, c->norm_expert_weight,
+                             ids, w, s));
+    return MOE_OK;
+}
+
+size_t hidden_bytes(const Dims& d) { return (size_t)d.P * d.I * 2; }
+
+int max_tiles(const Dims& d) {
+    const int bm = moe::gemm_tile_m();
+    return (int)((d.P + bm - 1) / bm) + d.E;
+}
+
+// routed experts' first projection + clipped SwiGLU -> h
+moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
+                   const int32_t* r2p, const void* w13, void* h, char* ws, hipStream_t s) {
+    int32_t* tile_start = (int32_t*)ws;
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::gemm_tile_m(), tile_start, s));
+    HIP_TRY(moe::launch_gemm_swiglu(x, r2p, d.k, w13, (int64_t)2 * d.I * d.H, h, (int)d.T, d.I, d.H,
+                                    c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
+    return MOE_OK;
+}
+
+// routed experts' second projection -> y_rows
+moe_status_t do_down(const moe_config_t* c, const Dims& d, const void* h, const int32_t* offsets,
+                     const void* w2, void* y_rows, char* ws, hipStream_t s) {
+    (void)c;
+    int32_t* tile_start = (int32_t*)ws;
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::gemm_tile_m(), tile_start, s));
+    HIP_TRY(moe::launch_gemm_out(h, w2, (int64_t)d.H * d.I, y_rows, false, (int)d.P, d.H, d.I, offsets,
+                                 tile_start, d.E, max_tiles(d), s));
+    return MOE_OK;
+}
+
+moe_status_t do_grouped(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
+                        const int32_t* r2p, const void* w13, const void* w2, void* y_rows, char* ws,
+                        hipStream_t s) {
+    void* h = ws + align_up((size_t)(d.E + 1) * 4);
+    MOE_TRY(do_up(c, d, x, offsets, r2p, w13, h, ws, s));
+    MOE_TRY(do_down(c, d, h, offsets, w2, y_rows, ws, s));
+    return MOE_OK;
+}
+
+moe_status_t do_shared(const moe_config_t* c, const Dims& d, const void* x, const void* ws13,
+                       const void* ws2, float* y_sh, char* ws, hipStream_t s) {
+    uint16_t* hs = (uint16_t*)ws;
+    HIP_TRY(moe::launch_gemm_swiglu(x, nullptr, 1, ws13, 0, hs, (int)d.T, d.Is, d.H, c->swiglu_limit_shared,
+                                    nullptr, nullptr, 1, 0, s));
+    HIP_TRY(moe::launch_gemm_out(hs, ws2, 0, y_sh, true, (int)d.T, d.H, d.Is, nullptr, nullptr, 1, 0, s));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_config(cfg, T));
+    *bytes = layer_ws(dims(cfg, T)).total;
+    return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                       const float* router_bias, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !router_bias || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (ws_bytes < route_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_route(cfg, d, x, w_router, router_bias, topk_ids, topk_w, (char*)ws, stream);
+}
+
+moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk_ids, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* row_to_pair, int32_t* pair_to_row, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (T > 0 && (!topk_ids || !row_to_pair || !pair_to_row || !ws)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T > 0 && ws_bytes < permute_ws(d)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_permute(topk_ids, (int)T, d.k, d.E, expert_counts, expert_offsets,
+                                          row_to_pair, pair_to_row, ws, stream));
+}
+
+moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* x, const int32_t* expert_offsets,
+                                const int32_t* row_to_pair, const void* w13, const float* w13_scale,
+                                const void* w2, const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (cfg->expert_dtype == MOE_BF16 && (w13_scale || w2_scale)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!x || !expert_offsets || !row_to_pair || !w13 || !w2 || !y_rows || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (ws_bytes < grouped_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_grouped(cfg, d, x, expert_offsets, row_to_pair, w13, w2, y_rows, (char*)ws, stream);
+}
+
+moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t T, const void* x, const int32_t* expert_offsets,
+                           const int32_t* row_to_pair, const void* w13, const float* w13_scale, void* h, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (cfg->expert_dtype == MOE_BF16 && w13_scale) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!x || !expert_offsets || !row_to_pair || !w13 || !h || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (ws_bytes < plan_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_up(cfg, d, x, expert_offsets, row_to_pair, w13, h, (char*)ws, stream);
+}
+
+moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t T, const void* h, const int32_t* expert_offsets,
+                             const void* w2, const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (cfg->expert_dtype == MOE_BF16 && w2_scale) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!h || !expert_offsets || !w2 || !y_rows || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (ws_bytes < plan_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_down(cfg, d, h, expert_offsets, w2, y_rows, (char*)ws, stream);
+}
+
+moe_status_t moe_hidden_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_config(cfg, T));
+    *bytes = hidden_bytes(dims(cfg, T));
+    return MOE_OK;
+}
+
+moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x, const void* ws13, const void* ws2,
+                            float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (cfg->share_expert_dim == 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!x || !ws13 || !ws2 || !y_shared || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (ws_bytes < shared_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_shared(cfg, d, x, ws13, ws2, y_shared, (char*)ws, stream);
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows, const int32_t* pair_to_row,
+                         const float* topk_w, const float* y_shared, void* out, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (T == 0) return MOE_OK;
+    if (!y_rows || !pair_to_row || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_combine(y_rows, pair_to_row, topk_w, y_shared, out, cfg->out_dtype == MOE_BF16,
+                                          (int)T, cfg->hidden_size, cfg->top_k, stream));
+}
+
+moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                               const float* router_bias, const void* w13, const float* w13_scale, const void* w2,
+                               const float* w2_scale, const void* ws13, const void* ws2, void* out,
+                               int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (cfg->expert_dtype == MOE_BF16 && (w13_scale || w2_scale)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !router_bias || !w13 || !w2 || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    if (cfg->share_expert_dim > 0 && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    LayerWs L = layer_ws(d);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+    float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+    int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)(base + L.counts);
+    int32_t* offsets = (int32_t*)(base + L.offsets);
+    int32_t* r2p = (int32_t*)(base + L.r2p);
+    int32_t* p2r = (int32_t*)(base + L.p2r);
+    void* y_rows = base + L.y_rows;
+    float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
+    char* step = base + L.step;
+
+    MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, step, stream));
+    HIP_TRY(moe::launch_permute(ids, (int)T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
+    MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w2, y_rows, step, stream));
+    if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
+    HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, out, cfg->out_dtype == MOE_BF16, (int)T, d.H, d.k, stream));
+    return MOE_OK;
+}
+
+const char* moe_status_string(moe_status_t status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// moe_internal.h -- host-side launchers of the gfx950 kernels.  Each returns
+// hipSuccess or the launch error.  Shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router ---------------------------------------------------------------
+// logits[T,E] fp32 = x[T,H] . w_router[E,H]^T  (bf16 inputs, fp32 accumulate)
+hipError_t launch_router_logits(const void* x, const void* w_router, float* logits,
+                                int T, int E, int H, hipStream_t s);
+// per-token sigmoid + bias + top-k + weights
+hipError_t launch_topk(const float* logits, const float* bias, int T, int E, int k, float scale,
+                       int norm, int32_t* ids, float* w, hipStream_t s);
+
+// ---- permutation ----------------------------------------------------------
+size_t permute_scratch_bytes(int64_t P, int E);   // P = T * k pairs
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* row_to_pair, int32_t* pair_to_row, void* scratch, hipStream_t s);
+
+// ---- grouped / dense GEMMs ------------------------------------------------
+// Tile plan for a grouped GEMM with BM-row tiles: tile_start[E+1].
+hipError_t launch_tile_plan(const int32_t* offsets, int E, int bm, int32_t* tile_start, hipStream_t s);
+
+// h[rows, N] bf16 = act(A[rows] . W13^T) where A rows are gathered
+// (a_rows[r] / a_div) or dense, W13 [2N, K] per group (gate rows first).
+// Grouped when offsets != nullptr (groups = E, tile_start from the plan).
+hipError_t launch_gemm_swiglu(const void* A, const int32_t* a_rows, int a_div, const void* W13,
+                              int64_t w_group_stride, void* h, int M, int N, int K, float limit,
+                              const int32_t* offsets, const int32_t* tile_start, int groups,
+                              int max_tiles, hipStream_t s);
+// C[rows, N] = A[rows, K] . W^T with W [N, K] per group; C bf16 or fp32.
+hipError_t launch_gemm_out(const void* A, const void* W, int64_t w_group_stride, void* C, bool c_fp32,
+                           int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
+                           int groups, int max_tiles, hipStream_t s);
+int gemm_tile_m();
+
+// ---- combine --------------------------------------------------------------
+hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
+                          const float* y_shared, void* out, bool out_bf16, int T, int H, int k,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+"""Comparison rules shared by the GPU parity tests.
+
+Routing: ids are compared per token as sets (weights paired by id) and in
+order where the neighbouring corrected scores differ by more than the tie
+gap.  A token whose k-th and (k+1)-th corrected scores (in the oracle's
+fp32 values) are closer than GAP is exempt from the exact-set check: the GPU
+set must then contain every expert scoring above c_k + GAP and only experts
+scoring at least c_(k+1) - GAP.
+
+Outputs: max |gpu - oracle| <= tol * RMS(oracle output) over the compared
+tokens, with tol = 2e-2 for bf16 experts and 6e-2 for FP8 experts.
+"""
+import numpy as np
+
+GAP = 1e-6
+TOL_BF16 = 2e-2
+TOL_FP8 = 6e-2
+
+
+def exempt_tokens(corrected: np.ndarray, k: int) -> np.ndarray:
+    """Boolean [T]: True where the k-th / (k+1)-th gap is below GAP."""
+    c = np.where(np.isnan(corrected), -np.inf, corrected.astype(np.float64))
+    if c.shape[1] <= k:
+        return np.zeros(c.shape[0], bool)
+    part = -np.sort(-c, axis=1)
+    return (part[:, k - 1] - part[:, k]) < GAP
+
+
+def check_routing(gpu_ids, gpu_w, orc_ids, orc_w, corrected, k, w_rtol=1e-5, w_atol=1e-6):
+    """Asserts the routing rules; returns the exempt-token mask."""
+    gpu_ids = np.asarray(gpu_ids)
+    gpu_w = np.asarray(gpu_w)
+    ex = exempt_tokens(corrected, k)
+    c = corrected.astype(np.float64)
+    T = gpu_ids.shape[0]
+    assert gpu_ids.min() >= 0 and gpu_ids.max() < corrected.shape[1]
+    for t in range(T):
+        g, o = gpu_ids[t].tolist(), orc_ids[t].tolist()
+        assert len(set(g)) == k, f"token {t}: duplicate ids {g}"
+        if ex[t]:
+            srt = np.sort(c[t])[::-1]
+            ck, ck1 = srt[k - 1], srt[k]
+            must = set(np.nonzero(c[t] > ck + GAP)[0].tolist())
+            may = set(np.nonzero(c[t] >= ck1 - GAP)[0].tolist())
+            assert must <= set(g) <= may, f"token {t}: exempt set rule violated"
+            continue
+        assert set(g) == set(o), f"token {t}: gpu {g} oracle {o}"
+        # order: adjacent choices must agree unless their scores nearly tie
+        for j in range(k):
+            if g[j] != o[j]:
+                assert abs(c[t, g[j]] - c[t, o[j]]) < GAP, f"token {t}: order {g} vs {o}"
+        gw = dict(zip(g, gpu_w[t].tolist()))
+        for j, e in enumerate(o):
+            assert abs(gw[e] - orc_w[t, j]) <= w_atol + w_rtol * abs(orc_w[t, j]), \
+                f"token {t}: weight of expert {e}: {gw[e]} vs {orc_w[t, j]}"
+    return ex
+
+
+def check_counts(gpu_counts, orc_ids, gpu_ids, exempt, E):
+    """Per-expert counts bit-exact once exempt tokens are taken out of both."""
+    gpu_counts = np.asarray(gpu_counts).astype(np.int64)
+    keep = ~exempt
+    want = np.bincount(np.asarray(orc_ids)[keep].reshape(-1), minlength=E)
+    gpu_ex = np.bincount(np.asarray(gpu_ids)[exempt].reshape(-1), minlength=E)
+    assert gpu_counts.sum() == np.asarray(gpu_ids).size
+    assert np.array_equal(gpu_counts - gpu_ex, want)
+
+
+def max_err_over_rms(gpu_out, orc_out):
+    gpu_out = np.asarray(gpu_out, dtype=np.float64)
+    orc_out = np.asarray(orc_out, dtype=np.float64)
+    rms = np.sqrt((orc_out ** 2).mean())
+    return float(np.abs(gpu_out - orc_out).max() / rms), rms

@@ -1,0 +1,138 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status before
+anything is launched (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_inputs as mi
+import sparse_moe_layer_route_amd as moe
+from sparse_moe_layer_route_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_moe_layer_route_amd import build
+        build.build()
+    return B.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_are_exported(lib):
+    names = header_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s, want in [(0, "ok"), (1, "invalid argument"), (2, "unsupported shape or dtype"),
+                    (3, "workspace too small"), (4, "HIP launch or runtime error")]:
+        assert moe.status_string(s) == want
+
+
+def cfg_of(**over):
+    return B.make_config(mi.workload("tiny", **over).cfg)
+
+
+def ws_size(c, T):
+    n = ctypes.c_size_t(0)
+    st = B.load().moe_workspace_size(ctypes.byref(c), T, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    c = cfg_of()
+    st0, n0 = ws_size(c, 0)
+    st1, n1 = ws_size(c, 64)
+    st2, n2 = ws_size(c, 4096)
+    assert st0 == st1 == st2 == 0 and n0 < n1 < n2
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hidden_size", 0, 1), ("hidden_size", 100, 2), ("num_experts", 0, 1), ("num_experts", 2048, 2),
+    ("top_k", 0, 1), ("top_k", 17, 1), ("moe_intermediate_size", 96, 2), ("share_expert_dim", -64, 1),
+    ("share_expert_dim", 32, 2), ("swiglu_limit", -1.0, 1), ("swiglu_limit", float("nan"), 1),
+    ("swiglu_limit_shared", float("inf"), 1), ("router_scaling_factor", float("nan"), 1),
+    ("norm_expert_weight", 2, 1), ("expert_dtype", 7, 1), ("out_dtype", 2, 1), ("expert_dtype", 1, 1),
+])
+def test_config_validation(lib, field, value, status):
+    c = cfg_of()
+    setattr(c, field, value)
+    assert ws_size(c, 64)[0] == status
+
+
+def test_topk_above_32_unsupported(lib):
+    c = cfg_of(num_experts=64, top_k=33)
+    assert ws_size(c, 8)[0] == 2
+
+
+def test_negative_tokens_and_null_out(lib):
+    c = cfg_of()
+    assert ws_size(c, -1)[0] == 1
+    assert lib.moe_workspace_size(ctypes.byref(c), 4, None) == 1
+    assert lib.moe_workspace_size(None, 4, ctypes.byref(ctypes.c_size_t())) == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)    # never dereferenced: every call below fails its checks first
+
+
+def test_entry_points_reject_null_pointers(lib):
+    c = ctypes.byref(cfg_of())
+    assert lib.moe_route(c, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_permute(c, 4, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_grouped_swiglu(c, 4, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 30,
+                                  None) == 1
+    assert lib.moe_shared_ffn(c, 4, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.moe_combine(c, 4, FAKE, FAKE, None, None, FAKE, None) == 1
+    assert lib.moe_layer_forward(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, None,
+                                 None, None, FAKE, 1 << 30, None) == 1   # shared weights missing
+
+
+def test_bf16_experts_reject_scales(lib):
+    c = ctypes.byref(cfg_of())
+    assert lib.moe_grouped_swiglu(c, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30,
+                                  None) == 1
+
+
+def test_shared_ffn_needs_a_shared_expert(lib):
+    c = ctypes.byref(cfg_of(share_expert_dim=0))
+    assert lib.moe_shared_ffn(c, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+
+
+def test_small_workspace_is_reported(lib):
+    c = ctypes.byref(cfg_of())
+    assert lib.moe_route(c, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    assert lib.moe_permute(c, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    assert lib.moe_grouped_swiglu(c, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 16, None) == 3
+    assert lib.moe_shared_ffn(c, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    st, need = ws_size(cfg_of(), 64)
+    assert lib.moe_layer_forward(c, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None,
+                                 None, None, FAKE, need - 1, None) == 3
+
+
+def test_zero_tokens_is_a_noop(lib):
+    c = ctypes.byref(cfg_of())
+    assert lib.moe_route(c, 0, None, None, None, None, None, None, 0, None) == 0
+    assert lib.moe_grouped_swiglu(c, 0, None, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.moe_combine(c, 0, None, None, None, None, None, None) == 0
+    assert lib.moe_layer_forward(c, 0, None, None, None, None, None, None, None, None, None, None, None,
+                                 None, None, None, 0, None) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    wl = mi.workload("tiny")
+    inp = mi.make_inputs(wl, "cpu")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"],
+                      topk_ids=torch.empty(1), topk_w=torch.empty(1), ws=torch.empty(1))

@@ -1,0 +1,225 @@
+"""GPU parity: every entry point of libmoe.so against the CPU oracle on
+identical seeded inputs.
+
+Small workloads (tiny, ragged and edge-case shapes spanning several tiles and
+ragged tails) are compared on every token; the full-size Step-3.5-Flash and
+Step-5-Preview workloads are run through moe_layer_forward exactly as the
+benchmark runs them, with routing and per-expert counts checked on every token
+and outputs on a seeded sample of tokens (rows are independent, so a sampled
+row is checked exactly).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import sparse_moe_layer_route_amd as moe
+from oracle import oracle as orc
+from parity import (TOL_BF16, check_counts, check_routing, exempt_tokens, max_err_over_rms)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    moe.load()
+
+
+def gpu_inputs(wl, seed=0):
+    return mi.make_inputs(wl, DEV, seed)
+
+
+def host(inp):
+    return {k: v.cpu() for k, v in inp.items()}
+
+
+def run_layer(wl, inp, ws=None):
+    T, k, E = wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    counts = torch.empty((E,), dtype=torch.int32, device=DEV)
+    out = moe.moe_layer_forward(wl.cfg, inp, ws=ws, topk_ids=ids, topk_w=w, expert_counts=counts)
+    torch.cuda.synchronize()
+    return out, ids, w, counts
+
+
+# ----------------------------------------------------------------------------------------
+# small and edge-case workloads: every token
+
+SMALL = {
+    "tiny": dict(),
+    "tiny_clip_stress": dict(x_scale=40.0),
+    "one_token": dict(T=1),
+    "three_tokens": dict(T=3),
+    "ragged_130_tokens_20_experts": dict(T=130, num_experts=20, top_k=3),
+    "top1": dict(top_k=1, T=77),
+    "all_experts_chosen": dict(top_k=16, T=40),
+    "no_norm": dict(norm_expert_weight=False, router_scaling_factor=2.5),
+    "no_shared": dict(share_expert_dim=0, T=96),
+    "limits_off": dict(swiglu_limit=0.0, swiglu_limit_shared=0.0, x_scale=8.0),
+    "shared_clip": dict(swiglu_limit=0.5, swiglu_limit_shared=0.5, x_scale=8.0),
+    "bf16_out": dict(out_dtype="bf16"),
+    "narrow_64": dict(hidden_size=64, moe_intermediate_size=64, share_expert_dim=64, T=200),
+    "wide_tiles": dict(hidden_size=512, moe_intermediate_size=320, share_expert_dim=192, T=300,
+                       num_experts=12, top_k=2),
+    "max_experts_max_k": dict(hidden_size=128, num_experts=1024, top_k=32, moe_intermediate_size=64,
+                              share_expert_dim=64, T=64),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name):
+    wl = mi.workload("tiny", **SMALL[name])
+    say(f"[layer_small] {name} T={wl.T} cfg={wl.cfg}")
+    inp = gpu_inputs(wl)
+    out, ids, w, counts = run_layer(wl, inp)
+    h = host(inp)
+    ref = orc.layer(wl.cfg, h)
+    _, _, _, corr = orc.route(wl.cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ex = check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], corr, wl.cfg.top_k)
+    check_counts(counts.cpu().numpy(), ref["ids"], ids.cpu().numpy(), ex, wl.cfg.num_experts)
+    keep = ~ex
+    err, rms = max_err_over_rms(out.float().cpu().numpy()[keep], ref["out"][keep])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e}), exempt tokens {int(ex.sum())}")
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_130_tokens_20_experts", "wide_tiles"])
+def test_steps_small(name):
+    """Each entry point on its own: route, permute, grouped experts, shared
+    expert, combine."""
+    wl = mi.workload("tiny", **SMALL[name])
+    cfg, T, k, E, H = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size
+    say(f"[steps_small] {name}")
+    inp = gpu_inputs(wl)
+    h = host(inp)
+    ws = moe.workspace(cfg, T)
+    ids, w = moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ws=ws)
+    counts, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws)
+    y_rows = moe.moe_grouped_swiglu(cfg, inp["x"], offsets, r2p, inp["w13"], inp["w2"], ws=ws)
+    y_sh = moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], ws=ws)
+    out = moe.moe_combine(cfg, y_rows, p2r, w, y_sh)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    # permutation: bit-exact against the oracle's stable grouping of the GPU's ids
+    oc, oo, or2p, op2r = orc.permute(ids_h, E)
+    assert np.array_equal(counts.cpu().numpy(), oc)
+    assert np.array_equal(offsets.cpu().numpy(), oo)
+    assert np.array_equal(r2p.cpu().numpy(), or2p)
+    assert np.array_equal(p2r.cpu().numpy(), op2r)
+    # experts: row r of y_rows is pair r2p[r]'s expert output, unweighted
+    ref = orc.layer(cfg, h, want_parts=True)
+    _, _, _, corr = orc.route(cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ex = check_routing(ids_h, w.cpu().numpy(), ref["ids"], ref["w"], corr, k)
+    yr = y_rows.float().cpu().numpy()
+    pairs = or2p
+    t_of, j_of = pairs // k, pairs % k
+    keep = ~ex[t_of]
+    # the oracle's slot order may differ from the GPU's only among near-ties
+    orc_slot = {(t, e): j for t in range(T) for j, e in enumerate(ref["ids"][t].tolist())}
+    ref_rows = np.stack([ref["y_routed"][t, orc_slot[(t, ids_h[t, j])]] for t, j in zip(t_of, j_of)])
+    err, _ = max_err_over_rms(yr[keep], ref_rows[keep])
+    say(f"  grouped rows max_err/rms = {err:.3e}")
+    assert err <= TOL_BF16
+    err, _ = max_err_over_rms(y_sh.cpu().numpy(), ref["y_shared"])
+    say(f"  shared max_err/rms = {err:.3e}")
+    assert err <= TOL_BF16
+    # combine: exact fp32 sum of the GPU's own buffers, in slot order
+    want = y_sh.double().cpu().numpy().copy()
+    wh = w.double().cpu().numpy()
+    p2r_h = p2r.cpu().numpy()
+    for t in range(T):
+        for j in range(k):
+            want[t] += wh[t, j] * yr[p2r_h[t * k + j]]
+    assert np.abs(out.cpu().numpy() - want).max() <= 1e-5 * np.abs(want).max()
+
+
+def test_permute_arbitrary_ids_with_duplicates():
+    """Stable grouping is defined for any ids in range, duplicates included."""
+    wl = mi.workload("tiny", T=333, num_experts=37, top_k=5)
+    g = torch.Generator().manual_seed(7)
+    ids = torch.randint(0, 37, (333, 5), generator=g, dtype=torch.int32)
+    counts, offsets, r2p, p2r = moe.moe_permute(wl.cfg, ids.to(DEV))
+    torch.cuda.synchronize()
+    oc, oo, or2p, op2r = orc.permute(ids.numpy(), 37)
+    assert np.array_equal(counts.cpu().numpy(), oc) and np.array_equal(offsets.cpu().numpy(), oo)
+    assert np.array_equal(r2p.cpu().numpy(), or2p) and np.array_equal(p2r.cpu().numpy(), op2r)
+
+
+def test_nan_inf_inputs_keep_ids_in_range():
+    wl = mi.workload("tiny")
+    inp = gpu_inputs(wl)
+    inp["x"][0] = float("nan")
+    inp["x"][1, 5] = float("inf")
+    inp["x"][2] = float("-inf")
+    ids, w = moe.moe_route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"])
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    assert ids.min() >= 0 and ids.max() < wl.cfg.num_experts
+    assert ids[0].tolist() == list(range(wl.cfg.top_k))      # all scores NaN -> lowest indices
+    ref_ids, _ = orc.route(wl.cfg, *(inp[n].cpu() for n in ("x", "w_router", "router_bias")))
+    assert np.array_equal(ids[:3], ref_ids[:3])
+
+
+def test_zero_tokens():
+    wl = mi.workload("tiny", T=0)
+    inp = gpu_inputs(wl)
+    out = moe.moe_layer_forward(wl.cfg, inp)
+    torch.cuda.synchronize()
+    assert out.shape == (0, wl.cfg.hidden_size)
+
+
+def test_deterministic():
+    wl = mi.workload("tiny", T=257)
+    inp = gpu_inputs(wl)
+    a = run_layer(wl, inp)
+    b = run_layer(wl, inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# ----------------------------------------------------------------------------------------
+# full-size workloads through moe_layer_forward
+
+FULL = ["step35_prefill", "step5_prefill", "step5_decode", "step5_decode_half"]
+N_SAMPLE = 24
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_full_size(name):
+    wl = mi.WORKLOADS[name]
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    say(f"[layer_full] {name} T={T} E={E} k={k} H={cfg.hidden_size} I={cfg.moe_intermediate_size}")
+    inp = gpu_inputs(wl)
+    out, ids, w, counts = run_layer(wl, inp)
+    out2, *_ = run_layer(wl, inp)
+    assert torch.equal(out, out2), "repeat run differs"
+    say("  gpu done; copying inputs to host")
+    h = host(inp)
+    del inp
+    torch.cuda.empty_cache()
+    o_ids, o_w, _, corr = orc.route(cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ids_h = ids.cpu().numpy()
+    ex = check_routing(ids_h, w.cpu().numpy(), o_ids, o_w, corr, k)
+    check_counts(counts.cpu().numpy(), o_ids, ids_h, ex, E)
+    say(f"  routing ok on all {T} tokens; exempt {int(ex.sum())}; experts touched "
+        f"{int((counts.cpu().numpy() > 0).sum())}")
+    rng = np.random.default_rng(0)
+    cand = np.nonzero(~ex)[0]
+    sample = np.unique(np.concatenate([cand[:2], cand[-2:], rng.choice(cand, min(N_SAMPLE, cand.size),
+                                                                        replace=False)]))
+    ref = orc.layer(cfg, h, tokens=sample)
+    assert np.array_equal(ref["ids"], o_ids[sample])
+    err, rms = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
+    say(f"  sampled {sample.size} tokens: max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_BF16
