@@ -94,7 +94,7 @@ def main():
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     h = torch.empty(moe.moe_hidden_bytes(cfg, T), dtype=torch.uint8, device=dev)
-    y_rows = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    y_rows = torch.empty((T * k, H), dtype=torch.float16, device=dev)
     y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
 
     def step(ev=None):

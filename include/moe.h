@@ -112,7 +112,9 @@ moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk
  * expert_dtype is MOE_FP8_E4M3_B128 (miles page "Step-5-Preview", section
  * 1 Model Introduction); scales must be NULL for bf16.  In FP8 mode x and h
  * are quantised per (row, 128 columns) to E4M3FN with scale amax/448.
- * y_rows [T*k, H] bf16, unweighted, in row order. */
+ * y_rows [T*k, H] fp16 (round to nearest even, saturating at +-65504),
+ * unweighted, in row order: fp16 keeps 11 significant bits for the same
+ * bytes as bf16, so the rows add at most 2^-11 relative rounding. */
 moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* x,
                                 const int32_t* expert_offsets, const int32_t* row_to_pair,
                                 const void* w13, const float* w13_scale,
@@ -146,7 +148,8 @@ moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x,
 
 /* Weighted combine (MAX page, MoE section: routed output plus the shared
  * expert's): out[t] = sum_j topk_w[t,j] * y_rows[pair_to_row[t*k+j]] + y_shared[t]
- * accumulated in fp32; y_shared may be NULL (no shared term).  out [T,H] in
+ * accumulated in fp32 in slot order; y_rows [T*k,H] fp16 as written by the
+ * routed experts; y_shared may be NULL (no shared term).  out [T,H] in
  * out_dtype (fp32 or bf16). */
 moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows,
                          const int32_t* pair_to_row, const float* topk_w,

@@ -173,7 +173,7 @@ def moe_grouped_swiglu(cfg, x, expert_offsets, row_to_pair, w13, w2, w13_scale=N
                        y_rows=None, ws=None, stream=None):
     T, H, E, k, I = x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size
     wdt = _weights_dtype(cfg)
-    y_rows = y_rows if y_rows is not None else torch.empty((T * k, H), dtype=torch.bfloat16, device=x.device)
+    y_rows = y_rows if y_rows is not None else torch.empty((T * k, H), dtype=torch.float16, device=x.device)
     ws = ws if ws is not None else workspace(cfg, T, x.device)
     fp8 = cfg.expert_dtype == "fp8"
     c = make_config(cfg)
@@ -185,7 +185,7 @@ def moe_grouped_swiglu(cfg, x, expert_offsets, row_to_pair, w13, w2, w13_scale=N
         _ptr(w13_scale, torch.float32, (E, 2 * I // 128, H // 128) if fp8 else None, "w13_scale"),
         _ptr(w2, wdt, (E, H, I), "w2"),
         _ptr(w2_scale, torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
-        _ptr(y_rows, torch.bfloat16, (T * k, H), "y_rows"),
+        _ptr(y_rows, torch.float16, (T * k, H), "y_rows"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_grouped_swiglu")
     return y_rows
@@ -225,7 +225,7 @@ def moe_expert_down(cfg, T, h, expert_offsets, w2, w2_scale=None, y_rows=None, w
     fp8 = cfg.expert_dtype == "fp8"
     if h.numel() * h.element_size() < moe_hidden_bytes(cfg, T):
         raise ValueError("h is smaller than moe_hidden_bytes()")
-    y_rows = y_rows if y_rows is not None else torch.empty((T * k, H), dtype=torch.bfloat16, device=h.device)
+    y_rows = y_rows if y_rows is not None else torch.empty((T * k, H), dtype=torch.float16, device=h.device)
     ws = ws if ws is not None else workspace(cfg, T, h.device)
     c = make_config(cfg)
     st = load().moe_expert_down(
@@ -233,7 +233,7 @@ def moe_expert_down(cfg, T, h, expert_offsets, w2, w2_scale=None, y_rows=None, w
         _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
         _ptr(w2, _weights_dtype(cfg), (E, H, I), "w2"),
         _ptr(w2_scale, torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
-        _ptr(y_rows, torch.bfloat16, (T * k, H), "y_rows"),
+        _ptr(y_rows, torch.float16, (T * k, H), "y_rows"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_expert_down")
     return y_rows
@@ -261,7 +261,7 @@ def moe_combine(cfg, y_rows, pair_to_row, topk_w, y_shared=None, out=None, strea
     T, H, k = topk_w.shape[0], cfg.hidden_size, cfg.top_k
     out = out if out is not None else torch.empty((T, H), dtype=_out_dtype(cfg), device=y_rows.device)
     c = make_config(cfg)
-    st = load().moe_combine(ctypes.byref(c), T, _ptr(y_rows, torch.bfloat16, (T * k, H), "y_rows"),
+    st = load().moe_combine(ctypes.byref(c), T, _ptr(y_rows, torch.float16, (T * k, H), "y_rows"),
                             _ptr(pair_to_row, torch.int32, (T * k,), "pair_to_row"),
                             _ptr(topk_w, torch.float32, (T, k), "topk_w"),
                             _ptr(y_shared, torch.float32, (T, H), "y_shared"),

@@ -5,14 +5,14 @@
 //   out[t, :] = sum_j w[t, j] * y_rows[pair_to_row[t*k + j], :] + y_shared[t, :]
 // fp32 accumulation, in slot order j = 0..k-1, so results are deterministic.
 // One block of 256 threads per (token, 2048-column slice); each thread moves
-// 8 contiguous columns (16-byte bf16 loads of each of the k rows).
+// 8 contiguous columns (16-byte loads of each of the k fp16 rows).
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_rows,
+__global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict__ y_rows,
                                                       const int32_t* __restrict__ pair_to_row,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ y_shared,
@@ -33,13 +33,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     for (int j = 0; j < k; ++j) {
         const int64_t r = pair_to_row[(int64_t)t * k + j];
         const float w = topk_w[(int64_t)t * k + j];
-        uint4 v = *(const uint4*)(y_rows + r * H + col);
-        uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        f16x8 v = *(const f16x8*)(y_rows + r * H + col);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += w * __uint_as_float(u[i] << 16);
-            acc[2 * i + 1] += w * __uint_as_float(u[i] & 0xffff0000u);
-        }
+        for (int i = 0; i < 8; ++i) acc[i] += w * (float)v[i];
     }
     if (OUT_BF16) {
         uint4 o;
@@ -61,10 +58,10 @@ hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const 
     if (T <= 0) return hipSuccess;
     dim3 grid(T, (H + 2047) / 2048);
     if (out_bf16)
-        combine_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)y_rows, pair_to_row, topk_w, y_shared,
+        combine_kernel<true><<<grid, 256, 0, s>>>((const _Float16*)y_rows, pair_to_row, topk_w, y_shared,
                                                   out, H, k);
     else
-        combine_kernel<false><<<grid, 256, 0, s>>>((const uint16_t*)y_rows, pair_to_row, topk_w, y_shared,
+        combine_kernel<false><<<grid, 256, 0, s>>>((const _Float16*)y_rows, pair_to_row, topk_w, y_shared,
                                                    out, H, k);
     return hipGetLastError();
 }

@@ -4,7 +4,7 @@
 //
 // used for the router logits (fp32 out), the routed experts' first
 // projection with the clipped SwiGLU fused into the epilogue (bf16 h out),
-// their second projection (bf16 rows out), and the shared expert.
+// their second projection (fp16 rows out), and the shared expert.
 //
 // Grouped mode: rows are the expert-major permuted rows; the tile plan maps
 // blockIdx.x to (expert g, first row of the tile); W_g = W + g * stride.  The
@@ -20,7 +20,7 @@
 
 namespace moe {
 
-enum { MODE_SWIGLU = 0, MODE_OUT_BF16 = 1, MODE_OUT_F32 = 2 };
+enum { MODE_SWIGLU = 0, MODE_OUT_F16 = 1, MODE_OUT_F32 = 2 };
 
 struct GemmParams {
     const uint16_t* A;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_kernel(Gem
                         if (MODE == MODE_OUT_F32)
                             ((float*)p.C)[(int64_t)row * p.N + col] = acc[i][j][v];
                         else
-                            ((uint16_t*)p.C)[(int64_t)row * p.N + col] = f32_to_bf16(acc[i][j][v]);
+                            ((_Float16*)p.C)[(int64_t)row * p.N + col] = f32_to_f16_sat(acc[i][j][v]);
                     }
                 }
             }
@@ -266,6 +266,7 @@ hipError_t launch_gemm_swiglu(const void* A, const int32_t* a_rows, int a_div, c
 hipError_t launch_gemm_out(const void* A, const void* W, int64_t w_group_stride, void* C, bool c_fp32,
                            int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
                            int groups, int max_tiles, hipStream_t s) {
+    // c_fp32 == false: fp16 output (the routed experts' rows)
     GemmParams p = make_params(A, nullptr, 1, W, w_group_stride, C, M, N, K, 0.f, offsets,
                                tile_start, groups);
     const int gx = tile_start ? max_tiles : (M + BIG_BM - 1) / BIG_BM;
@@ -274,7 +275,7 @@ hipError_t launch_gemm_out(const void* A, const void* W, int64_t w_group_stride,
     if (c_fp32)
         gemm_kernel<BIG_BM, BIG_BN, 64, 64, MODE_OUT_F32><<<grid, 256, 0, s>>>(p);
     else
-        gemm_kernel<BIG_BM, BIG_BN, 64, 64, MODE_OUT_BF16><<<grid, 256, 0, s>>>(p);
+        gemm_kernel<BIG_BM, BIG_BN, 64, 64, MODE_OUT_F16><<<grid, 256, 0, s>>>(p);
     return hipGetLastError();
 }
 

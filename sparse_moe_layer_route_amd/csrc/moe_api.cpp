@@ -99,7 +99,7 @@ moe_status_t do_route(const moe_config_t* c, const Dims& d, const void* x, const
 size_t hidden_bytes(const Dims& d) { return (size_t)d.P * d.I * 2; }
 
 int max_tiles(const Dims& d) {
-    const int bm = moe::gemm_tile_m();
+    const int bm = moe::grouped_tile_m();
     return (int)((d.P + bm - 1) / bm) + d.E;
 }
 
@@ -107,9 +107,9 @@ int max_tiles(const Dims& d) {
 moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
                    const int32_t* r2p, const void* w13, void* h, char* ws, hipStream_t s) {
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::gemm_tile_m(), tile_start, s));
-    HIP_TRY(moe::launch_gemm_swiglu(x, r2p, d.k, w13, (int64_t)2 * d.I * d.H, h, (int)d.T, d.I, d.H,
-                                    c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::grouped_tile_m(), tile_start, s));
+    HIP_TRY(moe::launch_grouped_up(x, r2p, d.k, (int)d.T, w13, (int64_t)2 * d.I * d.H, h, (int)d.P, d.I, d.H,
+                                   c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
     return MOE_OK;
 }
 
@@ -118,9 +118,9 @@ moe_status_t do_down(const moe_config_t* c, const Dims& d, const void* h, const 
                      const void* w2, void* y_rows, char* ws, hipStream_t s) {
     (void)c;
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::gemm_tile_m(), tile_start, s));
-    HIP_TRY(moe::launch_gemm_out(h, w2, (int64_t)d.H * d.I, y_rows, false, (int)d.P, d.H, d.I, offsets,
-                                 tile_start, d.E, max_tiles(d), s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::grouped_tile_m(), tile_start, s));
+    HIP_TRY(moe::launch_grouped_down(h, w2, (int64_t)d.H * d.I, y_rows, false, (int)d.P, d.H, d.I, offsets,
+                                     tile_start, d.E, max_tiles(d), s));
     return MOE_OK;
 }
 
@@ -136,9 +136,9 @@ moe_status_t do_grouped(const moe_config_t* c, const Dims& d, const void* x, con
 moe_status_t do_shared(const moe_config_t* c, const Dims& d, const void* x, const void* ws13,
                        const void* ws2, float* y_sh, char* ws, hipStream_t s) {
     uint16_t* hs = (uint16_t*)ws;
-    HIP_TRY(moe::launch_gemm_swiglu(x, nullptr, 1, ws13, 0, hs, (int)d.T, d.Is, d.H, c->swiglu_limit_shared,
-                                    nullptr, nullptr, 1, 0, s));
-    HIP_TRY(moe::launch_gemm_out(hs, ws2, 0, y_sh, true, (int)d.T, d.H, d.Is, nullptr, nullptr, 1, 0, s));
+    HIP_TRY(moe::launch_grouped_up(x, nullptr, 1, (int)d.T, ws13, 0, hs, (int)d.T, d.Is, d.H,
+                                   c->swiglu_limit_shared, nullptr, nullptr, 1, 0, s));
+    HIP_TRY(moe::launch_grouped_down(hs, ws2, 0, y_sh, true, (int)d.T, d.H, d.Is, nullptr, nullptr, 1, 0, s));
     return MOE_OK;
 }
 

@@ -10,6 +10,7 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -23,6 +24,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+// fp32 -> fp16, round to nearest even, finite values beyond the fp16 range
+// saturate to +-65504 (NaN stays NaN)
+__device__ __forceinline__ _Float16 f32_to_f16_sat(float f) {
+    const float m = 65504.0f;
+    float c = f > m ? m : (f < -m ? -m : f);
+    return (_Float16)c;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

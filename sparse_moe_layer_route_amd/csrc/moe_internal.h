@@ -32,11 +32,25 @@ hipError_t launch_gemm_swiglu(const void* A, const int32_t* a_rows, int a_div, c
                               int64_t w_group_stride, void* h, int M, int N, int K, float limit,
                               const int32_t* offsets, const int32_t* tile_start, int groups,
                               int max_tiles, hipStream_t s);
-// C[rows, N] = A[rows, K] . W^T with W [N, K] per group; C bf16 or fp32.
+// C[rows, N] = A[rows, K] . W^T with W [N, K] per group; C fp16 (saturating) or fp32.
 hipError_t launch_gemm_out(const void* A, const void* W, int64_t w_group_stride, void* C, bool c_fp32,
                            int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
                            int groups, int max_tiles, hipStream_t s);
 int gemm_tile_m();
+
+// Weight-streaming grouped GEMMs (256-row tiles, register-staged LDS ring).
+// Up: h[rows, N] bf16 = act(A[rows] . W13^T) with A rows gathered through
+// a_rows / a_div (clamped to a_nrows) or dense; W13 [2N, K] per group.
+// Down: C[rows, N] = A[rows, K] . W^T, C fp16 (saturating) or fp32.
+// K % 64 == 0; N % 64 == 0 (up) / any N (down).
+int grouped_tile_m();
+hipError_t launch_grouped_up(const void* A, const int32_t* a_rows, int a_div, int a_nrows, const void* W13,
+                             int64_t w_group_stride, void* h, int M, int N, int K, float limit,
+                             const int32_t* offsets, const int32_t* tile_start, int groups, int max_tiles,
+                             hipStream_t s);
+hipError_t launch_grouped_down(const void* A, const void* W, int64_t w_group_stride, void* C, bool c_fp32,
+                               int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
+                               int groups, int max_tiles, hipStream_t s);
 
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
