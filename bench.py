@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (scales HBM counters) and exit")
     return ap.parse_args()
 
 
@@ -82,6 +84,15 @@ def main():
     import sparse_moe_layer_route_amd as moe
 
     dev = "cuda"
+    if args.copy_calibration:
+        n = args.copy_calibration * 2**20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     moe.load()
     wl = mi.WORKLOADS[args.workload]
     cfg, T, k, E, H, I = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size, \

@@ -2,30 +2,35 @@
 //
 //   C[r, n] = sum_k A[src(r), k] * W_e[n, k]      for every row r of expert e
 //
-// Mode SWIGLU (first projection): the block's 128 weight rows are 64 gate
-// rows and the matching 64 up rows, and the epilogue writes
+// Mode SWIGLU (first projection): the block's 256 weight rows are 128 gate
+// rows and the matching 128 up rows, and the epilogue writes
 // h = act(gate, up, L) in bf16 (clipped SwiGLU).  Mode F16 / F32 (second
 // projection, shared expert): plain output.
 //
-// Shape of the work.  At the shapes of the layer the expert weights are
-// streamed from HBM once per M tile, so the M tile is 256 rows: with top-8
-// of 288-352 experts almost every expert fits one tile.  A block computes
-// 256 rows x 128 weight rows with 4 waves stacked along M (64 rows each);
-// MFMA 16-row sub-tiles past the expert's last row are skipped.
-//
-//   * B (weights): a ring of STAGES K-slices (64 wide) in LDS, filled by
-//     direct global->LDS loads (global_load_lds_dwordx4, one 1 KiB row group
-//     per wave instruction).  Each 128-byte row is stored with its eight
-//     16-byte chunks XOR-swizzled by (row & 7) so the fragment reads of 8
-//     consecutive rows hit 8 different bank groups.
-//   * A (activation rows): only the wave that owns a row uses it, so A goes
-//     straight from global memory (the gathered x row, or h) to registers in
-//     MFMA layout, prefetched one K-slice ahead.  No permuted copy of x is
-//     ever written.
-//   * K order inside a 64-wide slice: lane group g (lane >> 4) of MFMA step s
-//     takes chunk 2g+s, for A and B alike (a dot product does not care about
-//     the order of its terms), so each lane's A data for a slice are 32
-//     contiguous bytes.
+// Block tile: 256 rows x 256 weight rows, K in slices of 32, 8 waves (two
+// per SIMD) as 4 along M x 2 along N, each wave 64 rows x 128 columns of
+// 16x16x32 bf16 MFMA tiles.  Choices, each measured on MI355X:
+//   * Global traffic per FLOP: the vector-memory path of a CU takes about
+//     64 B/clk; a 256 x 256 tile needs ~32 B/clk at the full MFMA rate
+//     (a 256 x 128 tile needs ~48 and ran at about half the MFMA rate).
+//   * Operands go global -> LDS by direct DMA (global_load_lds_dwordx4), so
+//     no registers stage them.  The DMA is issued from inline asm and its
+//     completion is waited for explicitly (s_waitcnt vmcnt before the
+//     barrier of the step that reads it): the compiler cannot tell which LDS
+//     reads depend on which DMA and would otherwise wait for all of them at
+//     every step.  The instruction has no destination register.
+//   * LDS holds A and B in MFMA fragment order: a fragment (16 rows x 32 k)
+//     is 1 KiB with lane l's 16 bytes at 16*l, so each DMA instruction
+//     writes and each fragment read reads one contiguous 1 KiB (a contiguous
+//     1 KiB ds_read_b128 runs at twice the rate of any 16-rows-by-16-bytes
+//     pattern).  Lane l of a fragment covers row (l & 15), k-chunk (l >> 4).
+//   * 4 LDS stages of 32 KiB (16 A + 16 B fragments); slices are loaded 3
+//     steps ahead.
+//   * 16-row tiles are dealt to the waves along M round-robin (tile t to
+//     wave t % 4), so an expert's valid rows spread evenly over the SIMDs;
+//     tiles past the expert's last row skip their MFMAs.
+//   * A rows are gathered straight from x by the DMA (row_to_pair / k); no
+//     permuted copy of x is written.
 //   * Work order: (expert, n-tile, m-tile) with m fastest, so the m-tiles of
 //     one expert's weight panel run together and share it in L2; each XCD
 //     (blocks b with b % 8 == x) takes a contiguous range of that list.
@@ -36,9 +41,14 @@ namespace moe {
 
 namespace gg {
 
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int TM = 4;    // 16-row MFMA tiles per wave (64 rows)
-constexpr int TN = 8;    // 16-col MFMA tiles per wave (128 cols)
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int NW = 8;                 // waves per block: 4 along M x 2 along N
+constexpr int NT = NW * 64;           // threads per block
+constexpr int TM = 4;                 // 16-row tiles per wave (tiles wm, wm+4, wm+8, wm+12)
+constexpr int TN = 8;                 // 16-col tiles per wave (128 columns)
+constexpr int STAGES = 4;
+constexpr int FRAG = 1024;            // bytes per fragment
+constexpr int STAGE_BYTES = 32 * FRAG;   // 16 A + 16 B fragments
 constexpr int NXCD = 8;
 
 enum { SWIGLU = 0, OUT_F16 = 1, OUT_F32 = 2 };
@@ -61,20 +71,28 @@ struct Params {
     int n_tiles;                // BN tiles along N (SWIGLU: of 2N weight rows)
 };
 
-// Register rings: B slices are loaded RING-1 ahead into registers and
-// written to the LDS double buffer one slice ahead of use; A slices are
-// loaded RING-1 ahead.  The K loop is unrolled by RING so every ring slot
-// is a compile-time register set.
-constexpr int RING = 3;
-constexpr int B_CHUNKS = BN * BK / 8 / 256;   // 16-byte chunks per thread per slice (4)
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// one 1 KiB fragment: lane l's 16 bytes from g land at LDS byte lds_off + 16*l
+__device__ __forceinline__ void dma_frag(const void* g, unsigned lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g) : "memory");
+}
+
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+__global__ __launch_bounds__(NT, 1) void kernel(Params p) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
 
     // ---- decode the work item ------------------------------------------
     int g = 0, m_tile, n_tile, row0, row_end;
@@ -118,40 +136,48 @@ __global__ __launch_bounds__(256, 1) void kernel(Params p) {
     const int K = p.K;
     const uint16_t* Wg = p.W + (int64_t)g * p.w_group_stride;
 
-    // ---- B: this thread's 4 chunks of each 128 x 64 slice ------------------
-    const uint16_t* bsrc[B_CHUNKS];
-    int bdst[B_CHUNKS];
+    // ---- DMA sources: wave w loads A fragments 2w, 2w+1 and B fragments
+    // 2w, 2w+1 of every slice; lane l takes row 16j + (l & 15), chunk l >> 4
+    const uint16_t* src[4];
 #pragma unroll
-    for (int q = 0; q < B_CHUNKS; ++q) {
-        const int c = tid + 256 * q;
-        const int r = c >> 3, kc = c & 7;             // tile row, k-chunk
+    for (int q = 0; q < 2; ++q) {
+        const int j = 2 * wave + q;                       // 16-row tile 0..15
+        const int r = 16 * j + (lane & 15);               // tile row 0..255
+        // A: the gathered activation row (clamped inside the expert, and to A)
+        int ar = row0 + min(r, valid - 1);
+        if (p.a_rows) ar = min(max(p.a_rows[ar] / p.a_div, 0), p.a_nrows - 1);
+        src[q] = p.A + (int64_t)ar * K + (lane >> 4) * 8;
+        // B: weight row of tile column r
         int wrow;
         if (MODE == SWIGLU) {
-            const int hcol = min(n_tile * (BN / 2) + (r & 63), p.N - 1);
-            wrow = (r < 64) ? hcol : p.N + hcol;
+            // columns [128 wn', 128 wn' + 128): 64 gate then the matching 64 up
+            const int half = r >> 7, u = r & 127;
+            const int hcol = min(n_tile * (BN / 2) + 64 * half + (u & 63), p.N - 1);
+            wrow = (u < 64) ? hcol : p.N + hcol;
         } else {
             wrow = min(n_tile * BN + r, p.N - 1);
         }
-        bsrc[q] = Wg + (int64_t)wrow * K + kc * 8;
-        bdst[q] = r * BK + ((kc ^ (r & 7)) << 3);     // swizzled slot
+        src[2 + q] = Wg + (int64_t)wrow * K + (lane >> 4) * 8;
     }
-
-    // ---- A: per-lane row pointers (rows of this wave) ---------------------
-    const int g4 = lane >> 4;                         // lane group: chunks 2*g4, 2*g4+1
-    int n_i = (valid - 64 * wave + 15) >> 4;          // valid 16-row tiles of this wave
-    n_i = n_i < 0 ? 0 : (n_i > TM ? TM : n_i);
-    n_i = __builtin_amdgcn_readfirstlane(n_i);        // wave-uniform: scalar branches
-    const uint16_t* asrc[TM];
+    const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
+    // LDS byte offsets of this wave's 4 fragments within a stage
+    const unsigned frag_off[4] = {(unsigned)(2 * wave) * FRAG, (unsigned)(2 * wave + 1) * FRAG,
+                                  (unsigned)(16 + 2 * wave) * FRAG, (unsigned)(17 + 2 * wave) * FRAG};
+    auto issue = [&](int kt, int stage) {
+        const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        int r = row0 + min(64 * wave + 16 * i + (lane & 15), valid - 1);
-        int src = r;
-        if (p.a_rows) src = min(max(p.a_rows[r] / p.a_div, 0), p.a_nrows - 1);
-        asrc[i] = p.A + (int64_t)src * K + g4 * 16;
-    }
+        for (int q = 0; q < 4; ++q)
+            dma_frag(src[q] + k0,
+                     __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE_BYTES + frag_off[q]));
+    };
 
-    u32x4 breg[RING][B_CHUNKS];
-    bf16x8 areg[RING][TM][2];
+    // valid 16-row tiles of this wave: tiles wm + 4 i with 16 (wm + 4 i) < valid
+    const int ntile_valid = (valid + 15) >> 4;
+    int n_i = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) n_i += (wm + 4 * i < ntile_valid) ? 1 : 0;
+    n_i = __builtin_amdgcn_readfirstlane(n_i);
+
     f32x4 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -159,78 +185,37 @@ __global__ __launch_bounds__(256, 1) void kernel(Params p) {
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / BK;
-    const int frow = lane & 15;
-
-#define GG_LOAD(J, KT)                                                              \
-    do {                                                                            \
-        const int k0_ = (KT) * BK;                                                  \
-        _Pragma("unroll") for (int q = 0; q < B_CHUNKS; ++q)                        \
-            breg[J][q] = *(const u32x4*)(bsrc[q] + k0_);                            \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) {                            \
-            areg[J][i][0] = *(const bf16x8*)(asrc[i] + k0_);                        \
-            areg[J][i][1] = *(const bf16x8*)(asrc[i] + k0_ + 8);                    \
-        }                                                                           \
-    } while (0)
-
-#define GG_STORE_B(J, BUF)                                                          \
-    do {                                                                            \
-        _Pragma("unroll") for (int q = 0; q < B_CHUNKS; ++q)                        \
-            *(u32x4*)(&Bs[BUF][bdst[q]]) = breg[J][q];                              \
-    } while (0)
-
-#define GG_COMPUTE(J, BUF)                                                          \
-    do {                                                                            \
-        const uint16_t* bs_ = Bs[BUF];                                              \
-        _Pragma("unroll") for (int s = 0; s < 2; ++s) {                             \
-            bf16x8 bfr[TN];                                                         \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j) {                        \
-                const int r = 16 * j + frow;                                        \
-                const int c = 2 * g4 + s;                                           \
-                bfr[j] = *(const bf16x8*)(bs_ + r * BK + ((c ^ (r & 7)) << 3));     \
-            }                                                                       \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i) {                        \
-                if (i < n_i) {                                                      \
-                    _Pragma("unroll") for (int j = 0; j < TN; ++j)                  \
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(        \
-                            areg[J][i][s], bfr[j], acc[i][j], 0, 0, 0);             \
-                }                                                                   \
-            }                                                                       \
-        }                                                                           \
-    } while (0)
-
-    // One K step: slice KT+RING-1 starts loading into the register slot that
-    // slice KT-1 used; slice KT (slot J = KT % RING) is computed from LDS
-    // buffer KT % 2; then slice KT+1 moves registers -> LDS buffer (KT+1) % 2
-    // (read in the previous step, which every wave has left), so the B loads
-    // of a slice have two steps to arrive.  Loads past the last slice re-read
-    // the last slice, so every step issues the same loads and the compiler's
-    // wait counts stay exact.
-#define GG_STEP(J, KT)                                                              \
-    do {                                                                            \
-        GG_LOAD(((J) + RING - 1) % RING, min((KT) + RING - 1, nk - 1));             \
-        GG_COMPUTE(J, (KT) & 1);                                                    \
-        GG_STORE_B(((J) + 1) % RING, ((KT) + 1) & 1);                               \
-        __syncthreads();                                                            \
-    } while (0)
-
-    // prologue: slices 0 .. RING-2 loading, slice 0 staged in LDS
+    // prologue: slices 0 .. STAGES-2 in flight (clamped re-reads past the end
+    // keep the per-step DMA count fixed, which the waits below rely on)
 #pragma unroll
-    for (int j = 0; j < RING - 1; ++j) GG_LOAD(j, min(j, nk - 1));
-    GG_STORE_B(0, 0);
-    __syncthreads();
+    for (int s = 0; s < STAGES - 1; ++s) issue(min(s, nk - 1), s);
 
-    int kt = 0;
-    for (; kt + RING <= nk; kt += RING) {
-        GG_STEP(0, kt);
-        GG_STEP(1, kt + 1);
-        GG_STEP(2, kt + 2);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt % STAGES;
+        // slices kt+1, kt+2 (4 DMAs each) may stay in flight; slice kt has landed
+        wait_vm<4 * (STAGES - 2)>();
+        __builtin_amdgcn_s_barrier();
+        // every wave has finished reading the stage of slice kt-1: refill it
+        issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
+
+        const unsigned char* st = smem + stage * STAGE_BYTES;
+        bf16x8 bfr[TN], afr[TM];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            bfr[j] = *(const bf16x8*)(st + (16 + wn * TN + j) * FRAG + lane * 16);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)   // rows past the end hold clamped copies: reading them is safe
+            afr[i] = *(const bf16x8*)(st + (wm + 4 * i) * FRAG + lane * 16);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i < n_i) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr[j], acc[i][j], 0, 0, 0);
+            }
+        }
     }
-    if (kt < nk) GG_STEP(0, kt);
-    if (kt + 1 < nk) GG_STEP(1, kt + 1);
-#undef GG_STEP
-#undef GG_COMPUTE
-#undef GG_STORE_B
-#undef GG_LOAD
+    wait_vm<0>();
 
     // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + v ---
     const int ccol = lane & 15, crow = (lane >> 4) * 4;
@@ -241,10 +226,10 @@ __global__ __launch_bounds__(256, 1) void kernel(Params p) {
             if (i >= n_i) continue;
 #pragma unroll
             for (int j = 0; j < TN / 2; ++j) {
-                const int hcol = n_tile * (BN / 2) + 16 * j + ccol;
+                const int hcol = n_tile * (BN / 2) + 64 * wn + 16 * j + ccol;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int lr = 64 * wave + 16 * i + crow + v;
+                    const int lr = 16 * (wm + 4 * i) + crow + v;
                     if (lr < valid && hcol < p.N)
                         H[(int64_t)(row0 + lr) * p.N + hcol] =
                             f32_to_bf16(swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], p.limit));
@@ -257,10 +242,10 @@ __global__ __launch_bounds__(256, 1) void kernel(Params p) {
             if (i >= n_i) continue;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int col = n_tile * BN + 16 * j + ccol;
+                const int col = n_tile * BN + 128 * wn + 16 * j + ccol;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int lr = 64 * wave + 16 * i + crow + v;
+                    const int lr = 16 * (wm + 4 * i) + crow + v;
                     if (lr < valid && col < p.N) {
                         if (MODE == OUT_F32)
                             ((float*)p.C)[(int64_t)(row0 + lr) * p.N + col] = acc[i][j][v];
@@ -301,10 +286,10 @@ hipError_t launch_grouped_up(const void* A, const int32_t* a_rows, int a_div, in
     p.tile_start = tile_start;
     p.groups = groups;
     p.M = M;
-    p.n_tiles = (2 * N) / gg::BN;
+    p.n_tiles = (2 * N + gg::BN - 1) / gg::BN;
     const int64_t tiles = offsets ? max_tiles : (M + gg::BM - 1) / gg::BM;
     if (tiles <= 0) return hipSuccess;
-    gg::kernel<gg::SWIGLU><<<gg::grid_blocks(tiles * p.n_tiles), 256, 0, s>>>(p);
+    gg::kernel<gg::SWIGLU><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -329,9 +314,9 @@ hipError_t launch_grouped_down(const void* A, const void* W, int64_t w_group_str
     const int64_t tiles = offsets ? max_tiles : (M + gg::BM - 1) / gg::BM;
     if (tiles <= 0) return hipSuccess;
     if (c_fp32)
-        gg::kernel<gg::OUT_F32><<<gg::grid_blocks(tiles * p.n_tiles), 256, 0, s>>>(p);
+        gg::kernel<gg::OUT_F32><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
     else
-        gg::kernel<gg::OUT_F16><<<gg::grid_blocks(tiles * p.n_tiles), 256, 0, s>>>(p);
+        gg::kernel<gg::OUT_F16><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
     return hipGetLastError();
 }
 
