@@ -2,7 +2,7 @@
 //
 //   C[r, n] = sum_k A[src(r), k] * W_g[n, k]        (both operands K-contiguous)
 //
-// used for the router logits (fp32 out), the routed experts' first
+// used for the routed experts' first
 // projection with the clipped SwiGLU fused into the epilogue (bf16 h out),
 // their second projection (fp16 rows out), and the shared expert.
 //
@@ -276,22 +276,6 @@ hipError_t launch_gemm_out(const void* A, const void* W, int64_t w_group_stride,
         gemm_kernel<BIG_BM, BIG_BN, 64, 64, MODE_OUT_F32><<<grid, 256, 0, s>>>(p);
     else
         gemm_kernel<BIG_BM, BIG_BN, 64, 64, MODE_OUT_F16><<<grid, 256, 0, s>>>(p);
-    return hipGetLastError();
-}
-
-// Router logits: small token counts use 32x32 tiles so the expert dimension
-// spreads over many blocks; large ones use the 128x128 tile.
-hipError_t launch_router_logits(const void* x, const void* w_router, float* logits, int T, int E, int H,
-                                hipStream_t s) {
-    GemmParams p = make_params(x, nullptr, 1, w_router, 0, logits, T, E, H, 0.f, nullptr, nullptr, 1);
-    if (T <= 0) return hipSuccess;
-    if (T <= 512) {
-        dim3 grid((T + 31) / 32, (E + 31) / 32);
-        gemm_kernel<32, 32, 16, 16, MODE_OUT_F32><<<grid, 256, 0, s>>>(p);
-    } else {
-        dim3 grid((T + BIG_BM - 1) / BIG_BM, (E + BIG_BN - 1) / BIG_BN);
-        gemm_kernel<BIG_BM, BIG_BN, 64, 64, MODE_OUT_F32><<<grid, 256, 0, s>>>(p);
-    }
     return hipGetLastError();
 }
 

@@ -58,6 +58,25 @@ __device__ __forceinline__ T wave_sum(T v) {
     return v;
 }
 
+// Wave-wide max / min of a 32-bit unsigned value through DPP lane moves
+// (VALU only): quad permutes, row rotates, then row broadcasts 15 and 31
+// carry the result into lane 63, which is read back to every lane.
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, uint32_t d) { return v > d ? v : d; }
+__device__ __forceinline__ uint32_t dpp_min(uint32_t v, uint32_t d) { return v < d ? v : d; }
+
+#define MOE_DPP_REDUCE(OP, ID)                                                                        \
+    v = OP(v, (uint32_t)__builtin_amdgcn_update_dpp((int)(ID), (int)v, 0xB1, 0xF, 0xF, false));     \
+    v = OP(v, (uint32_t)__builtin_amdgcn_update_dpp((int)(ID), (int)v, 0x4E, 0xF, 0xF, false));     \
+    v = OP(v, (uint32_t)__builtin_amdgcn_update_dpp((int)(ID), (int)v, 0x124, 0xF, 0xF, false));    \
+    v = OP(v, (uint32_t)__builtin_amdgcn_update_dpp((int)(ID), (int)v, 0x128, 0xF, 0xF, false));    \
+    v = OP(v, (uint32_t)__builtin_amdgcn_update_dpp((int)(ID), (int)v, 0x142, 0xA, 0xF, false));    \
+    v = OP(v, (uint32_t)__builtin_amdgcn_update_dpp((int)(ID), (int)v, 0x143, 0xC, 0xF, false));    \
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { MOE_DPP_REDUCE(dpp_max, 0u) }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { MOE_DPP_REDUCE(dpp_min, 0xFFFFFFFFu) }
+#undef MOE_DPP_REDUCE
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {

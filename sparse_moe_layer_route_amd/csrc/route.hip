@@ -6,13 +6,14 @@
 //   ids = the k largest c, descending, ties to the lower index, NaN last
 //   w_j = s[ids_j]; if norm: w_j /= sum_j w_j; w_j *= scale
 //
-// Each lane holds up to 16 of the E <= 1024 scores in registers.  The order
-// is encoded in one 64-bit key per expert: the high word is the fp32 bit
-// pattern of c mapped to an unsigned order (negative values flipped, -0
-// folded into +0, NaN mapped to 0 so it ranks below every number), the low
-// word is ~index so that equal scores prefer the lower index.  Each of the k
-// rounds is a lane-local max followed by a 6-step xor-shuffle max across
-// the wave; the winner's owner lane retires it (key 0, below every live key).
+// Each lane holds up to 16 of the E <= 1024 scores in registers as 32-bit
+// order keys: the fp32 bit pattern of c mapped to an unsigned order
+// (negative values flipped, -0 folded into +0); NaN gets key 1, below every
+// number, and a retired expert key 0.  Each of the k rounds takes a
+// lane-local maximum (lowest index first among equal keys), a wave maximum
+// of the keys and then a wave minimum of the indices holding that key (the
+// lower-index tie-break), both as DPP reductions; the owner lane retires the
+// winner.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -20,15 +21,10 @@ namespace moe {
 
 constexpr int TOPK_MAX_PER_LANE = 16;   // E <= 1024
 
-__device__ __forceinline__ uint64_t order_key(float c, int e) {
-    uint32_t hi;
-    if (c != c) {
-        hi = 0u;                                   // NaN: lowest of all numbers
-    } else {
-        uint32_t u = __float_as_uint(c == 0.0f ? 0.0f : c);
-        hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    return ((uint64_t)hi << 32) | (uint64_t)(~(uint32_t)e);
+__device__ __forceinline__ uint32_t order_key(float c) {
+    if (c != c) return 1u;                                   // NaN: below every number
+    uint32_t u = __float_as_uint(c == 0.0f ? 0.0f : c);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);      // >= 0x007fffff for numbers
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
@@ -40,43 +36,44 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (t >= T) return;                            // whole wave leaves together
     const float* lg = logits + (int64_t)t * E;
 
-    uint64_t key[TOPK_MAX_PER_LANE];
+    uint32_t key[TOPK_MAX_PER_LANE];
     float sc[TOPK_MAX_PER_LANE];
 #pragma unroll
     for (int i = 0; i < TOPK_MAX_PER_LANE; ++i) {
-        int e = lane + 64 * i;
-        key[i] = 0;
+        const int e = lane + 64 * i;
+        key[i] = 0u;
         sc[i] = 0.f;
         if (e < E) {
-            float a = lg[e];
-            float s = 1.0f / (1.0f + expf(-a));
+            const float s = 1.0f / (1.0f + expf(-lg[e]));
             sc[i] = s;
-            key[i] = order_key(s + bias[e], e);
+            key[i] = order_key(s + bias[e]);
         }
     }
 
     float my_w = 0.f;   // lane j < k keeps the raw score of the j-th choice
     for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
-        float best_s = 0.f;
+        uint32_t bk = 0u;
+        int bi = 0;
+        float bs = 0.f;
 #pragma unroll
         for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
-            if (key[i] > best) { best = key[i]; best_s = sc[i]; }
-        uint64_t win = wave_max_u64(best);
-        int e = (int)(~(uint32_t)(win & 0xffffffffu));
+            if (key[i] > bk) { bk = key[i]; bi = i; bs = sc[i]; }
+        const uint32_t wmax = wave_max_u32(bk);
+        const uint32_t cand = (bk == wmax) ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu;
+        int e = (int)wave_min_u32(cand);
         e = min(max(e, 0), E - 1);                 // index guard
-        int owner = e & 63;
-        float s_win = __shfl(best_s, owner, kWave);
+        const int owner = e & 63;
+        const float s_win = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(bs), owner));
         if (lane == owner) {
 #pragma unroll
             for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
-                if (lane + 64 * i == e) key[i] = 0;
+                if (64 * i + lane == e) key[i] = 0u;
         }
         if (lane == j) my_w = s_win;
         if (lane == 0) ids[(int64_t)t * k + j] = e;
     }
-    float sum = wave_sum(lane < k ? my_w : 0.f);
-    float w = norm ? my_w / sum : my_w;
+    const float sum = wave_sum(lane < k ? my_w : 0.f);
+    const float w = norm ? my_w / sum : my_w;
     if (lane < k) wout[(int64_t)t * k + lane] = w * scale;
 }
 
