@@ -110,8 +110,11 @@ moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk
  * w13 [E,2I,H], w2 [E,H,I]: bf16, or E4M3FN codes with w13_scale
  * [E,2I/128,H/128] and w2_scale [E,H/128,I/128] fp32 (multiplying) when
  * expert_dtype is MOE_FP8_E4M3_B128 (miles page "Step-5-Preview", section
- * 1 Model Introduction); scales must be NULL for bf16.  In FP8 mode x and h
- * are quantised per (row, 128 columns) to E4M3FN with scale amax/448.
+ * 1 Model Introduction); scales must be NULL for bf16 and both non-NULL for
+ * FP8.  In FP8 mode x (per token) and h (per row) are quantised per 128
+ * columns to E4M3FN (round to nearest even) with scale amax/448, or 1 for an
+ * all-zero group, and both projections accumulate the exact code products
+ * of each 128-wide block in fp32 before applying the two scales.
  * y_rows [T*k, H] fp16 (round to nearest even, saturating at +-65504),
  * unweighted, in row order: fp16 keeps 11 significant bits for the same
  * bytes as bf16, so the rows add at most 2^-11 relative rounding. */
@@ -125,7 +128,8 @@ moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* 
  * apart (and for timing the first projection on its own).
  * moe_expert_up: h = act(W13[e] x[row_to_pair[r] / k], L) for every row r.
  *   h is [T*k, I] bf16 for bf16 experts; for FP8 experts it is [T*k, I]
- *   E4M3FN codes followed by [T*k, I/128] fp32 scales (moe_hidden_bytes()).
+ *   E4M3FN codes, then, at the next multiple of 256 bytes, fp32 scales laid
+ *   out block-major as [I/128][T*k] (moe_hidden_bytes() covers both).
  * moe_expert_down: y_rows[r] = W2[e] h[r] (h dequantised in FP8 mode). */
 moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t T, const void* x,
                            const int32_t* expert_offsets, const int32_t* row_to_pair,

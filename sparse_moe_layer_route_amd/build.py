@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
-SOURCES = ["moe_api.cpp", "router.hip", "route.hip", "permute.hip", "gemm.hip", "grouped_gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.cpp", "router.hip", "route.hip", "permute.hip", "gemm.hip", "grouped_gemm.hip", "fp8_gemm.hip",
+           "combine.hip"]
 
 # Packed fp32 VALU ops are disabled for the device code (hipcc-only flag).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -18,6 +18,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Dims {
     int64_t T, P;
     int H, E, k, I, Is;
+    bool fp8;
 };
 
 moe_status_t check_config(const moe_config_t* c, int64_t T) {
@@ -38,20 +39,36 @@ moe_status_t check_config(const moe_config_t* c, int64_t T) {
     if (c->top_k > 32 || c->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
     if (T * (int64_t)c->top_k >= ((int64_t)1 << 31) || T >= ((int64_t)1 << 31) / 8)
         return MOE_ERR_UNSUPPORTED;
-    if (c->expert_dtype == MOE_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;   // not built yet
+    if (c->expert_dtype == MOE_FP8_E4M3_B128 && (c->hidden_size % 128 || c->moe_intermediate_size % 128))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
+}
+
+// bf16 experts take no scales; FP8 experts need both
+moe_status_t check_scales(const moe_config_t* c, const float* s1, const float* s2) {
+    if (c->expert_dtype == MOE_BF16) return (s1 || s2) ? MOE_ERR_INVALID_ARGUMENT : MOE_OK;
+    return (s1 && s2) ? MOE_OK : MOE_ERR_INVALID_ARGUMENT;
 }
 
 Dims dims(const moe_config_t* c, int64_t T) {
     return Dims{T, T * c->top_k, c->hidden_size, c->num_experts, c->top_k, c->moe_intermediate_size,
-                c->share_expert_dim};
+                c->share_expert_dim, c->expert_dtype == MOE_FP8_E4M3_B128};
 }
 
 // scratch each step needs at the start of the workspace it is handed
 size_t route_ws(const Dims& d) { return align_up((size_t)d.T * d.E * 4); }
 size_t permute_ws(const Dims& d) { return align_up(moe::permute_scratch_bytes(d.P, d.E)); }
 size_t plan_ws(const Dims& d) { return align_up((size_t)(d.E + 1) * 4); }
-size_t grouped_ws(const Dims& d) { return plan_ws(d) + align_up((size_t)d.P * d.I * 2); }
+// FP8: x quantised per token, codes [T, H] then scales [H/128][T]
+size_t xq_bytes(const Dims& d) { return align_up((size_t)d.T * d.H); }
+size_t xq_ws(const Dims& d) { return d.fp8 ? xq_bytes(d) + align_up((size_t)(d.H / 128) * d.T * 4) : 0; }
+size_t up_ws(const Dims& d) { return plan_ws(d) + xq_ws(d); }
+// h: bf16 [P, I]; FP8: codes [P, I] then scales [I/128][P]
+size_t hcode_bytes(const Dims& d) { return align_up((size_t)d.P * d.I); }
+size_t hidden_bytes(const Dims& d) {
+    return d.fp8 ? hcode_bytes(d) + (size_t)(d.I / 128) * d.P * 4 : (size_t)d.P * d.I * 2;
+}
+size_t grouped_ws(const Dims& d) { return up_ws(d) + align_up(hidden_bytes(d)); }
 size_t shared_ws(const Dims& d) { return align_up((size_t)d.T * d.Is * 2); }
 
 // the whole layer: its own buffers followed by each step's scratch
@@ -96,18 +113,25 @@ moe_status_t do_route(const moe_config_t* c, const Dims& d, const void* x, const
     return MOE_OK;
 }
 
-size_t hidden_bytes(const Dims& d) { return (size_t)d.P * d.I * 2; }
+int tile_m(const Dims& d) { return d.fp8 ? moe::fp8_tile_m() : moe::grouped_tile_m(); }
 
-int max_tiles(const Dims& d) {
-    const int bm = moe::grouped_tile_m();
-    return (int)((d.P + bm - 1) / bm) + d.E;
-}
+// upper bound on the tiles of a grouped launch: every group may end in a partial tile
+int max_tiles(const Dims& d) { return (int)((d.P + tile_m(d) - 1) / tile_m(d)) + d.E; }
 
 // routed experts' first projection + clipped SwiGLU -> h
 moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
-                   const int32_t* r2p, const void* w13, void* h, char* ws, hipStream_t s) {
+                   const int32_t* r2p, const void* w13, const float* w13s, void* h, char* ws, hipStream_t s) {
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::grouped_tile_m(), tile_start, s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), tile_start, s));
+    if (d.fp8) {
+        char* xq = ws + plan_ws(d);
+        float* xs = (float*)(xq + xq_bytes(d));
+        float* hs = (float*)((char*)h + hcode_bytes(d));
+        HIP_TRY(moe::launch_quant_rows(x, (int)d.T, d.H, xq, xs, (int)d.T, s));
+        HIP_TRY(moe::launch_fp8_up(xq, xs, (int)d.T, r2p, d.k, (int)d.T, w13, w13s, h, hs, (int)d.P, d.I, d.H,
+                                   c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
+        return MOE_OK;
+    }
     HIP_TRY(moe::launch_grouped_up(x, r2p, d.k, (int)d.T, w13, (int64_t)2 * d.I * d.H, h, (int)d.P, d.I, d.H,
                                    c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
     return MOE_OK;
@@ -115,21 +139,27 @@ moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const in
 
 // routed experts' second projection -> y_rows
 moe_status_t do_down(const moe_config_t* c, const Dims& d, const void* h, const int32_t* offsets,
-                     const void* w2, void* y_rows, char* ws, hipStream_t s) {
+                     const void* w2, const float* w2s, void* y_rows, char* ws, hipStream_t s) {
     (void)c;
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, moe::grouped_tile_m(), tile_start, s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), tile_start, s));
+    if (d.fp8) {
+        const float* hs = (const float*)((const char*)h + hcode_bytes(d));
+        HIP_TRY(moe::launch_fp8_down(h, hs, (int)d.P, (int)d.P, w2, w2s, y_rows, d.H, d.I, offsets, tile_start,
+                                     d.E, max_tiles(d), s));
+        return MOE_OK;
+    }
     HIP_TRY(moe::launch_grouped_down(h, w2, (int64_t)d.H * d.I, y_rows, false, (int)d.P, d.H, d.I, offsets,
                                      tile_start, d.E, max_tiles(d), s));
     return MOE_OK;
 }
 
 moe_status_t do_grouped(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
-                        const int32_t* r2p, const void* w13, const void* w2, void* y_rows, char* ws,
-                        hipStream_t s) {
-    void* h = ws + align_up((size_t)(d.E + 1) * 4);
-    MOE_TRY(do_up(c, d, x, offsets, r2p, w13, h, ws, s));
-    MOE_TRY(do_down(c, d, h, offsets, w2, y_rows, ws, s));
+                        const int32_t* r2p, const void* w13, const float* w13s, const void* w2, const float* w2s,
+                        void* y_rows, char* ws, hipStream_t s) {
+    void* h = ws + up_ws(d);
+    MOE_TRY(do_up(c, d, x, offsets, r2p, w13, w13s, h, ws, s));
+    MOE_TRY(do_down(c, d, h, offsets, w2, w2s, y_rows, ws, s));
     return MOE_OK;
 }
 
@@ -181,36 +211,37 @@ moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* 
                                 const void* w2, const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
-    if (cfg->expert_dtype == MOE_BF16 && (w13_scale || w2_scale)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_scales(cfg, w13_scale, w2_scale));
     if (T == 0) return MOE_OK;
     if (!x || !expert_offsets || !row_to_pair || !w13 || !w2 || !y_rows || !ws) return MOE_ERR_INVALID_ARGUMENT;
     Dims d = dims(cfg, T);
     if (ws_bytes < grouped_ws(d)) return MOE_ERR_WORKSPACE;
-    return do_grouped(cfg, d, x, expert_offsets, row_to_pair, w13, w2, y_rows, (char*)ws, stream);
+    return do_grouped(cfg, d, x, expert_offsets, row_to_pair, w13, w13_scale, w2, w2_scale, y_rows, (char*)ws,
+                      stream);
 }
 
 moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t T, const void* x, const int32_t* expert_offsets,
                            const int32_t* row_to_pair, const void* w13, const float* w13_scale, void* h, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
-    if (cfg->expert_dtype == MOE_BF16 && w13_scale) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_scales(cfg, w13_scale, w13_scale));
     if (T == 0) return MOE_OK;
     if (!x || !expert_offsets || !row_to_pair || !w13 || !h || !ws) return MOE_ERR_INVALID_ARGUMENT;
     Dims d = dims(cfg, T);
-    if (ws_bytes < plan_ws(d)) return MOE_ERR_WORKSPACE;
-    return do_up(cfg, d, x, expert_offsets, row_to_pair, w13, h, (char*)ws, stream);
+    if (ws_bytes < up_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_up(cfg, d, x, expert_offsets, row_to_pair, w13, w13_scale, h, (char*)ws, stream);
 }
 
 moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t T, const void* h, const int32_t* expert_offsets,
                              const void* w2, const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
                              hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
-    if (cfg->expert_dtype == MOE_BF16 && w2_scale) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_scales(cfg, w2_scale, w2_scale));
     if (T == 0) return MOE_OK;
     if (!h || !expert_offsets || !w2 || !y_rows || !ws) return MOE_ERR_INVALID_ARGUMENT;
     Dims d = dims(cfg, T);
     if (ws_bytes < plan_ws(d)) return MOE_ERR_WORKSPACE;
-    return do_down(cfg, d, h, expert_offsets, w2, y_rows, (char*)ws, stream);
+    return do_down(cfg, d, h, expert_offsets, w2, w2_scale, y_rows, (char*)ws, stream);
 }
 
 moe_status_t moe_hidden_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes) {
@@ -246,7 +277,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
                                int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
-    if (cfg->expert_dtype == MOE_BF16 && (w13_scale || w2_scale)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_scales(cfg, w13_scale, w2_scale));
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !router_bias || !w13 || !w2 || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
     if (cfg->share_expert_dim > 0 && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARGUMENT;
@@ -266,7 +297,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
 
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, step, stream));
     HIP_TRY(moe::launch_permute(ids, (int)T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
-    MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w2, y_rows, step, stream));
+    MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w13_scale, w2, w2_scale, y_rows, step, stream));
     if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
     HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, out, cfg->out_dtype == MOE_BF16, (int)T, d.H, d.k, stream));
     return MOE_OK;

@@ -52,6 +52,23 @@ hipError_t launch_grouped_down(const void* A, const void* W, int64_t w_group_str
                                int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
                                int groups, int max_tiles, hipStream_t s);
 
+// FP8 E4M3 routed experts (128 x 128 block-scaled weights, activations
+// quantised per (row, 128 columns), 128-row tiles).
+// quant: xq[rows, H] E4M3 codes, xs[H/128][ld] fp32 scales (amax / 448).
+// up: hq[rows, N] codes + hs[N/128][hs_ld] scales of act(A . W13^T), A rows
+// gathered through a_rows / a_div; W13 [groups][2N, K] codes, w13s
+// [groups][2N/128][K/128].  down: y[rows, N] fp16 (saturating) = hq . W2^T.
+// K % 128 == 0, N % 128 == 0.
+int fp8_tile_m();
+hipError_t launch_quant_rows(const void* x, int rows, int H, void* xq, float* xs, int ld, hipStream_t s);
+hipError_t launch_fp8_up(const void* xq, const float* xs, int xs_ld, const int32_t* a_rows, int a_div,
+                         int a_nrows, const void* w13, const float* w13s, void* hq, float* hs, int hs_ld, int N,
+                         int K, float limit, const int32_t* offsets, const int32_t* tile_start, int groups,
+                         int max_tiles, hipStream_t s);
+hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows, const void* w2, const float* w2s,
+                           void* y, int N, int K, const int32_t* offsets, const int32_t* tile_start, int groups,
+                           int max_tiles, hipStream_t s);
+
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
                           const float* y_shared, void* out, bool out_bf16, int T, int H, int k,

@@ -136,3 +136,28 @@ def test_binding_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError, match="GPU tensor"):
         moe.moe_route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"],
                       topk_ids=torch.empty(1), topk_w=torch.empty(1), ws=torch.empty(1))
+
+
+def test_fp8_shape_and_scale_rules(lib):
+    # FP8 experts need H and I multiples of 128
+    assert ws_size(cfg_of(expert_dtype="fp8", hidden_size=192), 8)[0] == 2
+    assert ws_size(cfg_of(expert_dtype="fp8", moe_intermediate_size=192), 8)[0] == 2
+    assert ws_size(cfg_of(expert_dtype="fp8"), 8)[0] == 0
+    c = ctypes.byref(cfg_of(expert_dtype="fp8"))
+    # FP8 experts need both scale tensors
+    assert lib.moe_grouped_swiglu(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                  None) == 1
+    assert lib.moe_expert_up(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_expert_down(c, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+
+
+def test_fp8_hidden_bytes(lib):
+    c = cfg_of(expert_dtype="fp8")
+    T = 100
+    n = ctypes.c_size_t()
+    assert lib.moe_hidden_bytes(ctypes.byref(c), T, ctypes.byref(n)) == 0
+    P, I = T * c.top_k, c.moe_intermediate_size
+    assert n.value == (P * I + 255) // 256 * 256 + (I // 128) * P * 4
+    cb = cfg_of()
+    assert lib.moe_hidden_bytes(ctypes.byref(cb), T, ctypes.byref(n)) == 0
+    assert n.value == P * I * 2

@@ -17,7 +17,7 @@ import torch
 import moe_inputs as mi
 import sparse_moe_layer_route_amd as moe
 from oracle import oracle as orc
-from parity import (TOL_BF16, check_counts, check_routing, exempt_tokens, max_err_over_rms)
+from parity import (TOL_BF16, TOL_FP8, check_counts, check_routing, exempt_tokens, max_err_over_rms)
 
 pytestmark = pytest.mark.gpu
 
@@ -223,3 +223,116 @@ def test_layer_full_size(name):
     err, rms = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
     say(f"  sampled {sample.size} tokens: max_err/rms = {err:.3e} (rms {rms:.3e})")
     assert err <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------------------
+# FP8 E4M3 routed experts (128 x 128 block scales): oracle in its FP8 mode
+
+FP8_SMALL = {
+    "fp8_tiny": dict(),
+    "fp8_ragged_130_tokens_20_experts": dict(T=130, num_experts=20, top_k=3),
+    "fp8_top1": dict(top_k=1, T=77),
+    "fp8_clip_stress": dict(x_scale=40.0),
+    "fp8_limits_off": dict(swiglu_limit=0.0, swiglu_limit_shared=0.0, x_scale=8.0),
+    # H = 384: the second projection's last 256-column tile is half outside
+    "fp8_half_tile_384": dict(hidden_size=384, moe_intermediate_size=256, share_expert_dim=128, T=300,
+                              num_experts=12, top_k=2),
+    # 66 K blocks in the first projection: the weight-scale registers are reloaded
+    "fp8_deep_k_66_blocks": dict(hidden_size=128 * 66, moe_intermediate_size=128, share_expert_dim=64, T=24,
+                                 num_experts=4, top_k=2),
+    "fp8_no_shared_bf16_out": dict(share_expert_dim=0, out_dtype="bf16", T=96),
+}
+
+
+def fp8_workload(name):
+    kw = dict(hidden_size=256, moe_intermediate_size=128, expert_dtype="fp8")
+    kw.update(FP8_SMALL[name])
+    return mi.workload("tiny", **kw)
+
+
+@pytest.mark.parametrize("name", list(FP8_SMALL))
+def test_layer_fp8_small(name):
+    wl = fp8_workload(name)
+    say(f"[layer_fp8_small] {name} T={wl.T} cfg={wl.cfg}")
+    inp = gpu_inputs(wl)
+    inp["x"][0] = 0.0                               # an all-zero row: every group's scale is 1
+    out, ids, w, counts = run_layer(wl, inp)
+    h = host(inp)
+    ref = orc.layer(wl.cfg, h)
+    _, _, _, corr = orc.route(wl.cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ex = check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], corr, wl.cfg.top_k)
+    check_counts(counts.cpu().numpy(), ref["ids"], ids.cpu().numpy(), ex, wl.cfg.num_experts)
+    keep = ~ex
+    err, rms = max_err_over_rms(out.float().cpu().numpy()[keep], ref["out"][keep])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e}), exempt tokens {int(ex.sum())}")
+    assert err <= TOL_FP8
+
+
+def test_fp8_expert_steps():
+    """moe_expert_up then moe_expert_down in FP8 mode: every routed row
+    against the oracle's per-expert output, and the split path equal to
+    moe_grouped_swiglu bit for bit."""
+    wl = fp8_workload("fp8_ragged_130_tokens_20_experts")
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    say("[fp8_expert_steps]")
+    inp = gpu_inputs(wl)
+    h_in = host(inp)
+    ws = moe.workspace(cfg, T)
+    ids, w = moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ws=ws)
+    counts, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws)
+    hbuf = moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], inp["w13_scale"], ws=ws)
+    y_split = moe.moe_expert_down(cfg, T, hbuf, offsets, inp["w2"], inp["w2_scale"], ws=ws)
+    y_fused = moe.moe_grouped_swiglu(cfg, inp["x"], offsets, r2p, inp["w13"], inp["w2"],
+                                     w13_scale=inp["w13_scale"], w2_scale=inp["w2_scale"], ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_split, y_fused)
+    # h scales: positive, one per (row, 128 columns), block-major after the codes
+    P, I = T * k, cfg.moe_intermediate_size
+    code_bytes = (P * I + 255) // 256 * 256
+    hs = hbuf[code_bytes:code_bytes + (I // 128) * P * 4].view(torch.float32).cpu().numpy()
+    assert np.all(hs > 0) and np.all(np.isfinite(hs))
+    ids_h = ids.cpu().numpy()
+    ref = orc.layer(cfg, h_in, want_parts=True)
+    _, _, _, corr = orc.route(cfg, h_in["x"], h_in["w_router"], h_in["router_bias"], want_scores=True)
+    ex = check_routing(ids_h, w.cpu().numpy(), ref["ids"], ref["w"], corr, k)
+    pairs = r2p.cpu().numpy()
+    t_of, j_of = pairs // k, pairs % k
+    keep = ~ex[t_of]
+    orc_slot = {(t, e): j for t in range(T) for j, e in enumerate(ref["ids"][t].tolist())}
+    ref_rows = np.stack([ref["y_routed"][t, orc_slot[(t, ids_h[t, j])]] for t, j in zip(t_of, j_of)])
+    err, _ = max_err_over_rms(y_split.float().cpu().numpy()[keep], ref_rows[keep])
+    say(f"  routed rows max_err/rms = {err:.3e}")
+    assert err <= TOL_FP8
+
+
+def test_fp8_deterministic():
+    wl = fp8_workload("fp8_ragged_130_tokens_20_experts")
+    inp = gpu_inputs(wl)
+    a = run_layer(wl, inp)
+    b = run_layer(wl, inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_layer_fp8_full_size():
+    wl = mi.WORKLOADS["step5_fp8_prefill"]
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    say(f"[layer_fp8_full] T={T} E={E} k={k} H={cfg.hidden_size} I={cfg.moe_intermediate_size}")
+    inp = gpu_inputs(wl)
+    out, ids, w, counts = run_layer(wl, inp)
+    say("  gpu done; copying inputs to host")
+    h = host(inp)
+    del inp
+    torch.cuda.empty_cache()
+    o_ids, o_w, _, corr = orc.route(cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ids_h = ids.cpu().numpy()
+    ex = check_routing(ids_h, w.cpu().numpy(), o_ids, o_w, corr, k)
+    check_counts(counts.cpu().numpy(), o_ids, ids_h, ex, E)
+    rng = np.random.default_rng(1)
+    cand = np.nonzero(~ex)[0]
+    sample = np.unique(np.concatenate([cand[:2], cand[-2:], rng.choice(cand, min(N_SAMPLE, cand.size),
+                                                                        replace=False)]))
+    ref = orc.layer(cfg, h, tokens=sample)
+    err, rms = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
+    say(f"  sampled {sample.size} tokens: max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_FP8
