@@ -33,6 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="step5_prefill")
     ap.add_argument("--decode-workload", default="step5_decode")
+    ap.add_argument("--fp8-workload", default="step5_fp8_prefill", help="'' to skip the FP8 report")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
@@ -64,6 +65,9 @@ def up_kernel_bytes(wl, touched):
     touched expert once, x once, h written once."""
     c = wl.cfg
     T, H, k, I = wl.T, c.hidden_size, c.top_k, c.moe_intermediate_size
+    if c.expert_dtype == "fp8":
+        # codes + block scales of W13; x read once (bf16); h codes + scales written
+        return touched * (2 * I * H + (2 * I // 128) * (H // 128) * 4) + T * H * 2 + T * k * (I + I // 128 * 4)
     return touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
 
 
@@ -97,6 +101,62 @@ def main():
     wl = mi.WORKLOADS[args.workload]
     cfg, T, k, E, H, I = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size, \
         wl.cfg.moe_intermediate_size
+    r = time_layer(args, wl, moe, torch, mi)
+    ms_step, up_ms, layer_fwd_ms, touched = r["ms_step"], r["up_ms"], r["layer_forward_ms"], r["touched"]
+    tok_s = T / (ms_step * 1e-3)
+    fl = layer_flops(wl, touched)
+    by = layer_bytes(wl, touched)
+    up_bytes = up_kernel_bytes(wl, touched)
+    up_achieved = up_bytes / (up_ms * 1e-3)
+    res = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3" if cfg.expert_dtype == "fp8" else "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "hidden_size": H, "num_experts": E, "top_k": k,
+                   "moe_intermediate_size": I, "share_expert_dim": cfg.share_expert_dim,
+                   "swiglu_limit": cfg.swiglu_limit, "swiglu_limit_shared": cfg.swiglu_limit_shared,
+                   "router_scaling_factor": cfg.router_scaling_factor, "experts_touched": touched,
+                   "parallelism": "single GPU"},
+        "tflops": fl / (ms_step * 1e-3) / 1e12,
+        "mfma_frac": fl / (ms_step * 1e-3) / BF16_PEAK,
+        "layer_gbs": by / (ms_step * 1e-3) / 1e9,
+        "hbm_frac": by / (ms_step * 1e-3) / HBM_PEAK,
+        "layer_roofline_frac": max(fl / BF16_PEAK, by / HBM_PEAK) / (ms_step * 1e-3),
+        "layer_forward_ms": layer_fwd_ms,
+        "roofline": {"kernel": "routed experts: first projection + clipped SwiGLU (moe_expert_up)",
+                     "bound": "hbm", "achieved": up_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": up_achieved / HBM_PEAK, "traffic": None, "avg_ms": up_ms,
+                     "algorithmic_bytes": up_bytes},
+    }
+
+    if args.fp8_workload:
+        wf = mi.WORKLOADS[args.fp8_workload]
+        rf = time_layer(args, wf, moe, torch, mi)
+        ub = up_kernel_bytes(wf, rf["touched"])
+        res["fp8"] = {"workload": wf.name, "experts_touched": rf["touched"], "ms_per_step": rf["ms_step"],
+                      "tokens_per_s": wf.T / (rf["ms_step"] * 1e-3),
+                      "tflops": layer_flops(wf, rf["touched"]) / (rf["ms_step"] * 1e-3) / 1e12,
+                      "layer_forward_ms": rf["layer_forward_ms"],
+                      "up_ms": rf["up_ms"], "up_gbs": ub / (rf["up_ms"] * 1e-3) / 1e9,
+                      "up_hbm_frac": ub / (rf["up_ms"] * 1e-3) / HBM_PEAK}
+
+    if not args.no_decode:
+        note(f"decode workload {args.decode_workload}")
+        res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
+
+    if not args.no_cpu_baseline:
+        note("CPU baseline (oracle on a token sample)")
+        res["cpu_baseline"] = cpu_baseline(args, wl, mi)
+
+    print(json.dumps(res), flush=True)
+
+
+def time_layer(args, wl, moe, torch, mi):
+    """Warm up, then time args.steps steps of the stepwise path (the routed
+    experts' first projection bracketed by HIP events on its stream), and the
+    same count of moe_layer_forward calls."""
+    dev = "cuda"
+    cfg, T, k, H = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.hidden_size
     note(f"generating {wl.name} inputs")
     inp = mi.make_inputs(wl, dev, seed=0)
     ws = moe.workspace(cfg, T)
@@ -107,21 +167,22 @@ def main():
     h = torch.empty(moe.moe_hidden_bytes(cfg, T), dtype=torch.uint8, device=dev)
     y_rows = torch.empty((T * k, H), dtype=torch.float16, device=dev)
     y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
+    s13, s2 = inp.get("w13_scale"), inp.get("w2_scale")
 
     def step(ev=None):
         moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ids, w, ws=ws, stream=stream)
         counts, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], h=h, ws=ws, stream=stream)
+        moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], s13, h=h, ws=ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], y_rows=y_rows, ws=ws, stream=stream)
+        moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], s2, y_rows=y_rows, ws=ws, stream=stream)
         moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], y_shared=y_sh, ws=ws, stream=stream)
         moe.moe_combine(cfg, y_rows, p2r, w, y_sh, out=out, stream=stream)
         return counts
 
-    note(f"warmup {args.warmup} + timed {args.steps} steps")
+    note(f"{wl.name}: warmup {args.warmup} + timed {args.steps} steps")
     for _ in range(args.warmup):
         counts = step()
     torch.cuda.synchronize()
@@ -146,44 +207,9 @@ def main():
     lw[1].record(stream)
     torch.cuda.synchronize()
     layer_fwd_ms = lw[0].elapsed_time(lw[1]) / args.steps
-
-    tok_s = T / (ms_step * 1e-3)
-    fl = layer_flops(wl, touched)
-    by = layer_bytes(wl, touched)
-    up_bytes = up_kernel_bytes(wl, touched)
-    up_achieved = up_bytes / (up_ms * 1e-3)
-    res = {
-        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": T, "hidden_size": H, "num_experts": E, "top_k": k,
-                   "moe_intermediate_size": I, "share_expert_dim": cfg.share_expert_dim,
-                   "swiglu_limit": cfg.swiglu_limit, "swiglu_limit_shared": cfg.swiglu_limit_shared,
-                   "router_scaling_factor": cfg.router_scaling_factor, "experts_touched": touched,
-                   "parallelism": "single GPU"},
-        "tflops": fl / (ms_step * 1e-3) / 1e12,
-        "mfma_frac": fl / (ms_step * 1e-3) / BF16_PEAK,
-        "layer_gbs": by / (ms_step * 1e-3) / 1e9,
-        "hbm_frac": by / (ms_step * 1e-3) / HBM_PEAK,
-        "layer_roofline_frac": max(fl / BF16_PEAK, by / HBM_PEAK) / (ms_step * 1e-3),
-        "layer_forward_ms": layer_fwd_ms,
-        "roofline": {"kernel": "routed experts: first projection + clipped SwiGLU (moe_expert_up)",
-                     "bound": "hbm", "achieved": up_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": up_achieved / HBM_PEAK, "traffic": None, "avg_ms": up_ms,
-                     "algorithmic_bytes": up_bytes},
-    }
-
-    if not args.no_decode:
-        del inp, ws, h, y_rows, y_sh, out
-        torch.cuda.empty_cache()
-        note(f"decode workload {args.decode_workload}")
-        res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
-
-    if not args.no_cpu_baseline:
-        note("CPU baseline (oracle on a token sample)")
-        res["cpu_baseline"] = cpu_baseline(args, wl, mi)
-
-    print(json.dumps(res), flush=True)
+    del inp, ws, h, y_rows, y_sh, out
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "up_ms": up_ms, "layer_forward_ms": layer_fwd_ms, "touched": touched}
 
 
 def bench_decode(args, wl, moe, torch):

@@ -10,22 +10,22 @@
 // Block tile: 256 rows x 256 weight rows, K in slices of 32, 8 waves (two
 // per SIMD) as 4 along M x 2 along N, each wave 64 rows x 128 columns of
 // 16x16x32 bf16 MFMA tiles.  Choices, each measured on MI355X:
-//   * Global traffic per FLOP: the vector-memory path of a CU takes about
-//     64 B/clk; a 256 x 256 tile needs ~32 B/clk at the full MFMA rate
-//     (a 256 x 128 tile needs ~48 and ran at about half the MFMA rate).
 //   * Operands go global -> LDS by direct DMA (global_load_lds_dwordx4), so
 //     no registers stage them.  The DMA is issued from inline asm and its
 //     completion is waited for explicitly (s_waitcnt vmcnt before the
 //     barrier of the step that reads it): the compiler cannot tell which LDS
 //     reads depend on which DMA and would otherwise wait for all of them at
 //     every step.  The instruction has no destination register.
-//   * LDS holds A and B in MFMA fragment order: a fragment (16 rows x 32 k)
-//     is 1 KiB with lane l's 16 bytes at 16*l, so each DMA instruction
-//     writes and each fragment read reads one contiguous 1 KiB (a contiguous
-//     1 KiB ds_read_b128 runs at twice the rate of any 16-rows-by-16-bytes
-//     pattern).  Lane l of a fragment covers row (l & 15), k-chunk (l >> 4).
-//   * 4 LDS stages of 32 KiB (16 A + 16 B fragments); slices are loaded 3
-//     steps ahead.
+//   * Address pattern: each group of 4 lanes reads 64 contiguous bytes of
+//     one row (16 rows per instruction).  Spreading 16 lanes over 16 rows
+//     instead ran the address unit at a quarter of this rate (17 vs 61
+//     B/clk per CU on L2-resident data).
+//   * LDS: a DMA block lands lane-consecutive (16 rows x 64 B); the 4 blocks
+//     of a 64-row group sit at offsets chosen so that the MFMA fragment
+//     reads (lane l: row l & 15, 16 bytes of chunk l >> 4) are free of bank
+//     conflicts in the LDS's 32-lane passes.
+//   * 4 LDS stages; the fragments of slice k+1 are read into registers
+//     while the MFMAs of slice k run.
 //   * 16-row tiles are dealt to the waves along M round-robin (tile t to
 //     wave t % 4), so an expert's valid rows spread evenly over the SIMDs;
 //     tiles past the expert's last row skip their MFMAs.
@@ -47,8 +47,13 @@ constexpr int NT = NW * 64;           // threads per block
 constexpr int TM = 4;                 // 16-row tiles per wave (tiles wm, wm+4, wm+8, wm+12)
 constexpr int TN = 8;                 // 16-col tiles per wave (128 columns)
 constexpr int STAGES = 4;
-constexpr int FRAG = 1024;            // bytes per fragment
-constexpr int STAGE_BYTES = 32 * FRAG;   // 16 A + 16 B fragments
+// One DMA block is 16 rows x 64 B.  The 4 blocks of a 64-row group start at
+// these byte offsets: 16-byte bank groups 0, 2, 16, 18 (mod 32), which makes
+// every 32-lane pass of a fragment read touch 32 distinct bank groups.
+__device__ constexpr int BLK_OFF[4] = {0, 1024 + 32, 2048 + 256, 3072 + 288};
+constexpr int GROUP = 3072 + 288 + 1024;   // 4 blocks = 64 rows of one K slice
+constexpr int OPERAND = 4 * GROUP;    // 256 rows
+constexpr int STAGE_BYTES = 2 * OPERAND;   // A then B
 constexpr int NXCD = 8;
 
 enum { SWIGLU = 0, OUT_F16 = 1, OUT_F32 = 2 };
@@ -85,7 +90,10 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-template <int MODE>
+// GROUPED: rows come in expert groups (offsets + tile plan); otherwise one
+// dense group of M rows (the shared expert).  Separate instances also keep
+// the two uses apart in kernel traces.
+template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
 
@@ -99,7 +107,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     {
         const int b = blockIdx.x;
         const int xcd = b % NXCD, slot = b / NXCD;
-        if (p.offsets) {
+        if (GROUPED) {
             const int ntiles = p.tile_start[p.groups];
             const int total = ntiles * p.n_tiles;
             const int per = (total + NXCD - 1) / NXCD;
@@ -136,17 +144,29 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     const int K = p.K;
     const uint16_t* Wg = p.W + (int64_t)g * p.w_group_stride;
 
-    // ---- DMA sources: wave w loads A fragments 2w, 2w+1 and B fragments
-    // 2w, 2w+1 of every slice; lane l takes row 16j + (l & 15), chunk l >> 4
+    // ---- DMA sources.  One DMA instruction moves a block of 16 rows x 64 B
+    // (one K slice of 32): lane l reads 16 B of row quad l >> 2 at chunk
+    // l & 3, so every 4 lanes read 64 contiguous bytes (the address unit
+    // then runs at ~4x the rate of 16 distinct rows per 16 lanes), and lands
+    // at LDS byte 16*l of the block.  Block b (0..3) of row group g (64 rows)
+    // holds tile rows 64g + 16t + 4b + i for quad 4t + i, so the 16 rows of
+    // a 16-row MFMA tile come 4 apiece from the 4 blocks; with the block
+    // offsets of BLK_OFF, each 32-lane pass of a ds_read_b128 hits 32
+    // distinct bank groups.  Wave w moves A blocks 2w, 2w+1 and B blocks
+    // 2w, 2w+1 of every slice.
     const uint16_t* src[4];
+    unsigned blk_off[4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int j = 2 * wave + q;                       // 16-row tile 0..15
-        const int r = 16 * j + (lane & 15);               // tile row 0..255
+        const int blk = 2 * wave + q;                     // 0..15
+        const int g4 = blk >> 2, b4 = blk & 3;
+        const int quad = lane >> 2;
+        const int r = 64 * g4 + 16 * (quad >> 2) + 4 * b4 + (quad & 3);   // tile row / column 0..255
+        const int chunk = lane & 3;
         // A: the gathered activation row (clamped inside the expert, and to A)
         int ar = row0 + min(r, valid - 1);
-        if (p.a_rows) ar = min(max(p.a_rows[ar] / p.a_div, 0), p.a_nrows - 1);
-        src[q] = p.A + (int64_t)ar * K + (lane >> 4) * 8;
+        if (GROUPED && p.a_rows) ar = min(max(p.a_rows[ar] / p.a_div, 0), p.a_nrows - 1);
+        src[q] = p.A + (int64_t)ar * K + chunk * 8;
         // B: weight row of tile column r
         int wrow;
         if (MODE == SWIGLU) {
@@ -157,19 +177,23 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         } else {
             wrow = min(n_tile * BN + r, p.N - 1);
         }
-        src[2 + q] = Wg + (int64_t)wrow * K + (lane >> 4) * 8;
+        src[2 + q] = Wg + (int64_t)wrow * K + chunk * 8;
+        blk_off[q] = g4 * GROUP + BLK_OFF[b4];
+        blk_off[2 + q] = OPERAND + g4 * GROUP + BLK_OFF[b4];
     }
     const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
-    // LDS byte offsets of this wave's 4 fragments within a stage
-    const unsigned frag_off[4] = {(unsigned)(2 * wave) * FRAG, (unsigned)(2 * wave + 1) * FRAG,
-                                  (unsigned)(16 + 2 * wave) * FRAG, (unsigned)(17 + 2 * wave) * FRAG};
     auto issue = [&](int kt, int stage) {
         const int k0 = kt * BK;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            dma_frag(src[q] + k0,
-                     __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE_BYTES + frag_off[q]));
+            dma_frag(src[q] + k0, __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE_BYTES + blk_off[q]));
     };
+    // LDS byte offset of this lane's 16 B in 16-row tile tau = 4g + t:
+    // g * GROUP + 256 t + lane_off (row r = lane & 15 from block r >> 2,
+    // quad 4t + (r & 3); chunk lane >> 4)
+    const int fr = lane & 15;
+    const unsigned lane_off = BLK_OFF[fr >> 2] + 64 * (fr & 3) + 16 * (lane >> 4);
+    auto tile_off = [&](int tau) { return (unsigned)((tau >> 2) * GROUP + 256 * (tau & 3)) + lane_off; };
 
     // valid 16-row tiles of this wave: tiles wm + 4 i with 16 (wm + 4 i) < valid
     const int ntile_valid = (valid + 15) >> 4;
@@ -184,36 +208,51 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
+    const int nk = K / BK;                      // even: K % 64 == 0
     // prologue: slices 0 .. STAGES-2 in flight (clamped re-reads past the end
     // keep the per-step DMA count fixed, which the waits below rely on)
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(min(s, nk - 1), s);
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int stage = kt % STAGES;
-        // slices kt+1, kt+2 (4 DMAs each) may stay in flight; slice kt has landed
-        wait_vm<4 * (STAGES - 2)>();
-        __builtin_amdgcn_s_barrier();
-        // every wave has finished reading the stage of slice kt-1: refill it
-        issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
-
+    // fragments of one slice, double-buffered in registers: the LDS reads of
+    // slice kt+1 are issued before the MFMAs of slice kt, so they overlap
+    bf16x8 fa[2][TM], fb[2][TN];
+    auto read_frags = [&](int stage, bf16x8* a, bf16x8* b) {
         const unsigned char* st = smem + stage * STAGE_BYTES;
-        bf16x8 bfr[TN], afr[TM];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bfr[j] = *(const bf16x8*)(st + (16 + wn * TN + j) * FRAG + lane * 16);
+        for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8*)(st + OPERAND + tile_off(wn * TN + j));
 #pragma unroll
         for (int i = 0; i < TM; ++i)   // rows past the end hold clamped copies: reading them is safe
-            afr[i] = *(const bf16x8*)(st + (wm + 4 * i) * FRAG + lane * 16);
+            a[i] = *(const bf16x8*)(st + tile_off(wm + 4 * i));
+    };
+    auto mfmas = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if (i < n_i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
             }
         }
+    };
+    // one step: slice kt's fragments are in registers (cur); make slice kt+1
+    // visible, refill the stage slice kt-1 used, read slice kt+1 (nxt), multiply
+    auto step = [&](int kt, const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb) {
+        // slices kt+2 .. kt+STAGES-2 (4 DMAs each) may stay in flight
+        wait_vm<4 * (STAGES - 3)>();
+        __builtin_amdgcn_s_barrier();
+        // every wave finished reading slice kt-1 (its MFMAs waited for them)
+        issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
+        read_frags((kt + 1 < nk ? kt + 1 : kt) % STAGES, na, nb);
+        mfmas(ca, cb);
+    };
+
+    wait_vm<4 * (STAGES - 2)>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(0, fa[0], fb[0]);
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, fa[0], fb[0], fa[1], fb[1]);
+        step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
     }
     wait_vm<0>();
 
@@ -289,7 +328,10 @@ hipError_t launch_grouped_up(const void* A, const int32_t* a_rows, int a_div, in
     p.n_tiles = (2 * N + gg::BN - 1) / gg::BN;
     const int64_t tiles = offsets ? max_tiles : (M + gg::BM - 1) / gg::BM;
     if (tiles <= 0) return hipSuccess;
-    gg::kernel<gg::SWIGLU><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
+    if (offsets)
+        gg::kernel<gg::SWIGLU, true><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
+    else
+        gg::kernel<gg::SWIGLU, false><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -313,10 +355,14 @@ hipError_t launch_grouped_down(const void* A, const void* W, int64_t w_group_str
     p.n_tiles = (N + gg::BN - 1) / gg::BN;
     const int64_t tiles = offsets ? max_tiles : (M + gg::BM - 1) / gg::BM;
     if (tiles <= 0) return hipSuccess;
-    if (c_fp32)
-        gg::kernel<gg::OUT_F32><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
-    else
-        gg::kernel<gg::OUT_F16><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
+    const int nb = gg::grid_blocks(tiles * p.n_tiles);
+    if (c_fp32) {
+        if (offsets) gg::kernel<gg::OUT_F32, true><<<nb, gg::NT, 0, s>>>(p);
+        else gg::kernel<gg::OUT_F32, false><<<nb, gg::NT, 0, s>>>(p);
+    } else {
+        if (offsets) gg::kernel<gg::OUT_F16, true><<<nb, gg::NT, 0, s>>>(p);
+        else gg::kernel<gg::OUT_F16, false><<<nb, gg::NT, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 
