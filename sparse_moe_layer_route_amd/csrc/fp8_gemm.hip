@@ -21,8 +21,9 @@
 //   * block tile 128 rows x 256 weight rows, K slices of 128 bytes (one
 //     scale block), 3-stage LDS ring filled by direct global->LDS DMA from
 //     inline asm with explicit vmcnt waits (see grouped_gemm.hip);
-//   * fragments of 16 rows x 128 bytes stored as two contiguous 1 KiB halves
-//     (lane l's bytes 16h..16h+15 of its 32 at half h, offset 16*l);
+//   * each DMA instruction moves 16 rows x 64 B with every 4 lanes reading
+//     64 contiguous bytes of one row, and LDS blocks sit at offsets that keep
+//     the MFMA fragment reads free of bank conflicts (as in grouped_gemm.hip);
 //   * 8 waves as 2 along M x 4 along N, each 64 rows (16-row tiles wm + 2i)
 //     x 64 columns; weight-block scales are wave-uniform scalar loads.
 // The first projection's epilogue applies the clipped SwiGLU, takes each
@@ -40,11 +41,16 @@ constexpr int BM = 128, BN = 256, BKB = 128;      // K slice = 128 bytes = one s
 constexpr int NW = 8, NT = NW * 64;
 constexpr int TM = 4, TN = 4;
 constexpr int STAGES = 3;
-constexpr int FRAG = 2048;                         // 16 rows x 128 bytes
-constexpr int A_BYTES = 8 * FRAG;                  // 128 rows
-constexpr int B_BYTES = 16 * FRAG;                 // 256 weight rows
+// A DMA block is 16 rows x 64 B (half of a 128-byte K slice).  The 4 blocks
+// of one (64-row group, half) start at these byte offsets: 16-byte bank
+// groups 0, 1, 16, 17 (mod 32), which keeps both 16-byte reads of every
+// 32-lane fragment pass free of bank conflicts.
+__device__ constexpr int BOFF[4] = {0, 1024 + 16, 2048 + 256, 3072 + 272};
+constexpr int GROUP = 3072 + 272 + 1024;
+constexpr int A_BYTES = 4 * GROUP;                 // 128 rows: 2 row groups x 2 halves
+constexpr int B_BYTES = 8 * GROUP;                 // 256 weight rows
 constexpr int SA_OFF = A_BYTES + B_BYTES;          // 128 row scales (two 256-byte DMAs)
-constexpr int STAGE_BYTES = SA_OFF + 1024;
+constexpr int STAGE_BYTES = SA_OFF + 512;
 constexpr int NXCD = 8;
 
 enum { SWIGLU = 0, OUT_F16 = 1 };
@@ -135,15 +141,29 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         return min(max(sr, 0), p.a_nrows - 1);
     };
 
-    // ---- DMA sources (at k = 0)
-    //  A: wave w loads fragment w (tile rows 16w..16w+15), both halves
-    //  B: wave w loads fragments 2w, 2w+1, both halves
-    //  SA: waves 0 and 1 load the scales of tile rows 64w + lane
-    const uint8_t* a_src = p.A + (int64_t)src_row(16 * wave + (lane & 15)) * K + (lane >> 4) * 32;
-    const uint8_t* b_src[2];
+    // ---- DMA sources (at k = 0).  Every 4 lanes read 64 contiguous bytes
+    // of one row (lane l: row quad l >> 2, 16 bytes at (l & 3) * 16 of the
+    // block's half); block b of row group g holds rows 64g + 16t + 4b + i
+    // for quad 4t + i.  Wave w moves A blocks 2w, 2w+1 and B blocks
+    // 4w .. 4w+3 of every slice; waves 0 and 1 also move the scales of tile
+    // rows 64w + lane.
+    const int quad = lane >> 2, chunk = lane & 3;
+    auto block_row = [&](int blk) { return 64 * (blk >> 3) + 16 * (quad >> 2) + 4 * (blk & 3) + (quad & 3); };
+    auto block_lds = [&](int blk) { return (blk >> 2) * GROUP + BOFF[blk & 3]; };
+    const uint8_t* a_src[2];
+    unsigned a_lds[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int r = 16 * (2 * wave + q) + (lane & 15);      // tile column 0..255
+        const int blk = 2 * wave + q;                           // 0..15: (row group, half, block)
+        a_src[q] = p.A + (int64_t)src_row(block_row(blk)) * K + 64 * ((blk >> 2) & 1) + 16 * chunk;
+        a_lds[q] = block_lds(blk);
+    }
+    const uint8_t* b_src[4];
+    unsigned b_lds[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int blk = 4 * wave + q;                           // 0..31
+        const int r = block_row(blk);                           // tile column 0..255
         int wrow;
         if (MODE == SWIGLU) {
             // 64-column wave groups: 32 gate columns, then the matching 32 up columns
@@ -153,7 +173,8 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         } else {
             wrow = min(n_tile * BN + r, p.N - 1);
         }
-        b_src[q] = Wg + (int64_t)wrow * K + (lane >> 4) * 32;
+        b_src[q] = Wg + (int64_t)wrow * K + 64 * ((blk >> 2) & 1) + 16 * chunk;
+        b_lds[q] = A_BYTES + block_lds(blk);
     }
     const float* sa_src = p.As + src_row(64 * (wave & 1) + lane);
 
@@ -162,16 +183,17 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         const int k0 = kt * BKB;
         const unsigned sb = lds_base + stage * STAGE_BYTES;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            dma16(a_src + k0 + 16 * h, __builtin_amdgcn_readfirstlane(sb + wave * FRAG + h * 1024));
+        for (int q = 0; q < 2; ++q) dma16(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                dma16(b_src[q] + k0 + 16 * h,
-                      __builtin_amdgcn_readfirstlane(sb + A_BYTES + (2 * wave + q) * FRAG + h * 1024));
+        for (int q = 0; q < 4; ++q) dma16(b_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + b_lds[q]));
         if (wave < 2) dma4(sa_src + (int64_t)kt * p.a_ld, __builtin_amdgcn_readfirstlane(sb + SA_OFF + 256 * wave));
     };
+    // LDS offset of this lane's 32 bytes (two 16-byte reads, +0 and +16) in
+    // 16-row tile tau = 4g + t: row r = lane & 15 from block r >> 2 of
+    // half (lane >> 5), bytes 32 * ((lane >> 4) & 1) of that half
+    const int fr = lane & 15;
+    const unsigned lane_off = (lane >> 5) * GROUP + BOFF[fr >> 2] + 64 * (fr & 3) + 32 * ((lane >> 4) & 1);
+    auto tile_off = [&](int tau) { return (unsigned)((tau >> 2) * 2 * GROUP + 256 * (tau & 3)) + lane_off; };
 
     const int ntile_valid = (valid + 15) >> 4;
     int n_i = 0;
@@ -229,16 +251,16 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         i32x8 bfr[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const unsigned char* f = st + A_BYTES + (4 * wn + j) * FRAG + lane * 16;
-            const u32x4 lo = *(const u32x4*)f, hi = *(const u32x4*)(f + 1024);
+            const unsigned char* f = st + A_BYTES + tile_off(4 * wn + j);
+            const u32x4 lo = *(const u32x4*)f, hi = *(const u32x4*)(f + 16);
             bfr[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if (i < n_i) {
                 const int tile = wm + 2 * i;
-                const unsigned char* f = st + tile * FRAG + lane * 16;
-                const u32x4 lo = *(const u32x4*)f, hi = *(const u32x4*)(f + 1024);
+                const unsigned char* f = st + tile_off(tile);
+                const u32x4 lo = *(const u32x4*)f, hi = *(const u32x4*)(f + 16);
                 const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 const f32x4 sa = *(const f32x4*)(sa_l + 16 * tile + crow);
                 const f32x4 sga = sa * swa, sgb = sa * swb;
