@@ -71,6 +71,31 @@ def up_kernel_bytes(wl, touched):
     return touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
 
 
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "routed_up_bf16_step5_prefill_hbm_counters.md")
+KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_layer_route_amd", "csrc",
+                          "grouped_gemm.hip")
+
+
+def counter_traffic(wl):
+    """HBM bytes per launch of the routed first projection from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a plain copy's
+    counts), or None when the summary is for another workload or the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    import re
+    if wl.name != "step5_prefill" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    t = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not t or not h:
+        return None
+    if hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest() != h.group(1):
+        return None
+    return int(t.group(1))
+
+
 def note(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -125,7 +150,7 @@ def main():
         "layer_forward_ms": layer_fwd_ms,
         "roofline": {"kernel": "routed experts: first projection + clipped SwiGLU (moe_expert_up)",
                      "bound": "hbm", "achieved": up_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": up_achieved / HBM_PEAK, "traffic": None, "avg_ms": up_ms,
+                     "frac": up_achieved / HBM_PEAK, "traffic": counter_traffic(wl), "avg_ms": up_ms,
                      "algorithmic_bytes": up_bytes},
     }
 

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
-SOURCES = ["moe_api.cpp", "router.hip", "route.hip", "permute.hip", "gemm.hip", "grouped_gemm.hip", "fp8_gemm.hip",
+SOURCES = ["moe_api.cpp", "router.hip", "route.hip", "permute.hip", "tile_plan.hip", "grouped_gemm.hip", "fp8_gemm.hip",
            "combine.hip"]
 
 # Packed fp32 VALU ops are disabled for the device code (hipcc-only flag).

@@ -25,20 +25,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
 // Tile plan for a grouped GEMM with BM-row tiles: tile_start[E+1].
 hipError_t launch_tile_plan(const int32_t* offsets, int E, int bm, int32_t* tile_start, hipStream_t s);
 
-// h[rows, N] bf16 = act(A[rows] . W13^T) where A rows are gathered
-// (a_rows[r] / a_div) or dense, W13 [2N, K] per group (gate rows first).
-// Grouped when offsets != nullptr (groups = E, tile_start from the plan).
-hipError_t launch_gemm_swiglu(const void* A, const int32_t* a_rows, int a_div, const void* W13,
-                              int64_t w_group_stride, void* h, int M, int N, int K, float limit,
-                              const int32_t* offsets, const int32_t* tile_start, int groups,
-                              int max_tiles, hipStream_t s);
-// C[rows, N] = A[rows, K] . W^T with W [N, K] per group; C fp16 (saturating) or fp32.
-hipError_t launch_gemm_out(const void* A, const void* W, int64_t w_group_stride, void* C, bool c_fp32,
-                           int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
-                           int groups, int max_tiles, hipStream_t s);
-int gemm_tile_m();
-
-// Weight-streaming grouped GEMMs (256-row tiles, register-staged LDS ring).
+// Weight-streaming grouped GEMMs (256-row tiles, direct-to-LDS DMA ring).
 // Up: h[rows, N] bf16 = act(A[rows] . W13^T) with A rows gathered through
 // a_rows / a_div (clamped to a_nrows) or dense; W13 [2N, K] per group.
 // Down: C[rows, N] = A[rows, K] . W^T, C fp16 (saturating) or fp32.
