@@ -4,6 +4,8 @@
 // mixture plus the shared expert's output):
 //   out[t, :] = sum_j w[t, j] * y_rows[pair_to_row[t*k + j], :] + y_shared[t, :]
 // fp32 accumulation, in slot order j = 0..k-1, so results are deterministic.
+// The shared expert's output comes as fp32 rows (y_shared) or, when it ran
+// inside the grouped expert launches, as fp16 rows (shared_rows).
 // One block of 256 threads per (token, 2048-column slice); each thread moves
 // 8 contiguous columns (16-byte loads of each of the k fp16 rows).
 #include "moe_device.h"
@@ -16,6 +18,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
                                                       const int32_t* __restrict__ pair_to_row,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ y_shared,
+                                                      const _Float16* __restrict__ shared_rows,
                                                       void* __restrict__ out, int H, int k) {
     const int t = blockIdx.x;
     const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
@@ -26,6 +29,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
         float4 a = ys[0], b = ys[1];
         acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
         acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+    } else if (shared_rows) {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        const f16x8 v = *(const f16x8*)(shared_rows + (int64_t)t * H + col);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = (float)v[i];
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -53,16 +61,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
 }
 
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
-                          const float* y_shared, void* out, bool out_bf16, int T, int H, int k,
-                          hipStream_t s) {
+                          const float* y_shared, const void* shared_rows, void* out, bool out_bf16, int T, int H,
+                          int k, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     dim3 grid(T, (H + 2047) / 2048);
     if (out_bf16)
         combine_kernel<true><<<grid, 256, 0, s>>>((const _Float16*)y_rows, pair_to_row, topk_w, y_shared,
-                                                  out, H, k);
+                                                  (const _Float16*)shared_rows, out, H, k);
     else
         combine_kernel<false><<<grid, 256, 0, s>>>((const _Float16*)y_rows, pair_to_row, topk_w, y_shared,
-                                                   out, H, k);
+                                                   (const _Float16*)shared_rows, out, H, k);
     return hipGetLastError();
 }
 

@@ -41,20 +41,36 @@ namespace moe {
 
 namespace gg {
 
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int NW = 8;                 // waves per block: 4 along M x 2 along N
+constexpr int BK = 32;
+constexpr int NW = 8;                 // waves per block
 constexpr int NT = NW * 64;           // threads per block
-constexpr int TM = 4;                 // 16-row tiles per wave (tiles wm, wm+4, wm+8, wm+12)
-constexpr int TN = 8;                 // 16-col tiles per wave (128 columns)
-constexpr int STAGES = 4;
+constexpr int TM = 4;                 // 16-row tiles per wave
 // One DMA block is 16 rows x 64 B.  The 4 blocks of a 64-row group start at
 // these byte offsets: 16-byte bank groups 0, 2, 16, 18 (mod 32), which makes
 // every 32-lane pass of a fragment read touch 32 distinct bank groups.
 __device__ constexpr int BLK_OFF[4] = {0, 1024 + 32, 2048 + 256, 3072 + 288};
 constexpr int GROUP = 3072 + 288 + 1024;   // 4 blocks = 64 rows of one K slice
-constexpr int OPERAND = 4 * GROUP;    // 256 rows
-constexpr int STAGE_BYTES = 2 * OPERAND;   // A then B
 constexpr int NXCD = 8;
+
+// Tile shapes (rows BM x weight rows BN):
+//   256 x 256 (prefill): 8 waves as 4 along M x 2 along N, each 64 x 128;
+//   64 x 256 (few rows per expert): 8 waves along N, each 64 x 32, so no
+//     DMA and no LDS go to rows that are not there;
+//   64 x 128 (few rows, plain output): 8 waves along N, each 64 x 16 -- twice
+//     the work items, for launches whose item count would leave a ragged
+//     last round on 256 CUs.
+template <int BM, int BN>
+struct Shape {
+    static constexpr int WM = BM / 64;                 // waves along M
+    static constexpr int WN = NW / WM;                 // waves along N
+    static constexpr int TN = BN / 16 / WN;            // 16-col tiles per wave
+    static constexpr int GW = BN / WN;                 // columns per wave
+    static constexpr int NA = BM / 16;                 // A DMA blocks per slice
+    static constexpr int NB = BN / 16;                 // B DMA blocks per slice
+    static constexpr int A_OPERAND = (BM / 64) * GROUP;
+    static constexpr int STAGE_BYTES = A_OPERAND + (BN / 64) * GROUP;
+    static constexpr int STAGES = BM == 256 ? 4 : 6;
+};
 
 enum { SWIGLU = 0, OUT_F16 = 1, OUT_F32 = 2 };
 
@@ -70,15 +86,22 @@ struct Params {
     int K;
     float limit;
     const int32_t* offsets;     // [groups+1] row offsets; nullptr: dense with M rows
-    const int32_t* tile_start;  // [groups+1] BM-tile plan (grouped)
+    const int32_t* tile_start;  // [groups+2] BM-tile plan (grouped)
     int groups;
     int M;                      // dense rows
     int n_tiles;                // BN tiles along N (SWIGLU: of 2N weight rows)
+    // optional extra group (index `groups`): extra_rows rows after
+    // offsets[groups], its own weights and clip limit -- the shared expert
+    // run in the same launch; when A is gathered (a_rows), the extra group's
+    // A row is row - offsets[groups] (the token) instead
+    int extra_rows;
+    const uint16_t* W_extra;
+    float limit_extra;
 };
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-// one 1 KiB fragment: lane l's 16 bytes from g land at LDS byte lds_off + 16*l
+// one 1 KiB block: lane l's 16 bytes from g land at LDS byte lds_off + 16*l
 __device__ __forceinline__ void dma_frag(const void* g, unsigned lds_off) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g) : "memory");
 }
@@ -91,16 +114,19 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // GROUPED: rows come in expert groups (offsets + tile plan); otherwise one
-// dense group of M rows (the shared expert).  Separate instances also keep
-// the two uses apart in kernel traces.
-template <int MODE, bool GROUPED>
+// dense group of M rows.  Separate instances also keep the uses apart in
+// kernel traces.
+template <int MODE, bool GROUPED, int BM, int BN>
 __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
+    using S = Shape<BM, BN>;
+    static_assert(MODE != SWIGLU || S::TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
+    constexpr int STAGES = S::STAGES, STAGE_BYTES = S::STAGE_BYTES, TN = S::TN;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / S::WN, wn = wave % S::WN;
 
     // ---- decode the work item ------------------------------------------
     int g = 0, m_tile, n_tile, row0, row_end;
@@ -108,14 +134,15 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         const int b = blockIdx.x;
         const int xcd = b % NXCD, slot = b / NXCD;
         if (GROUPED) {
-            const int ntiles = p.tile_start[p.groups];
+            const int ng = p.groups + (p.extra_rows > 0 ? 1 : 0);
+            const int ntiles = p.tile_start[ng];
             const int total = ntiles * p.n_tiles;
             const int per = (total + NXCD - 1) / NXCD;
             if (slot >= per) return;
             const int w = xcd * per + slot;
             if (w >= total) return;
-            // expert owning work item w: largest g with tile_start[g]*n_tiles <= w
-            int lo = 0, hi = p.groups - 1;
+            // group owning work item w: largest g with tile_start[g]*n_tiles <= w
+            int lo = 0, hi = ng - 1;
             while (lo < hi) {
                 int mid = (lo + hi + 1) >> 1;
                 if (p.tile_start[mid] * p.n_tiles <= w) lo = mid; else hi = mid - 1;
@@ -126,7 +153,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             n_tile = local / mt;
             m_tile = local % mt;
             row0 = p.offsets[g] + m_tile * BM;
-            row_end = p.offsets[g + 1];
+            row_end = g < p.groups ? p.offsets[g + 1] : p.offsets[g] + p.extra_rows;
         } else {
             const int mt = (p.M + BM - 1) / BM;
             const int total = mt * p.n_tiles;
@@ -140,9 +167,11 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             row_end = p.M;
         }
     }
+    const bool extra = GROUPED && g == p.groups;
     const int valid = min(row_end - row0, BM);
     const int K = p.K;
-    const uint16_t* Wg = p.W + (int64_t)g * p.w_group_stride;
+    const uint16_t* Wg = extra ? p.W_extra : p.W + (int64_t)g * p.w_group_stride;
+    const float limit = extra ? p.limit_extra : p.limit;
 
     // ---- DMA sources.  One DMA instruction moves a block of 16 rows x 64 B
     // (one K slice of 32): lane l reads 16 B of row quad l >> 2 at chunk
@@ -152,41 +181,57 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     // holds tile rows 64g + 16t + 4b + i for quad 4t + i, so the 16 rows of
     // a 16-row MFMA tile come 4 apiece from the 4 blocks; with the block
     // offsets of BLK_OFF, each 32-lane pass of a ds_read_b128 hits 32
-    // distinct bank groups.  Wave w moves A blocks 2w, 2w+1 and B blocks
-    // 2w, 2w+1 of every slice.
-    const uint16_t* src[4];
-    unsigned blk_off[4];
+    // distinct bank groups.  Wave w moves B blocks (BN/128) w + q and A blocks
+    // 2w, 2w+1 (BM 256) or A block w for w < 4 (BM 64) of every slice.
+    constexpr int A_PER_WAVE = S::NA >= NW ? S::NA / NW : 1;
+    const bool a_mine = S::NA >= NW || wave < S::NA;
+    const int quad = lane >> 2, chunk = lane & 3;
+    auto block_row = [&](int blk) { return 64 * (blk >> 2) + 16 * (quad >> 2) + 4 * (blk & 3) + (quad & 3); };
+    const uint16_t* a_src[A_PER_WAVE];
+    unsigned a_lds[A_PER_WAVE];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int blk = 2 * wave + q;                     // 0..15
-        const int g4 = blk >> 2, b4 = blk & 3;
-        const int quad = lane >> 2;
-        const int r = 64 * g4 + 16 * (quad >> 2) + 4 * b4 + (quad & 3);   // tile row / column 0..255
-        const int chunk = lane & 3;
-        // A: the gathered activation row (clamped inside the expert, and to A)
-        int ar = row0 + min(r, valid - 1);
-        if (GROUPED && p.a_rows) ar = min(max(p.a_rows[ar] / p.a_div, 0), p.a_nrows - 1);
-        src[q] = p.A + (int64_t)ar * K + chunk * 8;
-        // B: weight row of tile column r
+    for (int q = 0; q < A_PER_WAVE; ++q) {
+        const int blk = S::NA >= NW ? A_PER_WAVE * wave + q : min(wave, S::NA - 1);
+        // the gathered activation row (clamped inside the group, and to A)
+        int ar = row0 + min(block_row(blk), valid - 1);
+        if (GROUPED && p.a_rows) {
+            // gathered rows (first projection): pair / k, or the token itself
+            // for the extra group; otherwise A rows are the output rows
+            ar = extra ? ar - p.offsets[p.groups] : p.a_rows[ar] / p.a_div;
+            ar = min(max(ar, 0), p.a_nrows - 1);
+        }
+        a_src[q] = p.A + (int64_t)ar * K + chunk * 8;
+        a_lds[q] = (blk >> 2) * GROUP + BLK_OFF[blk & 3];
+    }
+    constexpr int B_PER_WAVE = S::NB / NW;
+    const uint16_t* b_src[B_PER_WAVE];
+    unsigned b_lds[B_PER_WAVE];
+#pragma unroll
+    for (int q = 0; q < B_PER_WAVE; ++q) {
+        const int blk = B_PER_WAVE * wave + q;            // 0 .. NB-1
+        const int r = block_row(blk);                     // tile column 0..255
         int wrow;
         if (MODE == SWIGLU) {
-            // columns [128 wn', 128 wn' + 128): 64 gate then the matching 64 up
-            const int half = r >> 7, u = r & 127;
-            const int hcol = min(n_tile * (BN / 2) + 64 * half + (u & 63), p.N - 1);
-            wrow = (u < 64) ? hcol : p.N + hcol;
+            // each wave's GW columns: GW/2 gate columns, then the matching GW/2 up columns
+            const int grp = r / S::GW, u = r % S::GW;
+            const int hcol = min(n_tile * (BN / 2) + (S::GW / 2) * grp + u % (S::GW / 2), p.N - 1);
+            wrow = (u < S::GW / 2) ? hcol : p.N + hcol;
         } else {
             wrow = min(n_tile * BN + r, p.N - 1);
         }
-        src[2 + q] = Wg + (int64_t)wrow * K + chunk * 8;
-        blk_off[q] = g4 * GROUP + BLK_OFF[b4];
-        blk_off[2 + q] = OPERAND + g4 * GROUP + BLK_OFF[b4];
+        b_src[q] = Wg + (int64_t)wrow * K + chunk * 8;
+        b_lds[q] = S::A_OPERAND + (blk >> 2) * GROUP + BLK_OFF[blk & 3];
     }
     const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
     auto issue = [&](int kt, int stage) {
         const int k0 = kt * BK;
+        const unsigned sb = lds_base + stage * STAGE_BYTES;
+        if (a_mine) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dma_frag(src[q] + k0, __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE_BYTES + blk_off[q]));
+            for (int q = 0; q < A_PER_WAVE; ++q) dma_frag(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
+        }
+#pragma unroll
+        for (int q = 0; q < B_PER_WAVE; ++q) dma_frag(b_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + b_lds[q]));
     };
     // LDS byte offset of this lane's 16 B in 16-row tile tau = 4g + t:
     // g * GROUP + 256 t + lane_off (row r = lane & 15 from block r >> 2,
@@ -195,11 +240,11 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     const unsigned lane_off = BLK_OFF[fr >> 2] + 64 * (fr & 3) + 16 * (lane >> 4);
     auto tile_off = [&](int tau) { return (unsigned)((tau >> 2) * GROUP + 256 * (tau & 3)) + lane_off; };
 
-    // valid 16-row tiles of this wave: tiles wm + 4 i with 16 (wm + 4 i) < valid
+    // valid 16-row tiles of this wave: tiles wm + WM i with 16 (wm + WM i) < valid
     const int ntile_valid = (valid + 15) >> 4;
     int n_i = 0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) n_i += (wm + 4 * i < ntile_valid) ? 1 : 0;
+    for (int i = 0; i < TM; ++i) n_i += (wm + S::WM * i < ntile_valid) ? 1 : 0;
     n_i = __builtin_amdgcn_readfirstlane(n_i);
 
     f32x4 acc[TM][TN];
@@ -220,10 +265,10 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     auto read_frags = [&](int stage, bf16x8* a, bf16x8* b) {
         const unsigned char* st = smem + stage * STAGE_BYTES;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8*)(st + OPERAND + tile_off(wn * TN + j));
+        for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8*)(st + S::A_OPERAND + tile_off(wn * TN + j));
 #pragma unroll
         for (int i = 0; i < TM; ++i)   // rows past the end hold clamped copies: reading them is safe
-            a[i] = *(const bf16x8*)(st + tile_off(wm + 4 * i));
+            a[i] = *(const bf16x8*)(st + tile_off(wm + S::WM * i));
     };
     auto mfmas = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
@@ -235,11 +280,13 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             }
         }
     };
+    // DMAs per slice of this wave: B_PER_WAVE + A_PER_WAVE if it moves A blocks
+    constexpr int D_HI = B_PER_WAVE + A_PER_WAVE, D_LO = S::NA >= NW ? D_HI : B_PER_WAVE;
     // one step: slice kt's fragments are in registers (cur); make slice kt+1
     // visible, refill the stage slice kt-1 used, read slice kt+1 (nxt), multiply
     auto step = [&](int kt, const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb) {
-        // slices kt+2 .. kt+STAGES-2 (4 DMAs each) may stay in flight
-        wait_vm<4 * (STAGES - 3)>();
+        // slices kt+2 .. kt+STAGES-2 may stay in flight
+        if (a_mine) wait_vm<D_HI * (STAGES - 3)>(); else wait_vm<D_LO * (STAGES - 3)>();
         __builtin_amdgcn_s_barrier();
         // every wave finished reading slice kt-1 (its MFMAs waited for them)
         issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
@@ -247,7 +294,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         mfmas(ca, cb);
     };
 
-    wait_vm<4 * (STAGES - 2)>();
+    if (a_mine) wait_vm<D_HI * (STAGES - 2)>(); else wait_vm<D_LO * (STAGES - 2)>();
     __builtin_amdgcn_s_barrier();
     read_frags(0, fa[0], fb[0]);
     for (int kt = 0; kt < nk; kt += 2) {
@@ -265,13 +312,13 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             if (i >= n_i) continue;
 #pragma unroll
             for (int j = 0; j < TN / 2; ++j) {
-                const int hcol = n_tile * (BN / 2) + 64 * wn + 16 * j + ccol;
+                const int hcol = n_tile * (BN / 2) + (S::GW / 2) * wn + 16 * j + ccol;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int lr = 16 * (wm + 4 * i) + crow + v;
+                    const int lr = 16 * (wm + S::WM * i) + crow + v;
                     if (lr < valid && hcol < p.N)
                         H[(int64_t)(row0 + lr) * p.N + hcol] =
-                            f32_to_bf16(swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], p.limit));
+                            f32_to_bf16(swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit));
                 }
             }
         }
@@ -281,10 +328,10 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             if (i >= n_i) continue;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int col = n_tile * BN + 128 * wn + 16 * j + ccol;
+                const int col = n_tile * BN + S::GW * wn + 16 * j + ccol;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int lr = 16 * (wm + 4 * i) + crow + v;
+                    const int lr = 16 * (wm + S::WM * i) + crow + v;
                     if (lr < valid && col < p.N) {
                         if (MODE == OUT_F32)
                             ((float*)p.C)[(int64_t)(row0 + lr) * p.N + col] = acc[i][j][v];
@@ -302,66 +349,75 @@ static int grid_blocks(int64_t work) {
     return (int)(per * NXCD);
 }
 
+template <int MODE, int BM, int BN>
+void launch(Params p, int64_t tiles, hipStream_t s) {
+    p.n_tiles = MODE == SWIGLU ? (2 * p.N + BN - 1) / BN : (p.N + BN - 1) / BN;
+    const int nb = grid_blocks(tiles * p.n_tiles);
+    if (p.offsets) kernel<MODE, true, BM, BN><<<nb, NT, 0, s>>>(p);
+    else kernel<MODE, false, BM, BN><<<nb, NT, 0, s>>>(p);
+}
+
 }  // namespace gg
 
-int grouped_tile_m() { return gg::BM; }
+int grouped_tile_m(int64_t rows, int groups) {
+    // 64-row tiles when the groups average under 48 rows (decode-like
+    // batches), else 256-row tiles
+    return rows < (int64_t)48 * groups ? 64 : 256;
+}
 
-hipError_t launch_grouped_up(const void* A, const int32_t* a_rows, int a_div, int a_nrows, const void* W13,
-                             int64_t w_group_stride, void* h, int M, int N, int K, float limit,
-                             const int32_t* offsets, const int32_t* tile_start, int groups, int max_tiles,
-                             hipStream_t s) {
+hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s) {
     gg::Params p{};
-    p.A = (const uint16_t*)A;
-    p.a_rows = a_rows;
-    p.a_div = a_div > 0 ? a_div : 1;
-    p.a_nrows = a_nrows;
-    p.W = (const uint16_t*)W13;
-    p.w_group_stride = w_group_stride;
-    p.C = h;
-    p.N = N;
-    p.K = K;
-    p.limit = limit;
-    p.offsets = offsets;
-    p.tile_start = tile_start;
-    p.groups = groups;
-    p.M = M;
-    p.n_tiles = (2 * N + gg::BN - 1) / gg::BN;
-    const int64_t tiles = offsets ? max_tiles : (M + gg::BM - 1) / gg::BM;
+    p.A = (const uint16_t*)a.A;
+    p.a_rows = a.a_rows;
+    p.a_div = a.a_div > 0 ? a.a_div : 1;
+    p.a_nrows = a.a_nrows;
+    p.W = (const uint16_t*)a.W;
+    p.w_group_stride = a.w_group_stride;
+    p.C = a.C;
+    p.N = a.N;
+    p.K = a.K;
+    p.limit = a.limit;
+    p.offsets = a.offsets;
+    p.tile_start = a.tile_start;
+    p.groups = a.groups;
+    p.M = a.M;
+    p.extra_rows = a.extra_rows;
+    p.W_extra = (const uint16_t*)a.W_extra;
+    p.limit_extra = a.limit_extra;
+    const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
-    if (offsets)
-        gg::kernel<gg::SWIGLU, true><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
-    else
-        gg::kernel<gg::SWIGLU, false><<<gg::grid_blocks(tiles * p.n_tiles), gg::NT, 0, s>>>(p);
+    if (a.bm == 64) gg::launch<gg::SWIGLU, 64, 256>(p, tiles, s);
+    else gg::launch<gg::SWIGLU, 256, 256>(p, tiles, s);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_down(const void* A, const void* W, int64_t w_group_stride, void* C, bool c_fp32,
-                               int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
-                               int groups, int max_tiles, hipStream_t s) {
+hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s) {
     gg::Params p{};
-    p.A = (const uint16_t*)A;
+    p.A = (const uint16_t*)a.A;
     p.a_rows = nullptr;
     p.a_div = 1;
-    p.a_nrows = M;
-    p.W = (const uint16_t*)W;
-    p.w_group_stride = w_group_stride;
-    p.C = C;
-    p.N = N;
-    p.K = K;
-    p.offsets = offsets;
-    p.tile_start = tile_start;
-    p.groups = groups;
-    p.M = M;
-    p.n_tiles = (N + gg::BN - 1) / gg::BN;
-    const int64_t tiles = offsets ? max_tiles : (M + gg::BM - 1) / gg::BM;
+    p.a_nrows = a.a_nrows;
+    p.W = (const uint16_t*)a.W;
+    p.w_group_stride = a.w_group_stride;
+    p.C = a.C;
+    p.N = a.N;
+    p.K = a.K;
+    p.offsets = a.offsets;
+    p.tile_start = a.tile_start;
+    p.groups = a.groups;
+    p.M = a.M;
+    p.extra_rows = a.extra_rows;
+    p.W_extra = (const uint16_t*)a.W_extra;
+    const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
-    const int nb = gg::grid_blocks(tiles * p.n_tiles);
+    // 64-row tiles: 128-column tiles double the work items of these
+    // (HBM-bound) launches, which evens out the last round on 256 CUs
     if (c_fp32) {
-        if (offsets) gg::kernel<gg::OUT_F32, true><<<nb, gg::NT, 0, s>>>(p);
-        else gg::kernel<gg::OUT_F32, false><<<nb, gg::NT, 0, s>>>(p);
+        if (a.bm == 64) gg::launch<gg::OUT_F32, 64, 128>(p, tiles, s);
+        else gg::launch<gg::OUT_F32, 256, 256>(p, tiles, s);
     } else {
-        if (offsets) gg::kernel<gg::OUT_F16, true><<<nb, gg::NT, 0, s>>>(p);
-        else gg::kernel<gg::OUT_F16, false><<<nb, gg::NT, 0, s>>>(p);
+        if (a.bm == 64) gg::launch<gg::OUT_F16, 64, 128>(p, tiles, s);
+        else gg::launch<gg::OUT_F16, 256, 256>(p, tiles, s);
     }
     return hipGetLastError();
 }

@@ -56,9 +56,9 @@ Dims dims(const moe_config_t* c, int64_t T) {
 }
 
 // scratch each step needs at the start of the workspace it is handed
-size_t route_ws(const Dims& d) { return align_up((size_t)d.T * d.E * 4); }
+size_t route_ws(const Dims& d) { return align_up((size_t)moe::router_splits(d.T, d.H) * d.T * d.E * 4); }
 size_t permute_ws(const Dims& d) { return align_up(moe::permute_scratch_bytes(d.P, d.E)); }
-size_t plan_ws(const Dims& d) { return align_up((size_t)(d.E + 1) * 4); }
+size_t plan_ws(const Dims& d) { return align_up((size_t)(d.E + 2) * 4); }
 // FP8: x quantised per token, codes [T, H] then scales [H/128][T]
 size_t xq_bytes(const Dims& d) { return align_up((size_t)d.T * d.H); }
 size_t xq_ws(const Dims& d) { return d.fp8 ? xq_bytes(d) + align_up((size_t)(d.H / 128) * d.T * 4) : 0; }
@@ -71,12 +71,18 @@ size_t hidden_bytes(const Dims& d) {
 size_t grouped_ws(const Dims& d) { return up_ws(d) + align_up(hidden_bytes(d)); }
 size_t shared_ws(const Dims& d) { return align_up((size_t)d.T * d.Is * 2); }
 
+// The whole layer runs the shared expert inside the routed experts' grouped
+// launches (as one more group of T rows) when it has their width and dtype.
+bool fuse_shared(const Dims& d) { return !d.fp8 && d.Is > 0 && d.Is == d.I; }
+
 // the whole layer: its own buffers followed by each step's scratch
 struct LayerWs {
-    size_t ids, w, counts, offsets, r2p, p2r, y_rows, y_sh, step, total;
+    size_t ids, w, counts, offsets, r2p, p2r, plan, y_rows, y_sh, step, total;
 };
 
 LayerWs layer_ws(const Dims& d) {
+    const bool fuse = fuse_shared(d);
+    const int64_t rows = d.P + (fuse ? d.T : 0);      // routed rows, then the shared expert's
     LayerWs L;
     size_t o = 0;
     L.ids = o;     o += align_up((size_t)d.P * 4);
@@ -85,10 +91,12 @@ LayerWs layer_ws(const Dims& d) {
     L.offsets = o; o += align_up((size_t)(d.E + 1) * 4);
     L.r2p = o;     o += align_up((size_t)d.P * 4);
     L.p2r = o;     o += align_up((size_t)d.P * 4);
-    L.y_rows = o;  o += align_up((size_t)d.P * d.H * 2);
-    L.y_sh = o;    o += d.Is > 0 ? align_up((size_t)d.T * d.H * 4) : 0;
+    L.plan = o;    o += plan_ws(d);
+    L.y_rows = o;  o += align_up((size_t)rows * d.H * 2);
+    L.y_sh = o;    o += (d.Is > 0 && !fuse) ? align_up((size_t)d.T * d.H * 4) : 0;
     L.step = o;
-    o += std::max(std::max(route_ws(d), permute_ws(d)), std::max(grouped_ws(d), shared_ws(d)));
+    const size_t grouped = fuse ? align_up((size_t)rows * d.I * 2) : grouped_ws(d);
+    o += std::max(std::max(route_ws(d), permute_ws(d)), std::max(grouped, shared_ws(d)));
     L.total = o;
     return L;
 }
@@ -108,21 +116,78 @@ moe_status_t do_route(const moe_config_t* c, const Dims& d, const void* x, const
                       int32_t* ids, float* w, char* ws, hipStream_t s) {
     float* logits = (float*)ws;
     HIP_TRY(moe::launch_router_logits(x, wr, logits, (int)d.T, d.E, d.H, s));
-    HIP_TRY(moe::launch_topk(logits, b, (int)d.T, d.E, d.k, c->router_scaling_factor, c->norm_expert_weight,
-                             ids, w, s));
+    HIP_TRY(moe::launch_topk(logits, moe::router_splits(d.T, d.H), b, (int)d.T, d.E, d.k,
+                             c->router_scaling_factor, c->norm_expert_weight, ids, w, s));
     return MOE_OK;
 }
 
-int tile_m(const Dims& d) { return d.fp8 ? moe::fp8_tile_m() : moe::grouped_tile_m(); }
+int tile_m(const Dims& d) { return d.fp8 ? moe::fp8_tile_m() : moe::grouped_tile_m(d.P, d.E); }
 
-// upper bound on the tiles of a grouped launch: every group may end in a partial tile
-int max_tiles(const Dims& d) { return (int)((d.P + tile_m(d) - 1) / tile_m(d)) + d.E; }
+// upper bound on the tiles of a grouped launch: every group may end in a
+// partial tile (the extra group holds T rows)
+int max_tiles(const Dims& d, bool extra = false) {
+    const int bm = tile_m(d);
+    return (int)((d.P + bm - 1) / bm) + d.E + (extra ? (int)((d.T + bm - 1) / bm) + 1 : 0);
+}
+
+// the bf16 grouped launches of the routed experts (optionally with the
+// shared expert as an extra group of T rows after the P routed rows)
+moe::GroupedArgs up_args(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
+                         const int32_t* r2p, const void* w13, void* h, const int32_t* tile_start,
+                         const void* ws13 = nullptr) {
+    moe::GroupedArgs a;
+    a.A = x;
+    a.a_rows = r2p;
+    a.a_div = d.k;
+    a.a_nrows = (int)d.T;
+    a.W = w13;
+    a.w_group_stride = (int64_t)2 * d.I * d.H;
+    a.C = h;
+    a.M = (int)d.P;
+    a.N = d.I;
+    a.K = d.H;
+    a.limit = c->swiglu_limit;
+    a.offsets = offsets;
+    a.tile_start = tile_start;
+    a.groups = d.E;
+    a.bm = tile_m(d);
+    a.max_tiles = max_tiles(d, ws13 != nullptr);
+    if (ws13) {
+        a.extra_rows = (int)d.T;
+        a.W_extra = ws13;
+        a.limit_extra = c->swiglu_limit_shared;
+    }
+    return a;
+}
+
+moe::GroupedArgs down_args(const Dims& d, const void* h, const int32_t* offsets, const void* w2, void* y_rows,
+                           const int32_t* tile_start, const void* ws2 = nullptr) {
+    moe::GroupedArgs a;
+    a.A = h;
+    a.a_nrows = (int)(d.P + (ws2 ? d.T : 0));
+    a.W = w2;
+    a.w_group_stride = (int64_t)d.H * d.I;
+    a.C = y_rows;
+    a.M = (int)d.P;
+    a.N = d.H;
+    a.K = d.I;
+    a.offsets = offsets;
+    a.tile_start = tile_start;
+    a.groups = d.E;
+    a.bm = tile_m(d);
+    a.max_tiles = max_tiles(d, ws2 != nullptr);
+    if (ws2) {
+        a.extra_rows = (int)d.T;
+        a.W_extra = ws2;
+    }
+    return a;
+}
 
 // routed experts' first projection + clipped SwiGLU -> h
 moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
                    const int32_t* r2p, const void* w13, const float* w13s, void* h, char* ws, hipStream_t s) {
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), tile_start, s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), 0, tile_start, s));
     if (d.fp8) {
         char* xq = ws + plan_ws(d);
         float* xs = (float*)(xq + xq_bytes(d));
@@ -132,8 +197,7 @@ moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const in
                                    c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
         return MOE_OK;
     }
-    HIP_TRY(moe::launch_grouped_up(x, r2p, d.k, (int)d.T, w13, (int64_t)2 * d.I * d.H, h, (int)d.P, d.I, d.H,
-                                   c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
+    HIP_TRY(moe::launch_grouped_up(up_args(c, d, x, offsets, r2p, w13, h, tile_start), s));
     return MOE_OK;
 }
 
@@ -142,15 +206,14 @@ moe_status_t do_down(const moe_config_t* c, const Dims& d, const void* h, const 
                      const void* w2, const float* w2s, void* y_rows, char* ws, hipStream_t s) {
     (void)c;
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), tile_start, s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), 0, tile_start, s));
     if (d.fp8) {
         const float* hs = (const float*)((const char*)h + hcode_bytes(d));
         HIP_TRY(moe::launch_fp8_down(h, hs, (int)d.P, (int)d.P, w2, w2s, y_rows, d.H, d.I, offsets, tile_start,
                                      d.E, max_tiles(d), s));
         return MOE_OK;
     }
-    HIP_TRY(moe::launch_grouped_down(h, w2, (int64_t)d.H * d.I, y_rows, false, (int)d.P, d.H, d.I, offsets,
-                                     tile_start, d.E, max_tiles(d), s));
+    HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start), false, s));
     return MOE_OK;
 }
 
@@ -163,12 +226,31 @@ moe_status_t do_grouped(const moe_config_t* c, const Dims& d, const void* x, con
     return MOE_OK;
 }
 
+// shared expert on its own: dense launches, fp32 output
 moe_status_t do_shared(const moe_config_t* c, const Dims& d, const void* x, const void* ws13,
                        const void* ws2, float* y_sh, char* ws, hipStream_t s) {
     uint16_t* hs = (uint16_t*)ws;
-    HIP_TRY(moe::launch_grouped_up(x, nullptr, 1, (int)d.T, ws13, 0, hs, (int)d.T, d.Is, d.H,
-                                   c->swiglu_limit_shared, nullptr, nullptr, 1, 0, s));
-    HIP_TRY(moe::launch_grouped_down(hs, ws2, 0, y_sh, true, (int)d.T, d.H, d.Is, nullptr, nullptr, 1, 0, s));
+    moe::GroupedArgs a;
+    a.A = x;
+    a.a_nrows = (int)d.T;
+    a.W = ws13;
+    a.C = hs;
+    a.M = (int)d.T;
+    a.N = d.Is;
+    a.K = d.H;
+    a.limit = c->swiglu_limit_shared;
+    a.bm = d.T <= 64 ? 64 : 256;
+    HIP_TRY(moe::launch_grouped_up(a, s));
+    moe::GroupedArgs b;
+    b.A = hs;
+    b.a_nrows = (int)d.T;
+    b.W = ws2;
+    b.C = y_sh;
+    b.M = (int)d.T;
+    b.N = d.H;
+    b.K = d.Is;
+    b.bm = a.bm;
+    HIP_TRY(moe::launch_grouped_down(b, true, s));
     return MOE_OK;
 }
 
@@ -267,7 +349,8 @@ moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows,
     MOE_TRY(check_config(cfg, T));
     if (T == 0) return MOE_OK;
     if (!y_rows || !pair_to_row || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
-    return hip_status(moe::launch_combine(y_rows, pair_to_row, topk_w, y_shared, out, cfg->out_dtype == MOE_BF16,
+    return hip_status(moe::launch_combine(y_rows, pair_to_row, topk_w, y_shared, nullptr, out,
+                                          cfg->out_dtype == MOE_BF16,
                                           (int)T, cfg->hidden_size, cfg->top_k, stream));
 }
 
@@ -291,15 +374,30 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
     int32_t* offsets = (int32_t*)(base + L.offsets);
     int32_t* r2p = (int32_t*)(base + L.r2p);
     int32_t* p2r = (int32_t*)(base + L.p2r);
-    void* y_rows = base + L.y_rows;
-    float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
+    char* y_rows = base + L.y_rows;
     char* step = base + L.step;
+    const bool out_bf16 = cfg->out_dtype == MOE_BF16;
 
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, step, stream));
+    if (fuse_shared(d)) {
+        // one tile plan for both projections; the shared expert is group E.
+        // The plan sits in the layer's own area: the permutation's scratch
+        // (at `step`) is still in use while the plan is made.
+        int32_t* tile_start = (int32_t*)(base + L.plan);
+        void* h = step;
+        HIP_TRY(moe::launch_permute_plan(ids, (int)T, d.k, d.E, counts, offsets, r2p, p2r, step, tile_m(d),
+                                         (int)d.T, tile_start, stream));
+        HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, ws13), stream));
+        HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, stream));
+        HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * d.H * 2, out, out_bf16, (int)T,
+                                    d.H, d.k, stream));
+        return MOE_OK;
+    }
     HIP_TRY(moe::launch_permute(ids, (int)T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
+    float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
     MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w13_scale, w2, w2_scale, y_rows, step, stream));
     if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
-    HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, out, cfg->out_dtype == MOE_BF16, (int)T, d.H, d.k, stream));
+    HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, nullptr, out, out_bf16, (int)T, d.H, d.k, stream));
     return MOE_OK;
 }
 

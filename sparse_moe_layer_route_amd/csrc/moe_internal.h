@@ -9,35 +9,59 @@
 namespace moe {
 
 // ---- router ---------------------------------------------------------------
-// logits[T,E] fp32 = x[T,H] . w_router[E,H]^T  (bf16 inputs, fp32 accumulate)
+// logits = x[T,H] . w_router[E,H]^T (bf16 inputs, fp32 accumulate) as
+// router_splits(T, H) partial sums over K: logits [nsplit][T][E] fp32
+int router_splits(int64_t T, int H);
 hipError_t launch_router_logits(const void* x, const void* w_router, float* logits,
                                 int T, int E, int H, hipStream_t s);
-// per-token sigmoid + bias + top-k + weights
-hipError_t launch_topk(const float* logits, const float* bias, int T, int E, int k, float scale,
+// per-token sigmoid + bias + top-k + weights (partial logits summed in order)
+hipError_t launch_topk(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
                        int norm, int32_t* ids, float* w, hipStream_t s);
 
 // ---- permutation ----------------------------------------------------------
 size_t permute_scratch_bytes(int64_t P, int E);   // P = T * k pairs
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                           int32_t* row_to_pair, int32_t* pair_to_row, void* scratch, hipStream_t s);
+// the permutation and, when tile_start != nullptr, the bm-row tile plan
+// (with an extra group of extra_rows rows) in as few launches as the size allows
+hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                               int32_t* row_to_pair, int32_t* pair_to_row, void* scratch, int bm, int extra_rows,
+                               int32_t* tile_start, hipStream_t s);
 
 // ---- grouped / dense GEMMs ------------------------------------------------
-// Tile plan for a grouped GEMM with BM-row tiles: tile_start[E+1].
-hipError_t launch_tile_plan(const int32_t* offsets, int E, int bm, int32_t* tile_start, hipStream_t s);
+// Tile plan for a grouped GEMM with bm-row tiles: tile_start[E+1] (E+2 with
+// an extra group of extra_rows rows after the E groups).
+hipError_t launch_tile_plan(const int32_t* offsets, int E, int bm, int extra_rows, int32_t* tile_start,
+                            hipStream_t s);
 
-// Weight-streaming grouped GEMMs (256-row tiles, direct-to-LDS DMA ring).
+// Weight-streaming bf16 GEMMs (direct-to-LDS DMA ring).
 // Up: h[rows, N] bf16 = act(A[rows] . W13^T) with A rows gathered through
 // a_rows / a_div (clamped to a_nrows) or dense; W13 [2N, K] per group.
 // Down: C[rows, N] = A[rows, K] . W^T, C fp16 (saturating) or fp32.
-// K % 64 == 0; N % 64 == 0 (up) / any N (down).
-int grouped_tile_m();
-hipError_t launch_grouped_up(const void* A, const int32_t* a_rows, int a_div, int a_nrows, const void* W13,
-                             int64_t w_group_stride, void* h, int M, int N, int K, float limit,
-                             const int32_t* offsets, const int32_t* tile_start, int groups, int max_tiles,
-                             hipStream_t s);
-hipError_t launch_grouped_down(const void* A, const void* W, int64_t w_group_stride, void* C, bool c_fp32,
-                               int M, int N, int K, const int32_t* offsets, const int32_t* tile_start,
-                               int groups, int max_tiles, hipStream_t s);
+// Grouped when offsets != nullptr (groups, tile_start from the plan with the
+// same bm, max_tiles bounds the plan); otherwise dense with M rows.  An extra
+// group (extra_rows > 0, grouped only) follows the groups: rows
+// offsets[groups] .. + extra_rows, A row = row - offsets[groups], weights
+// W_extra, limit limit_extra.  K % 64 == 0; N % 64 == 0 (up).
+struct GroupedArgs {
+    const void* A = nullptr;
+    const int32_t* a_rows = nullptr;
+    int a_div = 1, a_nrows = 0;
+    const void* W = nullptr;
+    int64_t w_group_stride = 0;
+    void* C = nullptr;
+    int M = 0, N = 0, K = 0;
+    float limit = 0.f;
+    const int32_t* offsets = nullptr;
+    const int32_t* tile_start = nullptr;
+    int groups = 1, max_tiles = 0, bm = 256;
+    int extra_rows = 0;
+    const void* W_extra = nullptr;
+    float limit_extra = 0.f;
+};
+int grouped_tile_m(int64_t rows, int groups);
+hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s);
 
 // FP8 E4M3 routed experts (128 x 128 block-scaled weights, activations
 // quantised per (row, 128 columns), 128-row tiles).
@@ -57,8 +81,9 @@ hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows,
                            int max_tiles, hipStream_t s);
 
 // ---- combine --------------------------------------------------------------
+// shared expert output: y_shared fp32 [T, H], or shared_rows fp16 [T, H], or neither
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
-                          const float* y_shared, void* out, bool out_bf16, int T, int H, int k,
-                          hipStream_t s);
+                          const float* y_shared, const void* shared_rows, void* out, bool out_bf16, int T, int H,
+                          int k, hipStream_t s);
 
 }  // namespace moe

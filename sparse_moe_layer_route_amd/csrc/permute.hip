@@ -13,6 +13,9 @@
 //   4. one thread per pair: row = offsets[e] + word_prefix[e][p/32]
 //      + popcount(bitmap[e][p/32] & bits below p).
 // Scratch: 2 * E * ceil(P/32) words.
+// Small batches (all bitmaps fit in 64 KiB: decode) take one launch instead:
+// one block builds the bitmaps in LDS and does steps 2-4 there (same stable
+// order), and also writes the grouped GEMMs' tile plan when asked.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -112,9 +115,95 @@ __global__ void scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int E
     pair_to_row[p] = row;
 }
 
+// One-block path: bitmaps of all experts in LDS (E * ceil(P/32) words).
+constexpr int SMALL_WORDS = 16384;                // 64 KiB of LDS
+
+static bool small_path(int64_t P, int E) { return P > 0 && (int64_t)E * words_for(P) <= SMALL_WORDS; }
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ row_to_pair,
+                                                             int32_t* __restrict__ pair_to_row, int bm,
+                                                             int extra_rows, int32_t* __restrict__ tile_start) {
+    __shared__ uint32_t bits[SMALL_WORDS];
+    __shared__ int32_t part[1024];
+    const int t = threadIdx.x;
+    const int W = (P + 31) >> 5;
+    for (int i = t; i < E * W; i += 1024) bits[i] = 0u;
+    __syncthreads();
+    for (int p = t; p < P; p += 1024) {
+        const int e = min(max(ids[p], 0), E - 1);
+        atomicOr(&bits[e * W + (p >> 5)], 1u << (p & 31));   // bits commute: order-free
+    }
+    __syncthreads();
+    int cnt = 0;
+    if (t < E)
+        for (int w = 0; w < W; ++w) cnt += __popc(bits[t * W + w]);
+    // inclusive scan of the counts
+    part[t] = cnt;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int v = t >= o ? part[t - o] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    if (t < E) {
+        const int off = part[t] - cnt;
+        counts[t] = cnt;
+        offsets[t] = off;
+        if (t == E - 1) offsets[E] = off + cnt;
+    }
+    __syncthreads();
+    // rank of pair p inside its expert = set bits of the expert's bitmap below p
+    for (int p = t; p < P; p += 1024) {
+        const int e = min(max(ids[p], 0), E - 1);
+        const int wp = p >> 5;
+        int below = __popc(bits[e * W + wp] & ((1u << (p & 31)) - 1u));
+        for (int w = 0; w < wp; ++w) below += __popc(bits[e * W + w]);
+        const int row = (e > 0 ? part[e - 1] : 0) + below;    // exclusive offset of e + rank
+        row_to_pair[row] = p;
+        pair_to_row[p] = row;
+    }
+    if (!tile_start) return;                      // uniform over the block
+    const int tiles = t < E ? (cnt + bm - 1) / bm : 0;
+    __syncthreads();
+    part[t] = tiles;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int v = t >= o ? part[t - o] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    if (t < E) tile_start[t + 1] = part[t];
+    if (t == 0) tile_start[0] = 0;
+    if (t == E - 1 && extra_rows > 0) tile_start[E + 1] = part[t] + (extra_rows + bm - 1) / bm;
+}
+
+hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                               int32_t* row_to_pair, int32_t* pair_to_row, void* scratch, int bm, int extra_rows,
+                               int32_t* tile_start, hipStream_t s) {
+    const int64_t P = (int64_t)T * k;
+    if (small_path(P, E)) {
+        permute_small_kernel<<<1, 1024, 0, s>>>(ids, (int)P, E, counts, offsets, row_to_pair, pair_to_row, bm,
+                                                extra_rows, tile_start);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_permute(ids, T, k, E, counts, offsets, row_to_pair, pair_to_row, scratch, s);
+    if (e != hipSuccess || !tile_start) return e;
+    return launch_tile_plan(offsets, E, bm, extra_rows, tile_start, s);
+}
+
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                           int32_t* row_to_pair, int32_t* pair_to_row, void* scratch, hipStream_t s) {
     const int64_t P = (int64_t)T * k;
+    if (small_path(P, E)) {
+        permute_small_kernel<<<1, 1024, 0, s>>>(ids, (int)P, E, counts, offsets, row_to_pair, pair_to_row, 1, 0,
+                                                nullptr);
+        return hipGetLastError();
+    }
     const int64_t W = words_for(P);
     uint32_t* bm = (uint32_t*)scratch;
     int32_t* wp = (int32_t*)(bm + (int64_t)E * W);

@@ -1,7 +1,8 @@
 // route.hip -- the router's selection step on gfx950: one wavefront per token.
 //
 // From the fp32 router logits (page "MAX 中 Step-3.5-Flash 架构解析…", section
-// "MoE：共享专家、sigmoid 路由与激活裁剪", Step3p5MoEGate paragraph):
+// "MoE：共享专家、sigmoid 路由与激活裁剪", Step3p5MoEGate paragraph), given
+// as nsplit partial sums over K that are added in split order:
 //   s = sigmoid(logit), c = s + bias            (fp32)
 //   ids = the k largest c, descending, ties to the lower index, NaN last
 //   w_j = s[ids_j]; if norm: w_j /= sum_j w_j; w_j *= scale
@@ -27,7 +28,9 @@ __device__ __forceinline__ uint32_t order_key(float c) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);      // >= 0x007fffff for numbers
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+// BATCH: splits loaded at once (1 when the logits come whole)
+template <int BATCH>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit,
                                                    const float* __restrict__ bias, int T, int E, int k,
                                                    float scale, int norm, int32_t* __restrict__ ids,
                                                    float* __restrict__ wout) {
@@ -38,13 +41,33 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
     uint32_t key[TOPK_MAX_PER_LANE];
     float sc[TOPK_MAX_PER_LANE];
+    float a[TOPK_MAX_PER_LANE];
+    // partial logits, added in split order.  They were just written by other
+    // XCDs, so every read misses this XCD's L2: BATCH splits are loaded at
+    // once, then added, so the latency is paid once per BATCH splits.
+#pragma unroll
+    for (int i = 0; i < TOPK_MAX_PER_LANE; ++i) a[i] = 0.f;
+    for (int z0 = 0; z0 < nsplit; z0 += BATCH) {
+        float part[BATCH][TOPK_MAX_PER_LANE];
+#pragma unroll
+        for (int z = 0; z < BATCH; ++z)
+#pragma unroll
+            for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
+                part[z][i] = (z0 + z < nsplit && lane + 64 * i < E)
+                                 ? lg[(int64_t)(z0 + z) * T * E + lane + 64 * i] : 0.f;
+#pragma unroll
+        for (int z = 0; z < BATCH; ++z)
+#pragma unroll
+            for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
+                if (z0 + z < nsplit) a[i] += part[z][i];
+    }
 #pragma unroll
     for (int i = 0; i < TOPK_MAX_PER_LANE; ++i) {
         const int e = lane + 64 * i;
         key[i] = 0u;
         sc[i] = 0.f;
         if (e < E) {
-            const float s = 1.0f / (1.0f + expf(-lg[e]));
+            const float s = 1.0f / (1.0f + expf(-a[i]));
             sc[i] = s;
             key[i] = order_key(s + bias[e]);
         }
@@ -77,10 +100,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (lane < k) wout[(int64_t)t * k + lane] = w * scale;
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int T, int E, int k, float scale, int norm,
-                       int32_t* ids, float* w, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
+                       int norm, int32_t* ids, float* w, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, bias, T, E, k, scale, norm, ids, w);
+    if (nsplit > 1)
+        topk_kernel<8><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, bias, T, E, k, scale, norm, ids, w);
+    else
+        topk_kernel<1><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, bias, T, E, k, scale, norm, ids, w);
     return hipGetLastError();
 }
 

@@ -2,13 +2,17 @@
 // in fp32 from bf16 operands (the gate is computed in FP32: page "MAX 中
 // Step-3.5-Flash 架构解析…", section "MoE：共享专家、sigmoid 路由与激活裁剪").
 //
-// A small GEMM (2*T*E*H flops, about 1% of the layer), so it uses no LDS: each
-// wave owns a (16*TM tokens) x (16*TN experts) tile and feeds
+// A small GEMM (2*T*E*H flops, about 1% of the layer).  From 512 tokens it
+// runs on the dense instance of the grouped expert GEMM (64-token tiles,
+// direct-to-LDS DMA, fp32 out).  Below that, few tokens leave too little
+// work per wave for that kernel, and router_logits_kernel below is used: no
+// LDS, each wave owns a 16-token x 16-expert tile and feeds
 // v_mfma_f32_16x16x32_bf16 straight from global memory (x rows and router
 // rows stay in L2), with the next K slice's loads issued before the current
-// slice's MFMAs.  Few registers per wave, so many waves per SIMD hide the
-// load latency.  K order inside a 32-wide slice: lane group g = lane >> 4
-// takes 8-element chunk g, for both operands.
+// slice's MFMAs; K is split over `nsplit` blocks (blockIdx.z) that write
+// partial logits [nsplit][T][E], summed in split order by the top-k kernel,
+// so the dependent chain per wave is short.  K order inside a 32-wide slice:
+// lane group g = lane >> 4 takes 8-element chunk g, for both operands.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -19,6 +23,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ wg,
                                                             float* __restrict__ logits, int T, int E, int H) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // this block's K range: [kz * H/nsplit, (kz + 1) * H/nsplit)
+    const int hk = H / gridDim.z, kz = blockIdx.z;
+    x += (int64_t)kz * hk;
+    wg += (int64_t)kz * hk;
+    logits += (int64_t)kz * T * E;
     const int t0 = blockIdx.x * 16 * TM;
     const int e0 = (blockIdx.y * 4 + wave) * 16 * TN;
     if (e0 >= E) return;                          // no barriers: a wave may leave alone
@@ -41,8 +50,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8*)(ap[i]);
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8*)(bp[j]);
-    for (int k0 = 32; k0 <= H; k0 += 32) {
-        const int kn = min(k0, H - 32);           // the last step re-reads its own slice
+    for (int k0 = 32; k0 <= hk; k0 += 32) {
+        const int kn = min(k0, hk - 32);          // the last step re-reads its own slice
 #pragma unroll
         for (int i = 0; i < TM; ++i) an[i] = *(const bf16x8*)(ap[i] + kn);
 #pragma unroll
@@ -71,18 +80,32 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         }
 }
 
+int router_splits(int64_t T, int H) {
+    if (T >= 512) return 1;
+    int n = 8;
+    while (n > 1 && H % (32 * n)) n >>= 1;
+    return n;
+}
+
 hipError_t launch_router_logits(const void* x, const void* w_router, float* logits, int T, int E, int H,
                                 hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    const uint16_t* xp = (const uint16_t*)x;
-    const uint16_t* wp = (const uint16_t*)w_router;
-    if (T >= 1024) {
-        dim3 grid((T + 31) / 32, (E + 255) / 256);        // wave: 32 tokens x 64 experts
-        router_logits_kernel<2, 4><<<grid, 256, 0, s>>>(xp, wp, logits, T, E, H);
-    } else {
-        dim3 grid((T + 15) / 16, (E + 63) / 64);          // wave: 16 tokens x 16 experts
-        router_logits_kernel<1, 1><<<grid, 256, 0, s>>>(xp, wp, logits, T, E, H);
+    const int nsplit = router_splits(T, H);
+    if (nsplit == 1 && T >= 512) {
+        GroupedArgs a;
+        a.A = x;
+        a.a_nrows = T;
+        a.W = w_router;
+        a.C = logits;
+        a.M = T;
+        a.N = E;
+        a.K = H;
+        a.bm = 64;
+        return launch_grouped_down(a, true, s);
     }
+    dim3 grid((T + 15) / 16, (E + 63) / 64, nsplit);   // wave: 16 tokens x 16 experts x H/nsplit
+    router_logits_kernel<1, 1><<<grid, 256, 0, s>>>((const uint16_t*)x, (const uint16_t*)w_router, logits, T, E,
+                                                    H);
     return hipGetLastError();
 }
 

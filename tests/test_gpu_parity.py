@@ -74,6 +74,10 @@ SMALL = {
                        num_experts=12, top_k=2),
     "max_experts_max_k": dict(hidden_size=128, num_experts=1024, top_k=32, moe_intermediate_size=64,
                               share_expert_dim=64, T=64),
+    # ~37 rows per expert: 64-row tiles, several for the larger experts
+    "small_tiles_multi_tile": dict(T=600, num_experts=32, top_k=2),
+    # shared width differs from the experts': the shared expert runs on its own
+    "shared_width_differs": dict(moe_intermediate_size=192, share_expert_dim=128, T=100),
 }
 
 
