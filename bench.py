@@ -60,15 +60,23 @@ def layer_bytes(wl, touched):
     return b
 
 
+def shared_fused(cfg):
+    return cfg.expert_dtype == "bf16" and 0 < cfg.share_expert_dim == cfg.moe_intermediate_size
+
+
 def up_kernel_bytes(wl, touched):
-    """Algorithmic bytes of the routed experts' first projection: W13 of every
-    touched expert once, x once, h written once."""
+    """Algorithmic bytes of the first-projection launch: W13 of every touched
+    expert once, x once, h written once -- plus, when the shared expert runs
+    in the same launch, its W13 once and its h rows written once."""
     c = wl.cfg
-    T, H, k, I = wl.T, c.hidden_size, c.top_k, c.moe_intermediate_size
+    T, H, k, I, Is = wl.T, c.hidden_size, c.top_k, c.moe_intermediate_size, c.share_expert_dim
     if c.expert_dtype == "fp8":
         # codes + block scales of W13; x read once (bf16); h codes + scales written
         return touched * (2 * I * H + (2 * I // 128) * (H // 128) * 4) + T * H * 2 + T * k * (I + I // 128 * 4)
-    return touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+    b = touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+    if shared_fused(c):
+        b += 2 * Is * H * 2 + T * Is * 2
+    return b
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -148,7 +156,8 @@ def main():
         "hbm_frac": by / (ms_step * 1e-3) / HBM_PEAK,
         "layer_roofline_frac": max(fl / BF16_PEAK, by / HBM_PEAK) / (ms_step * 1e-3),
         "layer_forward_ms": layer_fwd_ms,
-        "roofline": {"kernel": "routed experts: first projection + clipped SwiGLU (moe_expert_up)",
+        "roofline": {"kernel": "first projection + clipped SwiGLU of the routed experts and the shared expert "
+                               "(moe_expert_up, gg::kernel<0, true, 256, 256>)",
                      "bound": "hbm", "achieved": up_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": up_achieved / HBM_PEAK, "traffic": counter_traffic(wl), "avg_ms": up_ms,
                      "algorithmic_bytes": up_bytes},
@@ -190,21 +199,28 @@ def time_layer(args, wl, moe, torch, mi):
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     h = torch.empty(moe.moe_hidden_bytes(cfg, T), dtype=torch.uint8, device=dev)
-    y_rows = torch.empty((T * k, H), dtype=torch.float16, device=dev)
-    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev)
+    # the shared expert runs inside the expert launches when it can (as
+    # moe_layer_forward does), else on its own
+    fused = moe.binding.shared_fusable(cfg)
+    y_rows = torch.empty((T * k + (T if fused else 0), H), dtype=torch.float16, device=dev)
+    y_sh = None if fused else torch.empty((T, H), dtype=torch.float32, device=dev)
     s13, s2 = inp.get("w13_scale"), inp.get("w2_scale")
+    ws13, ws2 = (inp["ws13"], inp["ws2"]) if fused else (None, None)
 
     def step(ev=None):
         moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ids, w, ws=ws, stream=stream)
         counts, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], s13, h=h, ws=ws, stream=stream)
+        moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], s13, h=h, ws=ws, stream=stream, ws13=ws13)
         if ev is not None:
             ev[1].record(stream)
-        moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], s2, y_rows=y_rows, ws=ws, stream=stream)
-        moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], y_shared=y_sh, ws=ws, stream=stream)
-        moe.moe_combine(cfg, y_rows, p2r, w, y_sh, out=out, stream=stream)
+        moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], s2, y_rows=y_rows, ws=ws, stream=stream, ws2=ws2)
+        if fused:
+            moe.moe_combine(cfg, y_rows, p2r, w, shared_rows=y_rows[T * k:], out=out, stream=stream)
+        else:
+            moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], y_shared=y_sh, ws=ws, stream=stream)
+            moe.moe_combine(cfg, y_rows, p2r, w, y_sh, out=out, stream=stream)
         return counts
 
     note(f"{wl.name}: warmup {args.warmup} + timed {args.steps} steps")

@@ -130,15 +130,25 @@ moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* 
  *   h is [T*k, I] bf16 for bf16 experts; for FP8 experts it is [T*k, I]
  *   E4M3FN codes, then, at the next multiple of 256 bytes, fp32 scales laid
  *   out block-major as [I/128][T*k] (moe_hidden_bytes() covers both).
- * moe_expert_down: y_rows[r] = W2[e] h[r] (h dequantised in FP8 mode). */
+ * moe_expert_down: y_rows[r] = W2[e] h[r] (h dequantised in FP8 mode).
+ * Shared expert in the same launches (optional): with bf16 experts and
+ * share_expert_dim == moe_intermediate_size, ws13 / ws2 (bf16 [2Is,H] /
+ * [H,Is], MAX page, MoE section) may be passed; the shared expert then runs
+ * as T more rows after the T*k routed ones -- h[T*k + t] = act(Ws13 x[t],
+ * swiglu_limit_shared) and y_rows[T*k + t] = Ws2 h[T*k + t], so h holds
+ * (T*k + T) rows (moe_hidden_bytes() covers them whenever the shared expert
+ * can run this way) and y_rows [T*k + T, H].  Pass ws13 and ws2 together or
+ * not at all; otherwise both are NULL.  Any other configuration with a
+ * non-NULL ws13/ws2 is MOE_ERR_INVALID_ARGUMENT. */
 moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t T, const void* x,
                            const int32_t* expert_offsets, const int32_t* row_to_pair,
-                           const void* w13, const float* w13_scale, void* h,
+                           const void* w13, const float* w13_scale, const void* ws13, void* h,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t T, const void* h,
                              const int32_t* expert_offsets, const void* w2, const float* w2_scale,
-                             void* y_rows, void* ws, size_t ws_bytes, hipStream_t stream);
-/* Bytes of the h buffer moe_expert_up writes for T tokens. */
+                             const void* ws2, void* y_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Bytes of the h buffer moe_expert_up writes for T tokens (with room for
+ * the shared expert's rows when it can run in the same launches). */
 moe_status_t moe_hidden_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes);
 
 /* Shared expert (MAX page, MoE section: always-on MLP of width
@@ -151,13 +161,16 @@ moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Weighted combine (MAX page, MoE section: routed output plus the shared
- * expert's): out[t] = sum_j topk_w[t,j] * y_rows[pair_to_row[t*k+j]] + y_shared[t]
+ * expert's): out[t] = sum_j topk_w[t,j] * y_rows[pair_to_row[t*k+j]] + s[t]
  * accumulated in fp32 in slot order; y_rows [T*k,H] fp16 as written by the
- * routed experts; y_shared may be NULL (no shared term).  out [T,H] in
+ * routed experts.  The shared term s is y_shared (fp32 [T,H], from
+ * moe_shared_ffn) or shared_rows (fp16 [T,H], the shared expert's rows
+ * written by moe_expert_down, i.e. y_rows + T*k*H), or absent when both
+ * are NULL; passing both is MOE_ERR_INVALID_ARGUMENT.  out [T,H] in
  * out_dtype (fp32 or bf16). */
 moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows,
                          const int32_t* pair_to_row, const float* topk_w,
-                         const float* y_shared, void* out, hipStream_t stream);
+                         const float* y_shared, const void* shared_rows, void* out, hipStream_t stream);
 
 /* The whole layer: route, permute, routed experts, shared expert, combine.
  * Inputs as above (ws13/ws2 may be NULL when share_expert_dim == 0).

@@ -61,11 +61,11 @@ def load(path: Optional[str] = None):
         "moe_route": [C, I64, P, P, P, P, P, P, SZ, P],
         "moe_permute": [C, I64, P, P, P, P, P, P, SZ, P],
         "moe_grouped_swiglu": [C, I64, P, P, P, P, P, P, P, P, P, SZ, P],
-        "moe_expert_up": [C, I64, P, P, P, P, P, P, P, SZ, P],
-        "moe_expert_down": [C, I64, P, P, P, P, P, P, SZ, P],
+        "moe_expert_up": [C, I64, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_expert_down": [C, I64, P, P, P, P, P, P, P, SZ, P],
         "moe_hidden_bytes": [C, I64, ctypes.POINTER(SZ)],
         "moe_shared_ffn": [C, I64, P, P, P, P, P, SZ, P],
-        "moe_combine": [C, I64, P, P, P, P, P, P],
+        "moe_combine": [C, I64, P, P, P, P, P, P, P],
         "moe_layer_forward": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
@@ -198,9 +198,18 @@ def moe_hidden_bytes(cfg, T: int) -> int:
     return n.value
 
 
-def moe_expert_up(cfg, x, expert_offsets, row_to_pair, w13, w13_scale=None, h=None, ws=None, stream=None):
-    """First projection + clipped SwiGLU of the routed experts; h is a byte
-    buffer of moe_hidden_bytes() (bf16 [T*k, I] for bf16 experts)."""
+def shared_fusable(cfg) -> bool:
+    """True when the shared expert can run inside the routed experts'
+    launches (bf16 experts, shared width equal to the experts')."""
+    return (cfg.expert_dtype == "bf16" and cfg.share_expert_dim > 0
+            and cfg.share_expert_dim == cfg.moe_intermediate_size)
+
+
+def moe_expert_up(cfg, x, expert_offsets, row_to_pair, w13, w13_scale=None, h=None, ws=None, stream=None,
+                  ws13=None):
+    """First projection + clipped SwiGLU of the routed experts (and, with
+    ws13, of the shared expert as T more rows); h is a byte buffer of
+    moe_hidden_bytes() (bf16 [T*k (+T), I] for bf16 experts)."""
     T, H, E, k, I = x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size
     fp8 = cfg.expert_dtype == "fp8"
     nb = moe_hidden_bytes(cfg, T)
@@ -209,31 +218,38 @@ def moe_expert_up(cfg, x, expert_offsets, row_to_pair, w13, w13_scale=None, h=No
         raise ValueError(f"h must hold {nb} bytes")
     ws = ws if ws is not None else workspace(cfg, T, x.device)
     c = make_config(cfg)
+    Is = cfg.share_expert_dim
     st = load().moe_expert_up(
         ctypes.byref(c), T, _ptr(x, torch.bfloat16, (T, H), "x"),
         _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
         _ptr(row_to_pair, torch.int32, (T * k,), "row_to_pair"),
         _ptr(w13, _weights_dtype(cfg), (E, 2 * I, H), "w13"),
         _ptr(w13_scale, torch.float32, (E, 2 * I // 128, H // 128) if fp8 else None, "w13_scale"),
+        _ptr(ws13, torch.bfloat16, (2 * Is, H), "ws13"),
         _ptr(h, None, None, "h"), _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_expert_up")
     return h
 
 
-def moe_expert_down(cfg, T, h, expert_offsets, w2, w2_scale=None, y_rows=None, ws=None, stream=None):
+def moe_expert_down(cfg, T, h, expert_offsets, w2, w2_scale=None, y_rows=None, ws=None, stream=None, ws2=None):
+    """Second projection: y_rows [T*k, H] fp16 (with ws2: [T*k + T, H], the
+    shared expert's rows last)."""
     H, E, k, I = cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size
     fp8 = cfg.expert_dtype == "fp8"
     if h.numel() * h.element_size() < moe_hidden_bytes(cfg, T):
         raise ValueError("h is smaller than moe_hidden_bytes()")
-    y_rows = y_rows if y_rows is not None else torch.empty((T * k, H), dtype=torch.float16, device=h.device)
+    rows = T * k + (T if ws2 is not None else 0)
+    y_rows = y_rows if y_rows is not None else torch.empty((rows, H), dtype=torch.float16, device=h.device)
     ws = ws if ws is not None else workspace(cfg, T, h.device)
     c = make_config(cfg)
+    Is = cfg.share_expert_dim
     st = load().moe_expert_down(
         ctypes.byref(c), T, _ptr(h, None, None, "h"),
         _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
         _ptr(w2, _weights_dtype(cfg), (E, H, I), "w2"),
         _ptr(w2_scale, torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
-        _ptr(y_rows, torch.float16, (T * k, H), "y_rows"),
+        _ptr(ws2, torch.bfloat16, (H, Is), "ws2"),
+        _ptr(y_rows, torch.float16, (rows, H), "y_rows"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_expert_down")
     return y_rows
@@ -257,14 +273,19 @@ def _out_dtype(cfg):
     return torch.bfloat16 if getattr(cfg, "out_dtype", "fp32") == "bf16" else torch.float32
 
 
-def moe_combine(cfg, y_rows, pair_to_row, topk_w, y_shared=None, out=None, stream=None):
+def moe_combine(cfg, y_rows, pair_to_row, topk_w, y_shared=None, out=None, stream=None, shared_rows=None):
+    """y_rows: at least T*k rows of [H] fp16 (the routed rows come first);
+    the shared term is y_shared (fp32 [T, H]) or shared_rows (fp16 [T, H])."""
     T, H, k = topk_w.shape[0], cfg.hidden_size, cfg.top_k
+    if y_rows.dim() != 2 or y_rows.shape[0] < T * k or y_rows.shape[1] != H:
+        raise ValueError(f"y_rows must be [>= {T * k}, {H}] (got {tuple(y_rows.shape)})")
     out = out if out is not None else torch.empty((T, H), dtype=_out_dtype(cfg), device=y_rows.device)
     c = make_config(cfg)
-    st = load().moe_combine(ctypes.byref(c), T, _ptr(y_rows, torch.float16, (T * k, H), "y_rows"),
+    st = load().moe_combine(ctypes.byref(c), T, _ptr(y_rows, torch.float16, None, "y_rows"),
                             _ptr(pair_to_row, torch.int32, (T * k,), "pair_to_row"),
                             _ptr(topk_w, torch.float32, (T, k), "topk_w"),
                             _ptr(y_shared, torch.float32, (T, H), "y_shared"),
+                            _ptr(shared_rows, torch.float16, (T, H), "shared_rows"),
                             _ptr(out, _out_dtype(cfg), (T, H), "out"), _stream(stream))
     _check(st, "moe_combine")
     return out

@@ -113,15 +113,35 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// GROUPED: rows come in expert groups (offsets + tile plan); otherwise one
-// dense group of M rows.  Separate instances also keep the uses apart in
-// kernel traces.
+// Work items: grouped, (group, n-tile, m-tile) with m fastest, from the
+// tile plan; dense, (n-tile, m-tile).  The routed items and the extra
+// group's are two segments; each is cut into 8 contiguous ranges, one per XCD
+// (block b runs on XCD b % 8), so every XCD gets an equal share of both and
+// the blocks that share a tile run on one L2.  An XCD runs its extra-group
+// items (full tiles) first, then its routed ones.
+struct Segments {
+    int total1, per1, total2, per2;           // routed / extra items, per-XCD range lengths
+};
+template <bool GROUPED, int BM>
+__device__ __forceinline__ Segments segments(const Params& p) {
+    Segments g;
+    if (GROUPED) {
+        g.total1 = p.tile_start[p.groups] * p.n_tiles;
+        g.total2 = p.extra_rows > 0 ? (p.tile_start[p.groups + 1] - p.tile_start[p.groups]) * p.n_tiles : 0;
+    } else {
+        g.total1 = ((p.M + BM - 1) / BM) * p.n_tiles;
+        g.total2 = 0;
+    }
+    g.per1 = (g.total1 + NXCD - 1) / NXCD;
+    g.per2 = (g.total2 + NXCD - 1) / NXCD;
+    return g;
+}
+
+// one work item w of the list
 template <int MODE, bool GROUPED, int BM, int BN>
-__global__ __launch_bounds__(NT, 1) void kernel(Params p) {
+__device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* smem) {
     using S = Shape<BM, BN>;
-    static_assert(MODE != SWIGLU || S::TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
     constexpr int STAGES = S::STAGES, STAGE_BYTES = S::STAGE_BYTES, TN = S::TN;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -130,48 +150,40 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
 
     // ---- decode the work item ------------------------------------------
     int g = 0, m_tile, n_tile, row0, row_end;
-    {
-        const int b = blockIdx.x;
-        const int xcd = b % NXCD, slot = b / NXCD;
-        if (GROUPED) {
-            const int ng = p.groups + (p.extra_rows > 0 ? 1 : 0);
-            const int ntiles = p.tile_start[ng];
-            const int total = ntiles * p.n_tiles;
-            const int per = (total + NXCD - 1) / NXCD;
-            if (slot >= per) return;
-            const int w = xcd * per + slot;
-            if (w >= total) return;
-            // group owning work item w: largest g with tile_start[g]*n_tiles <= w
-            int lo = 0, hi = ng - 1;
-            while (lo < hi) {
-                int mid = (lo + hi + 1) >> 1;
-                if (p.tile_start[mid] * p.n_tiles <= w) lo = mid; else hi = mid - 1;
-            }
-            g = lo;
-            const int mt = p.tile_start[g + 1] - p.tile_start[g];
-            const int local = w - p.tile_start[g] * p.n_tiles;
-            n_tile = local / mt;
-            m_tile = local % mt;
-            row0 = p.offsets[g] + m_tile * BM;
-            row_end = g < p.groups ? p.offsets[g + 1] : p.offsets[g] + p.extra_rows;
-        } else {
-            const int mt = (p.M + BM - 1) / BM;
-            const int total = mt * p.n_tiles;
-            const int per = (total + NXCD - 1) / NXCD;
-            if (slot >= per) return;
-            const int w = xcd * per + slot;
-            if (w >= total) return;
-            n_tile = w / mt;
-            m_tile = w % mt;
-            row0 = m_tile * BM;
-            row_end = p.M;
+    if (GROUPED) {
+        // group owning work item w: largest g with tile_start[g]*n_tiles <= w
+        int lo = 0, hi = p.groups + (p.extra_rows > 0 ? 1 : 0) - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (p.tile_start[mid] * p.n_tiles <= w) lo = mid; else hi = mid - 1;
         }
+        g = lo;
+        const int mt = p.tile_start[g + 1] - p.tile_start[g];
+        const int local = w - p.tile_start[g] * p.n_tiles;
+        n_tile = local / mt;
+        m_tile = local % mt;
+        row0 = p.offsets[g] + m_tile * BM;
+        row_end = g < p.groups ? p.offsets[g + 1] : p.offsets[g] + p.extra_rows;
+    } else {
+        const int mt = (p.M + BM - 1) / BM;
+        n_tile = w / mt;
+        m_tile = w % mt;
+        row0 = m_tile * BM;
+        row_end = p.M;
     }
     const bool extra = GROUPED && g == p.groups;
     const int valid = min(row_end - row0, BM);
     const int K = p.K;
     const uint16_t* Wg = extra ? p.W_extra : p.W + (int64_t)g * p.w_group_stride;
     const float limit = extra ? p.limit_extra : p.limit;
+    // K-slice rotation: the K loop starts at slice `rot`.  Weight and x rows
+    // are 8 KiB apart in the Step-5 shapes, so one K slice of all rows of a
+    // tile sits on few HBM channels; blocks that start at different slices
+    // spread over the channels (measured: 5.0 -> 6.4 TB/s for this DMA
+    // pattern).  One rotation per expert (per n-tile when dense) keeps the
+    // blocks that share an A tile (grouped) or a weight panel (dense) in step.
+    const int nk = K / BK;                      // even: K % 64 == 0
+    const int rot = (GROUPED ? (g + 1) * 37 : (n_tile + 1) * 37) % nk;
 
     // ---- DMA sources.  One DMA instruction moves a block of 16 rows x 64 B
     // (one K slice of 32): lane l reads 16 B of row quad l >> 2 at chunk
@@ -224,7 +236,8 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     }
     const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
     auto issue = [&](int kt, int stage) {
-        const int k0 = kt * BK;
+        const int ks = kt + rot < nk ? kt + rot : kt + rot - nk;
+        const int k0 = ks * BK;
         const unsigned sb = lds_base + stage * STAGE_BYTES;
         if (a_mine) {
 #pragma unroll
@@ -253,7 +266,6 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;                      // even: K % 64 == 0
     // prologue: slices 0 .. STAGES-2 in flight (clamped re-reads past the end
     // keep the per-step DMA count fixed, which the waits below rely on)
 #pragma unroll
@@ -344,8 +356,36 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     }
 }
 
+// GROUPED: rows come in expert groups (offsets + tile plan); otherwise one
+// dense group of M rows.  Separate instances also keep the uses apart in
+// kernel traces.  Block (xcd, slot) runs the items at slots slot, slot +
+// slots, ... of its XCD's ranges (one item when the grid covers them).
+template <int MODE, bool GROUPED, int BM, int BN>
+__global__ __launch_bounds__(NT, 1) void kernel(Params p) {
+    using S = Shape<BM, BN>;
+    static_assert(MODE != SWIGLU || S::TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::STAGES * S::STAGE_BYTES];
+    const Segments sg = segments<GROUPED, BM>(p);
+    const int xcd = blockIdx.x % NXCD, slots = gridDim.x / NXCD;
+    for (int s = blockIdx.x / NXCD; s < sg.per1 + sg.per2; s += slots) {
+        int w;
+        if (s < sg.per2) {
+            w = xcd * sg.per2 + s;
+            if (w >= sg.total2) continue;
+            w += sg.total1;
+        } else {
+            w = xcd * sg.per1 + (s - sg.per2);
+            if (w >= sg.total1) continue;
+        }
+        run_item<MODE, GROUPED, BM, BN>(p, w, smem);
+        __syncthreads();                          // LDS is reused by the next item
+    }
+}
+
+// blocks for `work` items in two segments: one more slot per XCD than the
+// items need, since each segment rounds its per-XCD range up
 static int grid_blocks(int64_t work) {
-    const int64_t per = (work + NXCD - 1) / NXCD;
+    const int64_t per = (work + NXCD - 1) / NXCD + 1;
     return (int)(per * NXCD);
 }
 

@@ -65,15 +65,15 @@ size_t xq_ws(const Dims& d) { return d.fp8 ? xq_bytes(d) + align_up((size_t)(d.H
 size_t up_ws(const Dims& d) { return plan_ws(d) + xq_ws(d); }
 // h: bf16 [P, I]; FP8: codes [P, I] then scales [I/128][P]
 size_t hcode_bytes(const Dims& d) { return align_up((size_t)d.P * d.I); }
+// The shared expert can run as one more group of the routed experts'
+// launches when it has their width and dtype.
+bool fuse_shared(const Dims& d) { return !d.fp8 && d.Is > 0 && d.Is == d.I; }
 size_t hidden_bytes(const Dims& d) {
-    return d.fp8 ? hcode_bytes(d) + (size_t)(d.I / 128) * d.P * 4 : (size_t)d.P * d.I * 2;
+    if (d.fp8) return hcode_bytes(d) + (size_t)(d.I / 128) * d.P * 4;
+    return (size_t)(d.P + (fuse_shared(d) ? d.T : 0)) * d.I * 2;
 }
 size_t grouped_ws(const Dims& d) { return up_ws(d) + align_up(hidden_bytes(d)); }
 size_t shared_ws(const Dims& d) { return align_up((size_t)d.T * d.Is * 2); }
-
-// The whole layer runs the shared expert inside the routed experts' grouped
-// launches (as one more group of T rows) when it has their width and dtype.
-bool fuse_shared(const Dims& d) { return !d.fp8 && d.Is > 0 && d.Is == d.I; }
 
 // the whole layer: its own buffers followed by each step's scratch
 struct LayerWs {
@@ -95,7 +95,7 @@ LayerWs layer_ws(const Dims& d) {
     L.y_rows = o;  o += align_up((size_t)rows * d.H * 2);
     L.y_sh = o;    o += (d.Is > 0 && !fuse) ? align_up((size_t)d.T * d.H * 4) : 0;
     L.step = o;
-    const size_t grouped = fuse ? align_up((size_t)rows * d.I * 2) : grouped_ws(d);
+    const size_t grouped = fuse ? align_up(hidden_bytes(d)) : grouped_ws(d);
     o += std::max(std::max(route_ws(d), permute_ws(d)), std::max(grouped, shared_ws(d)));
     L.total = o;
     return L;
@@ -185,9 +185,10 @@ moe::GroupedArgs down_args(const Dims& d, const void* h, const int32_t* offsets,
 
 // routed experts' first projection + clipped SwiGLU -> h
 moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const int32_t* offsets,
-                   const int32_t* r2p, const void* w13, const float* w13s, void* h, char* ws, hipStream_t s) {
+                   const int32_t* r2p, const void* w13, const float* w13s, void* h, char* ws, hipStream_t s,
+                   const void* ws13 = nullptr) {
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), 0, tile_start, s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), ws13 ? (int)d.T : 0, tile_start, s));
     if (d.fp8) {
         char* xq = ws + plan_ws(d);
         float* xs = (float*)(xq + xq_bytes(d));
@@ -197,23 +198,24 @@ moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const in
                                    c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
         return MOE_OK;
     }
-    HIP_TRY(moe::launch_grouped_up(up_args(c, d, x, offsets, r2p, w13, h, tile_start), s));
+    HIP_TRY(moe::launch_grouped_up(up_args(c, d, x, offsets, r2p, w13, h, tile_start, ws13), s));
     return MOE_OK;
 }
 
 // routed experts' second projection -> y_rows
 moe_status_t do_down(const moe_config_t* c, const Dims& d, const void* h, const int32_t* offsets,
-                     const void* w2, const float* w2s, void* y_rows, char* ws, hipStream_t s) {
+                     const void* w2, const float* w2s, void* y_rows, char* ws, hipStream_t s,
+                     const void* ws2 = nullptr) {
     (void)c;
     int32_t* tile_start = (int32_t*)ws;
-    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), 0, tile_start, s));
+    HIP_TRY(moe::launch_tile_plan(offsets, d.E, tile_m(d), ws2 ? (int)d.T : 0, tile_start, s));
     if (d.fp8) {
         const float* hs = (const float*)((const char*)h + hcode_bytes(d));
         HIP_TRY(moe::launch_fp8_down(h, hs, (int)d.P, (int)d.P, w2, w2s, y_rows, d.H, d.I, offsets, tile_start,
                                      d.E, max_tiles(d), s));
         return MOE_OK;
     }
-    HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start), false, s));
+    HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, s));
     return MOE_OK;
 }
 
@@ -303,27 +305,29 @@ moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* 
 }
 
 moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t T, const void* x, const int32_t* expert_offsets,
-                           const int32_t* row_to_pair, const void* w13, const float* w13_scale, void* h, void* ws,
-                           size_t ws_bytes, hipStream_t stream) {
+                           const int32_t* row_to_pair, const void* w13, const float* w13_scale, const void* ws13,
+                           void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
     MOE_TRY(check_scales(cfg, w13_scale, w13_scale));
+    if (ws13 && !fuse_shared(dims(cfg, T))) return MOE_ERR_INVALID_ARGUMENT;
     if (T == 0) return MOE_OK;
     if (!x || !expert_offsets || !row_to_pair || !w13 || !h || !ws) return MOE_ERR_INVALID_ARGUMENT;
     Dims d = dims(cfg, T);
     if (ws_bytes < up_ws(d)) return MOE_ERR_WORKSPACE;
-    return do_up(cfg, d, x, expert_offsets, row_to_pair, w13, w13_scale, h, (char*)ws, stream);
+    return do_up(cfg, d, x, expert_offsets, row_to_pair, w13, w13_scale, h, (char*)ws, stream, ws13);
 }
 
 moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t T, const void* h, const int32_t* expert_offsets,
-                             const void* w2, const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             const void* w2, const float* w2_scale, const void* ws2, void* y_rows, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
     MOE_TRY(check_scales(cfg, w2_scale, w2_scale));
+    if (ws2 && !fuse_shared(dims(cfg, T))) return MOE_ERR_INVALID_ARGUMENT;
     if (T == 0) return MOE_OK;
     if (!h || !expert_offsets || !w2 || !y_rows || !ws) return MOE_ERR_INVALID_ARGUMENT;
     Dims d = dims(cfg, T);
     if (ws_bytes < plan_ws(d)) return MOE_ERR_WORKSPACE;
-    return do_down(cfg, d, h, expert_offsets, w2, w2_scale, y_rows, (char*)ws, stream);
+    return do_down(cfg, d, h, expert_offsets, w2, w2_scale, y_rows, (char*)ws, stream, ws2);
 }
 
 moe_status_t moe_hidden_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes) {
@@ -345,13 +349,14 @@ moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x, c
 }
 
 moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows, const int32_t* pair_to_row,
-                         const float* topk_w, const float* y_shared, void* out, hipStream_t stream) {
+                         const float* topk_w, const float* y_shared, const void* shared_rows, void* out,
+                         hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
+    if (y_shared && shared_rows) return MOE_ERR_INVALID_ARGUMENT;
     if (T == 0) return MOE_OK;
     if (!y_rows || !pair_to_row || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
-    return hip_status(moe::launch_combine(y_rows, pair_to_row, topk_w, y_shared, nullptr, out,
-                                          cfg->out_dtype == MOE_BF16,
-                                          (int)T, cfg->hidden_size, cfg->top_k, stream));
+    return hip_status(moe::launch_combine(y_rows, pair_to_row, topk_w, y_shared, shared_rows, out,
+                                          cfg->out_dtype == MOE_BF16, (int)T, cfg->hidden_size, cfg->top_k, stream));
 }
 
 moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,

@@ -93,7 +93,7 @@ def test_entry_points_reject_null_pointers(lib):
     assert lib.moe_grouped_swiglu(c, 4, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 30,
                                   None) == 1
     assert lib.moe_shared_ffn(c, 4, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert lib.moe_combine(c, 4, FAKE, FAKE, None, None, FAKE, None) == 1
+    assert lib.moe_combine(c, 4, FAKE, FAKE, None, None, None, FAKE, None) == 1
     assert lib.moe_layer_forward(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, None,
                                  None, None, FAKE, 1 << 30, None) == 1   # shared weights missing
 
@@ -124,7 +124,7 @@ def test_zero_tokens_is_a_noop(lib):
     c = ctypes.byref(cfg_of())
     assert lib.moe_route(c, 0, None, None, None, None, None, None, 0, None) == 0
     assert lib.moe_grouped_swiglu(c, 0, None, None, None, None, None, None, None, None, None, 0, None) == 0
-    assert lib.moe_combine(c, 0, None, None, None, None, None, None) == 0
+    assert lib.moe_combine(c, 0, None, None, None, None, None, None, None) == 0
     assert lib.moe_layer_forward(c, 0, None, None, None, None, None, None, None, None, None, None, None,
                                  None, None, None, 0, None) == 0
 
@@ -147,8 +147,8 @@ def test_fp8_shape_and_scale_rules(lib):
     # FP8 experts need both scale tensors
     assert lib.moe_grouped_swiglu(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
                                   None) == 1
-    assert lib.moe_expert_up(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
-    assert lib.moe_expert_down(c, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_expert_up(c, 4, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_expert_down(c, 4, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 30, None) == 1
 
 
 def test_fp8_hidden_bytes(lib):
@@ -158,6 +158,30 @@ def test_fp8_hidden_bytes(lib):
     assert lib.moe_hidden_bytes(ctypes.byref(c), T, ctypes.byref(n)) == 0
     P, I = T * c.top_k, c.moe_intermediate_size
     assert n.value == (P * I + 255) // 256 * 256 + (I // 128) * P * 4
-    cb = cfg_of()
+    cb = cfg_of(share_expert_dim=0)
     assert lib.moe_hidden_bytes(ctypes.byref(cb), T, ctypes.byref(n)) == 0
     assert n.value == P * I * 2
+
+
+def test_shared_rows_rules(lib):
+    # the shared expert runs in the expert launches only with bf16 experts of its width
+    ok = ctypes.byref(cfg_of())                                    # tiny: I = Is = 128
+    assert lib.moe_expert_up(ok, 0, None, None, None, None, None, FAKE, None, None, 0, None) == 0
+    differ = ctypes.byref(cfg_of(share_expert_dim=64))
+    assert lib.moe_expert_up(differ, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_expert_down(differ, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    fp8 = ctypes.byref(cfg_of(expert_dtype="fp8"))
+    assert lib.moe_expert_up(fp8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    # combine takes one shared term at most
+    assert lib.moe_combine(ok, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_hidden_bytes_cover_shared_rows(lib):
+    T = 10
+    n = ctypes.c_size_t()
+    c = cfg_of()                                                   # fusable
+    assert lib.moe_hidden_bytes(ctypes.byref(c), T, ctypes.byref(n)) == 0
+    assert n.value == (T * c.top_k + T) * c.moe_intermediate_size * 2
+    c = cfg_of(share_expert_dim=0)
+    assert lib.moe_hidden_bytes(ctypes.byref(c), T, ctypes.byref(n)) == 0
+    assert n.value == T * c.top_k * c.moe_intermediate_size * 2

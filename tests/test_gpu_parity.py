@@ -148,6 +148,37 @@ def test_steps_small(name):
     assert np.abs(out.cpu().numpy() - want).max() <= 1e-5 * np.abs(want).max()
 
 
+@pytest.mark.parametrize("name", ["tiny", "small_tiles_multi_tile", "wide_tiles"])
+def test_steps_shared_rows(name):
+    """The split path with the shared expert inside the expert launches
+    (moe_expert_up / moe_expert_down with its weights, combine of its fp16
+    rows) equals moe_layer_forward bit for bit, and the oracle within
+    tolerance; where the widths differ, the entry points refuse."""
+    wl = mi.workload("tiny", **SMALL[name])
+    cfg, T, k = wl.cfg, wl.T, wl.cfg.top_k
+    say(f"[steps_shared_rows] {name}")
+    inp = gpu_inputs(wl)
+    ws = moe.workspace(cfg, T)
+    ids, w = moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ws=ws)
+    counts, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws)
+    if not moe.binding.shared_fusable(cfg):
+        with pytest.raises(moe.MoEError):
+            moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], ws=ws, ws13=inp["ws13"])
+        return
+    h = moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], ws=ws, ws13=inp["ws13"])
+    y_rows = moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], ws=ws, ws2=inp["ws2"])
+    out = moe.moe_combine(cfg, y_rows, p2r, w, shared_rows=y_rows[T * k:])
+    ref_out = moe.moe_layer_forward(cfg, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    ref = orc.layer(cfg, host(inp))
+    _, _, _, corr = orc.route(cfg, *(inp[n].cpu() for n in ("x", "w_router", "router_bias")), want_scores=True)
+    ex = check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], corr, k)
+    err, _ = max_err_over_rms(out.cpu().numpy()[~ex], ref["out"][~ex])
+    say(f"  max_err/rms = {err:.3e}")
+    assert err <= TOL_BF16
+
+
 def test_permute_arbitrary_ids_with_duplicates():
     """Stable grouping is defined for any ids in range, duplicates included."""
     wl = mi.workload("tiny", T=333, num_experts=37, top_k=5)
