@@ -38,13 +38,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
-    for (int j = 0; j < k; ++j) {
-        const int64_t r = pair_to_row[(int64_t)t * k + j];
-        const float w = topk_w[(int64_t)t * k + j];
-        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-        f16x8 v = *(const f16x8*)(y_rows + r * H + col);
+    // all k rows in flight at once: indices and weights first, then the
+    // rows (8 at a time), then the sums in slot order
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    const int32_t* pr = pair_to_row + (int64_t)t * k;
+    const float* pw = topk_w + (int64_t)t * k;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        const int nj = min(8, k - j0);
+        f16x8 v[8];
+        float wj[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += w * (float)v[i];
+        for (int j = 0; j < 8; ++j) {
+            if (j < nj) {
+                v[j] = *(const f16x8*)(y_rows + (int64_t)pr[j0 + j] * H + col);
+                wj[j] = pw[j0 + j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < nj) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += wj[j] * (float)v[j][i];
+            }
     }
     if (OUT_BF16) {
         uint4 o;
