@@ -274,10 +274,30 @@ def bench_decode(args, wl, moe, torch):
     torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / n
     by = layer_bytes(wl, touched)
-    del inp, ws
+    # the same layer call captured once into a HIP graph and replayed, as a
+    # decode loop would run it (launch gaps removed; the work is identical)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, stream=side)   # warm-up on the capture stream
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, stream=side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(n):
+        g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us_graph = ev[0].elapsed_time(ev[1]) * 1e3 / n
+    del g, inp, ws
     torch.cuda.empty_cache()
     return {"workload": wl.name, "tokens": T, "experts_touched": touched, "us_per_step": us,
             "tokens_per_s": T / (us * 1e-6), "gbs": by / (us * 1e-6) / 1e9, "hbm_frac": by / (us * 1e-6) / HBM_PEAK,
+            "us_per_step_graph": us_graph, "hbm_frac_graph": by / (us_graph * 1e-6) / HBM_PEAK,
             "algorithmic_bytes": by}
 
 

@@ -206,6 +206,37 @@ def test_nan_inf_inputs_keep_ids_in_range():
     assert np.array_equal(ids[:3], ref_ids[:3])
 
 
+@pytest.mark.parametrize("name", ["step5_decode", "tiny"])
+def test_graph_replay_matches_eager(name):
+    """moe_layer_forward captured into a HIP graph: every replay (with eager
+    work and synchronisations between them) equals the eager result."""
+    wl = mi.WORKLOADS[name]
+    cfg, T, H = wl.cfg, wl.T, wl.cfg.hidden_size
+    say(f"[graph_replay] {name}")
+    inp = gpu_inputs(wl)
+    ws = moe.workspace(cfg, T)
+    want = moe.moe_layer_forward(cfg, inp, ws=ws)
+    torch.cuda.synchronize()
+    out = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        moe.moe_layer_forward(cfg, inp, out=out, ws=ws, stream=side)
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            moe.moe_layer_forward(cfg, inp, out=out, ws=ws, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        scratch = torch.randn(1 << 20, device=DEV) * 3.0      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {rep} differs from eager"
+        del scratch
+
+
 def test_zero_tokens():
     wl = mi.workload("tiny", T=0)
     inp = gpu_inputs(wl)
