@@ -248,7 +248,11 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         const float swb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swb_v), kt & 63));
         const unsigned char* st = smem + stage * STAGE_BYTES;
         const float* sa_l = (const float*)(st + SA_OFF);
-        i32x8 bfr[TN];
+        // the slice's fragments and row scales first, then every MFMA of the
+        // slice into temporaries, then the block scales: no MFMA result is
+        // consumed right after issue
+        i32x8 bfr[TN], afr[TM];
+        f32x4 sa[TM];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const unsigned char* f = st + A_BYTES + tile_off(4 * wn + j);
@@ -261,16 +265,27 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
                 const int tile = wm + 2 * i;
                 const unsigned char* f = st + tile_off(tile);
                 const u32x4 lo = *(const u32x4*)f, hi = *(const u32x4*)(f + 16);
-                const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                const f32x4 sa = *(const f32x4*)(sa_l + 16 * tile + crow);
-                const f32x4 sga = sa * swa, sgb = sa * swb;
+                afr[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sa[i] = *(const f32x4*)(sa_l + 16 * tile + crow);
+            }
+        }
+        f32x4 r[TM][TN];
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < TM; ++i) {
+            if (i < n_i) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
                     // E8M0 scale 127 = 1.0 on both operands; the fp32 block scales follow
-                    const f32x4 r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bfr[j], z, 0, 0, 0, 127, 0, 127);
-                    acc[i][j] += r * ((MODE == SWIGLU && j >= TN / 2) ? sgb : sga);
-                }
+                    r[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr[i], bfr[j], z, 0, 0, 0, 127, 0, 127);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i < n_i) {
+                const f32x4 sga = sa[i] * swa, sgb = sa[i] * swb;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] += r[i][j] * ((MODE == SWIGLU && j >= TN / 2) ? sgb : sga);
             }
         }
     }
