@@ -237,6 +237,30 @@ def test_graph_replay_matches_eager(name):
         del scratch
 
 
+def test_many_tokens_small_dims():
+    """1.6 M (token, expert) pairs through the multi-kernel permutation and
+    several-tile experts: routing and counts on every token, outputs on a
+    sample (index ranges well beyond the other cases)."""
+    wl = mi.workload("tiny", T=200_000, hidden_size=128, num_experts=64, top_k=8, moe_intermediate_size=128,
+                     share_expert_dim=128)
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    say(f"[many_tokens] T={T} P={T * k}")
+    inp = gpu_inputs(wl)
+    out, ids, w, counts = run_layer(wl, inp)
+    h = host(inp)
+    o_ids, o_w, _, corr = orc.route(cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ids_h = ids.cpu().numpy()
+    ex = check_routing(ids_h, w.cpu().numpy(), o_ids, o_w, corr, k)
+    check_counts(counts.cpu().numpy(), o_ids, ids_h, ex, E)
+    rng = np.random.default_rng(3)
+    cand = np.nonzero(~ex)[0]
+    sample = np.unique(np.concatenate([cand[:3], cand[-3:], rng.choice(cand, 64, replace=False)]))
+    ref = orc.layer(cfg, h, tokens=sample)
+    err, _ = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
+    say(f"  sampled {sample.size} tokens: max_err/rms = {err:.3e}")
+    assert err <= TOL_BF16
+
+
 def test_zero_tokens():
     wl = mi.workload("tiny", T=0)
     inp = gpu_inputs(wl)
