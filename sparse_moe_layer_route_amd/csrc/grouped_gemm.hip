@@ -196,7 +196,10 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     // distinct bank groups.  Wave w moves B blocks (BN/128) w + q and A blocks
     // 2w, 2w+1 (BM 256) or A block w for w < 4 (BM 64) of every slice.
     constexpr int A_PER_WAVE = S::NA >= NW ? S::NA / NW : 1;
-    const bool a_mine = S::NA >= NW || wave < S::NA;
+    // A blocks of a 64-row group hold only that group's rows: a wave whose
+    // group starts past the group's valid rows moves none (those rows are
+    // never multiplied)
+    const bool a_mine = S::NA >= NW ? 64 * ((A_PER_WAVE * wave) >> 2) < valid : wave < S::NA;
     const int quad = lane >> 2, chunk = lane & 3;
     auto block_row = [&](int blk) { return 64 * (blk >> 2) + 16 * (quad >> 2) + 4 * (blk & 3) + (quad & 3); };
     const uint16_t* a_src[A_PER_WAVE];
@@ -293,7 +296,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         }
     };
     // DMAs per slice of this wave: B_PER_WAVE + A_PER_WAVE if it moves A blocks
-    constexpr int D_HI = B_PER_WAVE + A_PER_WAVE, D_LO = S::NA >= NW ? D_HI : B_PER_WAVE;
+    constexpr int D_HI = B_PER_WAVE + A_PER_WAVE, D_LO = B_PER_WAVE;
     // one step: slice kt's fragments are in registers (cur); make slice kt+1
     // visible, refill the stage slice kt-1 used, read slice kt+1 (nxt), multiply
     auto step = [&](int kt, const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb) {
