@@ -32,17 +32,21 @@ def _matvec(rows, v):
     return [math.fsum(r[i] * v[i] for i in range(len(v))) for r in rows]
 
 
-def token_forward(cfg, x, wg, bias, w13, w2, ws13=None, ws2=None):
+def token_forward(cfg, x, wg, bias, w13, w2, ws13=None, ws2=None, ids=None):
     """One token.  All arguments are nested Python lists of floats:
     x [H], wg [E][H], bias [E], w13 [E][2I][H], w2 [E][H][I], ws13 [2Is][H],
-    ws2 [H][Is].  Returns (ids, weights, out[H], corrected scores)."""
+    ws2 [H][Is].  ids (optional, k ints in [0, E)) replays an expert choice
+    instead of selecting one.  Returns (ids, weights, out[H], corrected
+    scores)."""
     E, k, I = cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size
     logits = _matvec(wg, x)
     s = [_sigmoid(a) for a in logits]
     c = [s[e] + bias[e] for e in range(E)]
-    order = sorted(range(E), key=lambda e: (0 if c[e] == c[e] else 1,
-                                            -c[e] if c[e] == c[e] else 0.0, e))
-    ids = order[:k]
+    if ids is None:
+        order = sorted(range(E), key=lambda e: (0 if c[e] == c[e] else 1,
+                                                -c[e] if c[e] == c[e] else 0.0, e))
+        ids = order[:k]
+    ids = list(ids)
     w = [s[e] for e in ids]
     if cfg.norm_expert_weight:
         tot = math.fsum(w)

@@ -148,10 +148,10 @@ static int ranks_above(float ca, int ia, float cb, int ib) {
 
 /* ---- routing ------------------------------------------------------------ */
 
-static void route_token(const orc_cfg* c, const uint16_t* xt, const uint16_t* wg,
-                        const float* bias, int32_t* ids, float* w,
+/* logits, raw scores s and corrected scores c of one token over all E experts */
+static void score_token(const orc_cfg* c, const uint16_t* xt, const uint16_t* wg, const float* bias,
                         float* logits_out, float* corr_out, float* s_buf, float* c_buf) {
-    const int H = c->H, E = c->E, k = c->k;
+    const int H = c->H, E = c->E;
     for (int e = 0; e < E; ++e) {
         double acc = 0.0;
         const uint16_t* we = wg + (size_t)e * H;
@@ -159,11 +159,15 @@ static void route_token(const orc_cfg* c, const uint16_t* xt, const uint16_t* wg
         float a = (float)acc;
         float s = (float)(1.0 / (1.0 + exp(-(double)a)));
         s_buf[e] = s;
-        c_buf[e] = s + bias[e];
+        c_buf[e] = bias ? s + bias[e] : s;
         if (logits_out) logits_out[e] = a;
         if (corr_out) corr_out[e] = c_buf[e];
     }
-    /* selection: k rounds, each picks the best not yet chosen */
+}
+
+/* selection: k rounds, each picks the best expert not yet chosen */
+static void select_topk(const orc_cfg* c, const float* c_buf, int32_t* ids) {
+    const int E = c->E, k = c->k;
     unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
     for (int j = 0; j < k; ++j) {
         int best = -1;
@@ -177,6 +181,11 @@ static void route_token(const orc_cfg* c, const uint16_t* xt, const uint16_t* wg
         ids[j] = best;
     }
     free(taken);
+}
+
+/* the k weights of the chosen experts from their raw scores */
+static void weigh(const orc_cfg* c, const float* s_buf, const int32_t* ids, float* w) {
+    const int k = c->k;
     double sum = 0.0;
     for (int j = 0; j < k; ++j) sum += (double)s_buf[ids[j]];
     for (int j = 0; j < k; ++j) {
@@ -186,10 +195,35 @@ static void route_token(const orc_cfg* c, const uint16_t* xt, const uint16_t* wg
     }
 }
 
+/* Routing of one token.  With ids_in == NULL the k experts are chosen from
+ * the corrected scores.  With ids_in given (routing replay: miles page
+ * "Step-5-Preview", section 5.2 Algorithm, where the trainer reuses the
+ * rollout's expert choices) the choice is taken as given, each id clamped to
+ * [0, E-1] as the selection's own guard does, and only the weights are
+ * computed, from the current raw scores.  That the replayed choice keeps the
+ * weights of the model being run is this oracle's reading: the page says only
+ * that the expert choices are replayed. */
+static void route_token(const orc_cfg* c, const uint16_t* xt, const uint16_t* wg,
+                        const float* bias, const int32_t* ids_in, int32_t* ids, float* w,
+                        float* logits_out, float* corr_out, float* s_buf, float* c_buf) {
+    score_token(c, xt, wg, bias, logits_out, corr_out, s_buf, c_buf);
+    if (ids_in) {
+        for (int j = 0; j < c->k; ++j) {
+            int e = ids_in[j];
+            ids[j] = e < 0 ? 0 : (e > c->E - 1 ? c->E - 1 : e);
+        }
+    } else {
+        select_topk(c, c_buf, ids);
+    }
+    weigh(c, s_buf, ids, w);
+}
+
 /* Route T tokens.  x [T,H] bf16, wg [E,H] bf16, bias [E] fp32 ->
- * ids [T,k] int32, w [T,k] fp32; logits/corrected [T,E] fp32 if non-NULL. */
+ * ids [T,k] int32, w [T,k] fp32; logits/corrected [T,E] fp32 if non-NULL.
+ * ids_in [T,k] (optional): replayed expert choices; bias is then unused. */
 int orc_route(const orc_cfg* c, int64_t T, const uint16_t* x, const uint16_t* wg,
-              const float* bias, int32_t* ids, float* w, float* logits, float* corrected) {
+              const float* bias, const int32_t* ids_in, int32_t* ids, float* w, float* logits,
+              float* corrected) {
     if (!c || c->k < 1 || c->k > c->E) return 1;
 #pragma omp parallel
     {
@@ -197,7 +231,8 @@ int orc_route(const orc_cfg* c, int64_t T, const uint16_t* x, const uint16_t* wg
         float* c_buf = (float*)malloc(sizeof(float) * (size_t)c->E);
 #pragma omp for schedule(dynamic, 4)
         for (int64_t t = 0; t < T; ++t)
-            route_token(c, x + t * c->H, wg, bias, ids + t * c->k, w + t * c->k,
+            route_token(c, x + t * c->H, wg, bias, ids_in ? ids_in + t * c->k : NULL, ids + t * c->k,
+                        w + t * c->k,
                         logits ? logits + t * c->E : NULL, corrected ? corrected + t * c->E : NULL,
                         s_buf, c_buf);
         free(s_buf);
@@ -244,9 +279,11 @@ static void mlp(const orc_cfg* c, int N, const float* xin, const void* W13, cons
  * (fp32, optional) expose the per-expert outputs for the tests.
  * w13: [E,2I,H] bf16 or E4M3 codes; w13s [E,2I/128,H/128] (FP8 only);
  * w2: [E,H,I]; w2s [E,H/128,I/128]; ws13 [2Is,H] bf16; ws2 [H,Is] bf16.
+ * ids_in [T,k] (optional, indexed by token like x): replayed expert choices,
+ * see route_token.
  */
 int orc_layer(const orc_cfg* c, int64_t n, const int64_t* tok, const uint16_t* x,
-              const uint16_t* wg, const float* bias, const void* w13, const float* w13s,
+              const uint16_t* wg, const float* bias, const int32_t* ids_in, const void* w13, const float* w13s,
               const void* w2, const float* w2s, const uint16_t* ws13, const uint16_t* ws2,
               float* out, int32_t* ids, float* w, float* y_routed, float* y_shared) {
     if (!c || c->k < 1 || c->k > c->E) return 1;
@@ -269,7 +306,7 @@ int orc_layer(const orc_cfg* c, int64_t n, const int64_t* tok, const uint16_t* x
             const uint16_t* xt = x + t * H;
             int32_t* id = ids + r * k;
             float* wt = w + r * k;
-            route_token(c, xt, wg, bias, id, wt, NULL, NULL, s_buf, c_buf);
+            route_token(c, xt, wg, bias, ids_in ? ids_in + t * k : NULL, id, wt, NULL, NULL, s_buf, c_buf);
             for (int h = 0; h < H; ++h) xin[h] = bf16_val(xt[h]);
             memcpy(xq, xin, sizeof(float) * (size_t)H);
             if (c->fp8) quant_row_fp8(xq, H);
@@ -320,6 +357,18 @@ int orc_permute(int64_t T, int32_t k, int32_t E, const int32_t* ids, int32_t* co
         pair_to_row[p] = r;
     }
     free(fill);
+    return 0;
+}
+
+/* Static balanced routing (AutoModel page, benchmark table: the Step-5
+ * benchmark runs with a fake, balanced, static expert routing).  The page
+ * gives no rule; this oracle's reading is the round-robin that deals the T*k
+ * (token, slot) pairs to the experts in turn: pair p = t*k + j goes to expert
+ * p mod E.  Every expert gets floor(T*k/E) or one more pair, and the k
+ * experts of one token are distinct because k <= E. */
+int orc_balanced_ids(int64_t T, int32_t k, int32_t E, int32_t* ids) {
+    if (k < 1 || k > E || T < 0) return 1;
+    for (int64_t p = 0; p < T * k; ++p) ids[p] = (int32_t)(p % E);
     return 0;
 }
 

@@ -45,9 +45,10 @@ def lib():
             build(force=False)
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
-        L.orc_route.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P]
-        L.orc_layer.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P,
+        L.orc_route.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P]
+        L.orc_layer.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P, P,
                                 P, P, P, P, P, P, P]
+        L.orc_balanced_ids.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
         L.orc_permute.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
         L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_decode.restype = ctypes.c_double
@@ -92,12 +93,15 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def route(cfg, x, w_router, router_bias, want_scores=False):
+def route(cfg, x, w_router, router_bias, want_scores=False, ids_in=None):
     """Routing of every token: ids [T,k] int32, weights [T,k] fp32
-    (+ logits, corrected scores [T,E] fp32 when want_scores)."""
+    (+ logits, corrected scores [T,E] fp32 when want_scores).  With ids_in
+    [T,k] the expert choices are replayed (clamped to [0, E-1]) and only the
+    weights come from the router; router_bias may then be None."""
     x = _np(x, np.uint16)
     wg = _np(w_router, np.uint16)
-    b = _np(router_bias, np.float32)
+    b = None if router_bias is None else _np(router_bias, np.float32)
+    ids_in = None if ids_in is None else _np(ids_in, np.int32)
     T = x.shape[0]
     E, k = cfg.num_experts, cfg.top_k
     ids = np.zeros((T, k), np.int32)
@@ -105,19 +109,23 @@ def route(cfg, x, w_router, router_bias, want_scores=False):
     lg = np.zeros((T, E), np.float32) if want_scores else None
     cs = np.zeros((T, E), np.float32) if want_scores else None
     c = _cfg(cfg)
-    rc = lib().orc_route(ctypes.byref(c), T, _p(x), _p(wg), _p(b), _p(ids), _p(w), _p(lg), _p(cs))
+    if ids_in is not None:
+        assert ids_in.shape == (T, k), ids_in.shape
+    rc = lib().orc_route(ctypes.byref(c), T, _p(x), _p(wg), _p(b), _p(ids_in), _p(ids), _p(w), _p(lg),
+                         _p(cs))
     assert rc == 0, rc
     if want_scores:
         return ids, w, lg, cs
     return ids, w
 
 
-def layer(cfg, inp, tokens=None, want_parts=False):
+def layer(cfg, inp, tokens=None, want_parts=False, ids_in=None):
     """Layer output for the given token rows (all rows if tokens is None).
 
     inp holds the tensors of ``moe_inputs.make_inputs``.  Returns a dict with
     out [n,H] fp32, ids [n,k], w [n,k] and, if want_parts, y_routed [n,k,H]
-    and y_shared [n,H]."""
+    and y_shared [n,H].  ids_in [T,k] (rows indexed like x) replays the given
+    expert choices instead of selecting them."""
     x = _np(inp["x"], np.uint16)
     T = x.shape[0]
     tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
@@ -138,7 +146,10 @@ def layer(cfg, inp, tokens=None, want_parts=False):
     yr = np.zeros((n, k, H), np.float32) if want_parts else None
     ys = np.zeros((n, H), np.float32) if want_parts else None
     c = _cfg(cfg)
-    rc = lib().orc_layer(ctypes.byref(c), n, _p(tok), _p(x), _p(wg), _p(b), _p(w13), _p(w13s),
+    ids_in = None if ids_in is None else _np(ids_in, np.int32)
+    if ids_in is not None:
+        assert ids_in.shape == (T, k), ids_in.shape
+    rc = lib().orc_layer(ctypes.byref(c), n, _p(tok), _p(x), _p(wg), _p(b), _p(ids_in), _p(w13), _p(w13s),
                          _p(w2), _p(w2s), _p(ws13), _p(ws2), _p(out), _p(ids), _p(w), _p(yr), _p(ys))
     assert rc == 0, rc
     res = {"out": out, "ids": ids, "w": w}
@@ -158,6 +169,14 @@ def permute(ids, num_experts):
     rc = lib().orc_permute(T, k, num_experts, _p(ids), _p(counts), _p(offs), _p(r2p), _p(p2r))
     assert rc == 0, rc
     return counts, offs, r2p, p2r
+
+
+def balanced_ids(T, top_k, num_experts):
+    """The static balanced routing: pair t*k + j goes to expert (t*k + j) mod E."""
+    ids = np.zeros((T, top_k), np.int32)
+    rc = lib().orc_balanced_ids(T, top_k, num_experts, _p(ids))
+    assert rc == 0, rc
+    return ids
 
 
 def e4m3_decode(code: int) -> float:

@@ -288,6 +288,120 @@ def test_oracle_matches_brute_force(orc, x_scale):
 
 
 # --------------------------------------------------------------------------
+# routing replay and static balanced routing
+
+
+def _replay_ids(wl, seed):
+    """k distinct experts per token, drawn at random (not the router's choice)."""
+    rng = np.random.default_rng(seed)
+    E, k = wl.cfg.num_experts, wl.cfg.top_k
+    return np.stack([rng.choice(E, k, replace=False) for _ in range(wl.T)]).astype(np.int32)
+
+
+def test_replay_of_own_choice_reproduces_route(orc):
+    """Replaying the router's own choice gives back its ids and weights
+    exactly; the bias plays no part once the choice is given."""
+    wl = tiny()
+    inp = _inputs(wl)
+    ids, w = orc.route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"])
+    ids2, w2 = orc.route(wl.cfg, inp["x"], inp["w_router"], None, ids_in=ids)
+    assert np.array_equal(ids, ids2) and np.array_equal(w, w2)
+    rnd = _replay_ids(wl, 1)
+    _, wa = orc.route(wl.cfg, inp["x"], inp["w_router"], None, ids_in=rnd)
+    _, wb = orc.route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"] * 100, ids_in=rnd)
+    assert np.array_equal(wa, wb)
+
+
+def test_replay_weights_zero_input_closed_form(orc):
+    """x = 0 -> every raw score is 0.5, whatever the replayed ids (duplicates
+    included): weights scale/k with normalisation, scale/2 without."""
+    wl = tiny()
+    inp = _inputs(wl)
+    x = torch.zeros_like(inp["x"])
+    ids = _replay_ids(wl, 2)
+    ids[0, 1] = ids[0, 0]
+    got, w = orc.route(wl.cfg, x, inp["w_router"], None, ids_in=ids)
+    assert np.array_equal(got, ids)
+    assert np.allclose(w, 3.0 / wl.cfg.top_k, rtol=0, atol=1e-7)
+    _, w2 = orc.route(dataclasses.replace(wl.cfg, norm_expert_weight=False), x, inp["w_router"], None,
+                      ids_in=ids)
+    assert np.array_equal(w2, np.full_like(w2, 1.5))
+
+
+def test_replay_clamps_out_of_range_ids(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    E = wl.cfg.num_experts
+    ids = _replay_ids(wl, 3)
+    bad = ids.copy()
+    bad[:, 0] = -7
+    bad[:, 1] = E + 5
+    fixed = ids.copy()
+    fixed[:, 0] = 0
+    fixed[:, 1] = E - 1
+    g1, w1 = orc.route(wl.cfg, inp["x"], inp["w_router"], None, ids_in=bad)
+    g2, w2 = orc.route(wl.cfg, inp["x"], inp["w_router"], None, ids_in=fixed)
+    assert np.array_equal(g1, fixed) and np.array_equal(w1, w2)
+    r1 = orc.layer(wl.cfg, inp, ids_in=bad, tokens=[0, 9])
+    r2 = orc.layer(wl.cfg, inp, ids_in=fixed, tokens=[0, 9])
+    assert np.array_equal(r1["out"], r2["out"])
+
+
+@pytest.mark.parametrize("x_scale", [1.0, 40.0])
+def test_replayed_layer_matches_brute_force(orc, x_scale):
+    wl = tiny(x_scale=x_scale)
+    inp = _inputs(wl)
+    ids_in = _replay_ids(wl, 4)
+    toks = [0, 1, 30, 63]
+    res = orc.layer(wl.cfg, inp, tokens=toks, ids_in=ids_in)
+    f = lambda t: t.double().tolist()
+    x = f(inp["x"])
+    args = (f(inp["w_router"]), f(inp["router_bias"]), f(inp["w13"]), f(inp["w2"]), f(inp["ws13"]), f(inp["ws2"]))
+    for r, t in enumerate(toks):
+        ids, w, out, _ = brute.token_forward(wl.cfg, x[t], *args, ids=ids_in[t].tolist())
+        assert res["ids"][r].tolist() == ids
+        assert np.allclose(res["w"][r], w, rtol=1e-6)
+        out = np.array(out)
+        assert np.abs(res["out"][r] - out).max() <= 1e-5 * np.abs(out).max()
+
+
+def test_replayed_layer_of_own_choice_equals_layer(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    ref = orc.layer(wl.cfg, inp)
+    rep = orc.layer(wl.cfg, inp, ids_in=ref["ids"])
+    for key in ("out", "ids", "w"):
+        assert np.array_equal(ref[key], rep[key])
+
+
+def test_replay_with_identical_experts_is_independent_of_ids(orc):
+    """All experts equal and weights normalised: the routed part is
+    scale x the one MLP for any choice, so out = 3 MLP(x) + shared(x)."""
+    wl = tiny()
+    inp = _inputs(wl)
+    inp["w13"][:] = inp["w13"][0]
+    inp["w2"][:] = inp["w2"][0]
+    res = orc.layer(wl.cfg, inp, ids_in=_replay_ids(wl, 5))
+    want = 3.0 * _torch_mlp(inp["x"], inp["w13"][0], inp["w2"][0], wl.cfg.swiglu_limit) + \
+        _torch_mlp(inp["x"], inp["ws13"], inp["ws2"], wl.cfg.swiglu_limit_shared)
+    assert np.abs(res["out"] - want.numpy()).max() <= 1e-5 * np.abs(want.numpy()).max()
+
+
+@pytest.mark.parametrize("T,k,E", [(8192, 8, 352), (64, 8, 352), (7, 3, 5), (5, 4, 4), (1, 1, 1), (0, 2, 3),
+                                   (100, 8, 288)])
+def test_balanced_ids_are_balanced_and_distinct(orc, T, k, E):
+    ids = orc.balanced_ids(T, k, E)
+    assert ids.shape == (T, k) and ids.dtype == np.int32
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    P = T * k
+    assert counts.sum() == P and counts.min() == P // E and counts.max() == -(-P // E)
+    assert all(len(set(r)) == k for r in ids.tolist())
+    assert ids.min(initial=0) >= 0 and ids.max(initial=0) < E
+    # static: the same for every call, and token t's choice does not depend on T
+    assert np.array_equal(orc.balanced_ids(T + 3, k, E)[:T], ids)
+
+
+# --------------------------------------------------------------------------
 # permutation
 
 
