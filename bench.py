@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--decode-workload", default="step5_decode")
     ap.add_argument("--fp8-workload", default="step5_fp8_prefill", help="'' to skip the FP8 report")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-balanced", action="store_true", help="skip the static balanced routing report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -174,6 +175,17 @@ def main():
                       "up_ms": rf["up_ms"], "up_gbs": ub / (rf["up_ms"] * 1e-3) / 1e9,
                       "up_hbm_frac": ub / (rf["up_ms"] * 1e-3) / HBM_PEAK}
 
+    if not args.no_balanced:
+        note(f"{wl.name} with the static balanced routing")
+        rb = time_balanced(args, wl, moe, torch, mi)
+        res["balanced_routing"] = {
+            "workload": wl.name, "routing": "static balanced (pair t*k+j -> expert (t*k+j) mod E), "
+                                            "moe_balanced_ids + moe_layer_forward_routed",
+            "experts_touched": rb["touched"], "ms_per_step": rb["ms_step"], "tokens_per_s": T / (rb["ms_step"] * 1e-3),
+            "tflops": layer_flops(wl, rb["touched"]) / (rb["ms_step"] * 1e-3) / 1e12,
+            "mfma_frac": layer_flops(wl, rb["touched"]) / (rb["ms_step"] * 1e-3) / BF16_PEAK,
+            "hbm_frac": layer_bytes(wl, rb["touched"]) / (rb["ms_step"] * 1e-3) / HBM_PEAK}
+
     if not args.no_decode:
         note(f"decode workload {args.decode_workload}")
         res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
@@ -253,6 +265,38 @@ def time_layer(args, wl, moe, torch, mi):
     return {"ms_step": ms_step, "up_ms": up_ms, "layer_forward_ms": layer_fwd_ms, "touched": touched}
 
 
+def time_balanced(args, wl, moe, torch, mi):
+    """The layer with the static balanced routing (the routing the Step-5
+    full-depth benchmark runs): each step writes the balanced ids and runs
+    moe_layer_forward_routed; steps bracketed by HIP events on the stream."""
+    cfg, T, H, E = wl.cfg, wl.T, wl.cfg.hidden_size, wl.cfg.num_experts
+    inp = mi.make_inputs(wl, "cuda", seed=0)
+    ws = moe.workspace(cfg, T)
+    stream = torch.cuda.current_stream()
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+
+    def step():
+        moe.moe_balanced_ids(cfg, T, ids, stream=stream)
+        moe.moe_layer_forward_routed(cfg, inp, ids, out=out, ws=ws, expert_counts=counts, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    touched = int((counts > 0).sum().item())
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    return {"ms_step": ms, "touched": touched}
+
+
 def bench_decode(args, wl, moe, torch):
     import moe_inputs as mi
     inp = mi.make_inputs(wl, "cuda", seed=0)
@@ -310,7 +354,7 @@ def cpu_baseline(args, wl, mi):
     host = {k: v.cpu() for k, v in inp.items()}
     del inp
     rng = np.random.default_rng(0)
-    n = 8
+    n = 4 * orc.num_threads()          # tokens are spread over the threads: calibrate with all busy
     t0 = time.perf_counter()
     orc.layer(wl.cfg, host, tokens=rng.choice(wl.T, n, replace=False))
     dt = time.perf_counter() - t0

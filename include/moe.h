@@ -185,6 +185,45 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
                                int32_t* expert_counts_out,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Routing replay (miles page "Step-5-Preview", section 5.2 Algorithm: the
+ * trainer reruns the expert choices its rollout made).  topk_ids [T,k] int32
+ * is an INPUT: the replayed choice, each id clamped to [0, E-1] (callers
+ * should pass ids in range; the clamp only keeps every access in bounds).
+ * Duplicate ids in a row are allowed; each slot is treated on its own.
+ * topk_w [T,k] fp32 = the raw sigmoid scores of those experts under the
+ * current router (x, w_router as for moe_route), divided by their sum if
+ * norm_expert_weight, times router_scaling_factor.  That the weights come
+ * from the current router is this library's reading; the page says only
+ * that the choices are replayed.  Replaying moe_route's own ids gives back
+ * its weights bit for bit.  There is no routing bias: it only steers the
+ * choice.  Uses ws for the logits (moe_workspace_size covers it). */
+moe_status_t moe_route_replay(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                              const int32_t* topk_ids, float* topk_w,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static balanced routing for benchmarks (AutoModel page, benchmark table:
+ * the Step-5 benchmark replaces the router's choice with a fake, balanced,
+ * static one).  Writes topk_ids [T,k] int32 with pair p = t*k + j sent to
+ * expert p mod E: every expert gets floor(T*k/E) or one more pair, and the
+ * k experts of a token are distinct.  The rule is this library's reading;
+ * the page names the mode only.  Feed the result to
+ * moe_layer_forward_routed. */
+moe_status_t moe_balanced_ids(const moe_config_t* cfg, int64_t T, int32_t* topk_ids, hipStream_t stream);
+
+/* The whole layer with the expert choice supplied by the caller (routing
+ * replay, or the static balanced routing above): the weights as in
+ * moe_route_replay, then the same permute, routed and shared experts and
+ * combine as moe_layer_forward.  topk_ids [T,k] int32 is an input (clamped
+ * to [0, E-1]); the other arguments are those of moe_layer_forward, less
+ * router_bias and topk_ids_out.  Same workspace size. */
+moe_status_t moe_layer_forward_routed(const moe_config_t* cfg, int64_t T, const void* x,
+                                      const void* w_router, const int32_t* topk_ids,
+                                      const void* w13, const float* w13_scale,
+                                      const void* w2, const float* w2_scale,
+                                      const void* ws13, const void* ws2, void* out,
+                                      float* topk_w_out, int32_t* expert_counts_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status_t status);
 

@@ -178,6 +178,15 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0,
     return out
 
 
+def random_expert_ids(wl: Workload, device="cpu", seed: int = 0) -> torch.Tensor:
+    """A seeded stand-in for a replayed expert choice: [T,k] int32, k distinct
+    experts per token drawn uniformly (the first k of a random permutation)."""
+    c = wl.cfg
+    g = _gen("cpu", seed, "replay_ids")
+    keys = torch.rand((wl.T, c.num_experts), generator=g)
+    return keys.argsort(dim=1)[:, :c.top_k].to(torch.int32).contiguous().to(device)
+
+
 def workload(name: str, **overrides) -> Workload:
     wl = WORKLOADS[name]
     if not overrides:

@@ -23,7 +23,7 @@ MOE_BF16, MOE_FP32, MOE_FP8_E4M3_B128 = range(3)
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_expert_up",
             "moe_expert_down", "moe_hidden_bytes", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
-            "moe_status_string")
+            "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_status_string")
 
 
 class MoEError(RuntimeError):
@@ -67,6 +67,9 @@ def load(path: Optional[str] = None):
         "moe_shared_ffn": [C, I64, P, P, P, P, P, SZ, P],
         "moe_combine": [C, I64, P, P, P, P, P, P, P],
         "moe_layer_forward": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_route_replay": [C, I64, P, P, P, P, P, SZ, P],
+        "moe_balanced_ids": [C, I64, P, P],
+        "moe_layer_forward_routed": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -151,6 +154,33 @@ def moe_route(cfg, x, w_router, router_bias, topk_ids=None, topk_w=None, ws=None
                           _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_route")
     return topk_ids, topk_w
+
+
+def moe_route_replay(cfg, x, w_router, topk_ids, topk_w=None, ws=None, stream=None):
+    """Weights of the caller's expert choice topk_ids [T,k] under the current
+    router; returns topk_w [T,k] fp32."""
+    T, H, E, k = x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k
+    topk_w = topk_w if topk_w is not None else torch.empty((T, k), dtype=torch.float32, device=x.device)
+    ws = ws if ws is not None else workspace(cfg, T, x.device)
+    c = make_config(cfg)
+    st = load().moe_route_replay(ctypes.byref(c), T, _ptr(x, torch.bfloat16, (T, H), "x"),
+                                 _ptr(w_router, torch.bfloat16, (E, H), "w_router"),
+                                 _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+                                 _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+                                 _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "moe_route_replay")
+    return topk_w
+
+
+def moe_balanced_ids(cfg, T: int, topk_ids=None, device="cuda", stream=None):
+    """The static balanced routing: topk_ids [T,k] int32, pair t*k+j -> expert (t*k+j) mod E."""
+    k = cfg.top_k
+    topk_ids = topk_ids if topk_ids is not None else torch.empty((T, k), dtype=torch.int32, device=device)
+    c = make_config(cfg)
+    st = load().moe_balanced_ids(ctypes.byref(c), T, _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+                                 _stream(stream))
+    _check(st, "moe_balanced_ids")
+    return topk_ids
 
 
 def moe_permute(cfg, topk_ids, ws=None, stream=None):
@@ -319,4 +349,36 @@ def moe_layer_forward(cfg, inp: dict, out=None, ws=None, topk_ids=None, topk_w=N
         _ptr(expert_counts, torch.int32, (E,), "expert_counts"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_layer_forward")
+    return out
+
+
+def moe_layer_forward_routed(cfg, inp: dict, topk_ids, out=None, ws=None, topk_w=None, expert_counts=None,
+                             stream=None):
+    """The whole layer with the expert choice topk_ids [T,k] int32 given by
+    the caller (routing replay or the static balanced routing); the tensors
+    of ``inp`` as for moe_layer_forward (router_bias is not used).  Returns
+    out [T,H]."""
+    x = inp["x"]
+    T, H, E, k, I, Is = (x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size,
+                         cfg.share_expert_dim)
+    wdt = _weights_dtype(cfg)
+    fp8 = cfg.expert_dtype == "fp8"
+    out = out if out is not None else torch.empty((T, H), dtype=_out_dtype(cfg), device=x.device)
+    ws = ws if ws is not None else workspace(cfg, T, x.device)
+    c = make_config(cfg)
+    st = load().moe_layer_forward_routed(
+        ctypes.byref(c), T, _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(inp["w_router"], torch.bfloat16, (E, H), "w_router"),
+        _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+        _ptr(inp["w13"], wdt, (E, 2 * I, H), "w13"),
+        _ptr(inp.get("w13_scale"), torch.float32, (E, 2 * I // 128, H // 128) if fp8 else None, "w13_scale"),
+        _ptr(inp["w2"], wdt, (E, H, I), "w2"),
+        _ptr(inp.get("w2_scale"), torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
+        _ptr(inp.get("ws13") if Is else None, torch.bfloat16, (2 * Is, H), "ws13"),
+        _ptr(inp.get("ws2") if Is else None, torch.bfloat16, (H, Is), "ws2"),
+        _ptr(out, _out_dtype(cfg), (T, H), "out"),
+        _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+        _ptr(expert_counts, torch.int32, (E,), "expert_counts"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "moe_layer_forward_routed")
     return out

@@ -121,6 +121,16 @@ moe_status_t do_route(const moe_config_t* c, const Dims& d, const void* x, const
     return MOE_OK;
 }
 
+// router logits, then the weights of caller-supplied ids
+moe_status_t do_replay(const moe_config_t* c, const Dims& d, const void* x, const void* wr, const int32_t* ids,
+                       float* w, char* ws, hipStream_t s) {
+    float* logits = (float*)ws;
+    HIP_TRY(moe::launch_router_logits(x, wr, logits, (int)d.T, d.E, d.H, s));
+    HIP_TRY(moe::launch_replay_weights(logits, moe::router_splits(d.T, d.H), ids, (int)d.T, d.E, d.k,
+                                       c->router_scaling_factor, c->norm_expert_weight, w, s));
+    return MOE_OK;
+}
+
 int tile_m(const Dims& d) { return d.fp8 ? moe::fp8_tile_m() : moe::grouped_tile_m(d.P, d.E); }
 
 // upper bound on the tiles of a grouped launch: every group may end in a
@@ -256,6 +266,54 @@ moe_status_t do_shared(const moe_config_t* c, const Dims& d, const void* x, cons
     return MOE_OK;
 }
 
+// argument checks shared by the whole-layer entry points
+moe_status_t check_layer(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                         const void* w13, const float* w13_scale, const void* w2, const float* w2_scale,
+                         const void* ws13, const void* ws2, const void* out, const void* ws, size_t ws_bytes) {
+    MOE_TRY(check_config(cfg, T));
+    MOE_TRY(check_scales(cfg, w13_scale, w2_scale));
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !w13 || !w2 || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    if (cfg->share_expert_dim > 0 && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < layer_ws(dims(cfg, T)).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+// the layer after routing: permute, routed + shared experts, combine
+moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs& L, char* base, const void* x,
+                           const int32_t* ids, const float* w, const void* w13, const float* w13_scale,
+                           const void* w2, const float* w2_scale, const void* ws13, const void* ws2, void* out,
+                           int32_t* expert_counts_out, hipStream_t stream) {
+    const int T = (int)d.T;
+    int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)(base + L.counts);
+    int32_t* offsets = (int32_t*)(base + L.offsets);
+    int32_t* r2p = (int32_t*)(base + L.r2p);
+    int32_t* p2r = (int32_t*)(base + L.p2r);
+    char* y_rows = base + L.y_rows;
+    char* step = base + L.step;
+    const bool out_bf16 = cfg->out_dtype == MOE_BF16;
+    if (fuse_shared(d)) {
+        // one tile plan for both projections; the shared expert is group E.
+        // The plan sits in the layer's own area: the permutation's scratch
+        // (at `step`) is still in use while the plan is made.
+        int32_t* tile_start = (int32_t*)(base + L.plan);
+        void* h = step;
+        HIP_TRY(moe::launch_permute_plan(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, tile_m(d), T,
+                                         tile_start, stream));
+        HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, ws13), stream));
+        HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, stream));
+        HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * d.H * 2, out, out_bf16, T,
+                                    d.H, d.k, stream));
+        return MOE_OK;
+    }
+    HIP_TRY(moe::launch_permute(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
+    float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
+    MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w13_scale, w2, w2_scale, y_rows, step, stream));
+    if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
+    HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, nullptr, out, out_bf16, T, d.H, d.k, stream));
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -364,46 +422,52 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
                                const float* w2_scale, const void* ws13, const void* ws2, void* out,
                                int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
-    MOE_TRY(check_config(cfg, T));
-    MOE_TRY(check_scales(cfg, w13_scale, w2_scale));
+    MOE_TRY(check_layer(cfg, T, x, w_router, w13, w13_scale, w2, w2_scale, ws13, ws2, out, ws, ws_bytes));
     if (T == 0) return MOE_OK;
-    if (!x || !w_router || !router_bias || !w13 || !w2 || !out || !ws) return MOE_ERR_INVALID_ARGUMENT;
-    if (cfg->share_expert_dim > 0 && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!router_bias) return MOE_ERR_INVALID_ARGUMENT;
     Dims d = dims(cfg, T);
     LayerWs L = layer_ws(d);
-    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     char* base = (char*)ws;
     int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
-    int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)(base + L.counts);
-    int32_t* offsets = (int32_t*)(base + L.offsets);
-    int32_t* r2p = (int32_t*)(base + L.r2p);
-    int32_t* p2r = (int32_t*)(base + L.p2r);
-    char* y_rows = base + L.y_rows;
-    char* step = base + L.step;
-    const bool out_bf16 = cfg->out_dtype == MOE_BF16;
+    MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
+    return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
+                         expert_counts_out, stream);
+}
 
-    MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, step, stream));
-    if (fuse_shared(d)) {
-        // one tile plan for both projections; the shared expert is group E.
-        // The plan sits in the layer's own area: the permutation's scratch
-        // (at `step`) is still in use while the plan is made.
-        int32_t* tile_start = (int32_t*)(base + L.plan);
-        void* h = step;
-        HIP_TRY(moe::launch_permute_plan(ids, (int)T, d.k, d.E, counts, offsets, r2p, p2r, step, tile_m(d),
-                                         (int)d.T, tile_start, stream));
-        HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, ws13), stream));
-        HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, stream));
-        HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * d.H * 2, out, out_bf16, (int)T,
-                                    d.H, d.k, stream));
-        return MOE_OK;
-    }
-    HIP_TRY(moe::launch_permute(ids, (int)T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
-    float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
-    MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w13_scale, w2, w2_scale, y_rows, step, stream));
-    if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
-    HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, nullptr, out, out_bf16, (int)T, d.H, d.k, stream));
-    return MOE_OK;
+moe_status_t moe_route_replay(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                              const int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (ws_bytes < route_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_replay(cfg, d, x, w_router, topk_ids, topk_w, (char*)ws, stream);
+}
+
+moe_status_t moe_balanced_ids(const moe_config_t* cfg, int64_t T, int32_t* topk_ids, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (T == 0) return MOE_OK;
+    if (!topk_ids) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_balanced_ids(topk_ids, T * cfg->top_k, cfg->num_experts, stream));
+}
+
+moe_status_t moe_layer_forward_routed(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                                      const int32_t* topk_ids, const void* w13, const float* w13_scale,
+                                      const void* w2, const float* w2_scale, const void* ws13, const void* ws2,
+                                      void* out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_layer(cfg, T, x, w_router, w13, w13_scale, w2, w2_scale, ws13, ws2, out, ws, ws_bytes));
+    if (T == 0) return MOE_OK;
+    if (!topk_ids) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    LayerWs L = layer_ws(d);
+    char* base = (char*)ws;
+    float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+    MOE_TRY(do_replay(cfg, d, x, w_router, topk_ids, w, base + L.step, stream));
+    return layer_experts(cfg, d, L, base, x, topk_ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
+                         expert_counts_out, stream);
 }
 
 const char* moe_status_string(moe_status_t status) {

@@ -17,6 +17,11 @@ hipError_t launch_router_logits(const void* x, const void* w_router, float* logi
 // per-token sigmoid + bias + top-k + weights (partial logits summed in order)
 hipError_t launch_topk(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
                        int norm, int32_t* ids, float* w, hipStream_t s);
+// weights of caller-supplied expert ids from the same partial logits
+hipError_t launch_replay_weights(const float* logits, int nsplit, const int32_t* ids, int T, int E, int k,
+                                 float scale, int norm, float* w, hipStream_t s);
+// ids[p] = p mod E for the P = T*k pairs
+hipError_t launch_balanced_ids(int32_t* ids, int64_t P, int E, hipStream_t s);
 
 // ---- permutation ----------------------------------------------------------
 size_t permute_scratch_bytes(int64_t P, int E);   // P = T * k pairs

@@ -100,6 +100,63 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (lane < k) wout[(int64_t)t * k + lane] = w * scale;
 }
 
+// Routing replay (miles page "Step-5-Preview", section 5.2 Algorithm: the
+// trainer reruns the rollout's expert choices).  The k ids of each token
+// come from the caller, clamped to [0, E-1] as the selection's own guard
+// does; only the weights are computed, from the current raw scores, with the
+// same arithmetic as topk_kernel (partial logits added in split order,
+// s = 1/(1+exp(-a)), a wave sum over the k slots), so replaying the router's
+// own choice gives back its weights bit for bit.  One wavefront per token;
+// lane j < k owns slot j.
+__global__ __launch_bounds__(256) void replay_kernel(const float* __restrict__ logits, int nsplit,
+                                                     const int32_t* __restrict__ ids_in, int T, int E, int k,
+                                                     float scale, int norm, float* __restrict__ wout) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float s = 0.f;
+    if (lane < k) {
+        const int e = min(max(ids_in[(int64_t)t * k + lane], 0), E - 1);
+        const float* lg = logits + (int64_t)t * E + e;
+        float part[8];
+        float a = 0.f;
+        for (int z0 = 0; z0 < nsplit; z0 += 8) {
+#pragma unroll
+            for (int z = 0; z < 8; ++z) part[z] = z0 + z < nsplit ? lg[(int64_t)(z0 + z) * T * E] : 0.f;
+#pragma unroll
+            for (int z = 0; z < 8; ++z)
+                if (z0 + z < nsplit) a += part[z];
+        }
+        s = 1.0f / (1.0f + expf(-a));
+    }
+    const float sum = wave_sum(lane < k ? s : 0.f);
+    const float w = norm ? s / sum : s;
+    if (lane < k) wout[(int64_t)t * k + lane] = w * scale;
+}
+
+// Static balanced routing (AutoModel page, benchmark table): pair
+// p = t*k + j goes to expert p mod E, so every expert gets floor(T*k/E) or
+// one more pair and a token's k experts are distinct (k <= E).
+__global__ __launch_bounds__(256) void balanced_ids_kernel(int32_t* __restrict__ ids, int64_t P, int E) {
+    for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < P; p += (int64_t)gridDim.x * 256)
+        ids[p] = (int32_t)(p % E);
+}
+
+hipError_t launch_replay_weights(const float* logits, int nsplit, const int32_t* ids, int T, int E, int k,
+                                 float scale, int norm, float* w, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    replay_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, ids, T, E, k, scale, norm, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_balanced_ids(int32_t* ids, int64_t P, int E, hipStream_t s) {
+    if (P <= 0) return hipSuccess;
+    const int64_t need = (P + 255) / 256;
+    const int64_t blocks = need < 2048 ? need : 2048;
+    balanced_ids_kernel<<<(unsigned)blocks, 256, 0, s>>>(ids, P, E);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
                        int norm, int32_t* ids, float* w, hipStream_t s) {
     if (T <= 0) return hipSuccess;

@@ -96,6 +96,12 @@ def test_entry_points_reject_null_pointers(lib):
     assert lib.moe_combine(c, 4, FAKE, FAKE, None, None, None, FAKE, None) == 1
     assert lib.moe_layer_forward(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, None,
                                  None, None, FAKE, 1 << 30, None) == 1   # shared weights missing
+    assert lib.moe_route_replay(c, 4, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1    # ids missing
+    assert lib.moe_balanced_ids(c, 4, None, None) == 1
+    assert lib.moe_layer_forward_routed(c, 4, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                                        None, None, FAKE, 1 << 30, None) == 1             # ids missing
+    assert lib.moe_layer_forward_routed(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE,
+                                        None, None, FAKE, 1 << 30, None) == 1             # shared weights
 
 
 def test_bf16_experts_reject_scales(lib):
@@ -118,6 +124,9 @@ def test_small_workspace_is_reported(lib):
     st, need = ws_size(cfg_of(), 64)
     assert lib.moe_layer_forward(c, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None,
                                  None, None, FAKE, need - 1, None) == 3
+    assert lib.moe_route_replay(c, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    assert lib.moe_layer_forward_routed(c, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                                        None, None, FAKE, need - 1, None) == 3
 
 
 def test_zero_tokens_is_a_noop(lib):
@@ -127,6 +136,20 @@ def test_zero_tokens_is_a_noop(lib):
     assert lib.moe_combine(c, 0, None, None, None, None, None, None, None) == 0
     assert lib.moe_layer_forward(c, 0, None, None, None, None, None, None, None, None, None, None, None,
                                  None, None, None, 0, None) == 0
+    assert lib.moe_route_replay(c, 0, None, None, None, None, None, 0, None) == 0
+    assert lib.moe_balanced_ids(c, 0, None, None) == 0
+    assert lib.moe_layer_forward_routed(c, 0, None, None, None, None, None, None, None, None, None, None,
+                                        None, None, None, 0, None) == 0
+
+
+def test_routed_entry_points_check_the_config(lib):
+    c = cfg_of()
+    c.top_k = c.num_experts + 1
+    assert lib.moe_balanced_ids(ctypes.byref(c), 4, FAKE, None) == 1
+    assert lib.moe_route_replay(ctypes.byref(c), 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    c = ctypes.byref(cfg_of())
+    assert lib.moe_layer_forward_routed(c, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                        None, None, FAKE, 1 << 30, None) == 1             # bf16 + scale
 
 
 def test_binding_refuses_cpu_tensors(lib):

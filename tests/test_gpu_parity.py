@@ -279,6 +279,122 @@ def test_deterministic():
 
 
 # ----------------------------------------------------------------------------------------
+# routing supplied by the caller: routing replay and the static balanced routing
+
+def run_routed(wl, inp, ids, ws=None):
+    E = wl.cfg.num_experts
+    w = torch.empty(ids.shape, dtype=torch.float32, device=DEV)
+    counts = torch.empty((E,), dtype=torch.int32, device=DEV)
+    out = moe.moe_layer_forward_routed(wl.cfg, inp, ids, ws=ws, topk_w=w, expert_counts=counts)
+    torch.cuda.synchronize()
+    return out, w, counts
+
+
+def check_weights(gpu_w, orc_w):
+    """Weights of a given choice: no selection involved, so every slot is
+    compared (fp32 sigmoid on the GPU vs double on the host)."""
+    gpu_w = np.asarray(gpu_w, np.float64)
+    orc_w = np.asarray(orc_w, np.float64)
+    assert np.all(np.abs(gpu_w - orc_w) <= 1e-6 + 1e-5 * np.abs(orc_w))
+
+
+REPLAY_SMALL = ["tiny", "tiny_clip_stress", "one_token", "ragged_130_tokens_20_experts", "top1",
+                "all_experts_chosen", "no_norm", "no_shared", "bf16_out", "max_experts_max_k",
+                "small_tiles_multi_tile", "shared_width_differs"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_130_tokens_20_experts", "no_norm", "max_experts_max_k",
+                                  "step5_decode"])
+def test_replay_of_own_choice_is_bit_exact(name):
+    """Replaying moe_route's own ids gives its weights and the layer output
+    of moe_layer_forward bit for bit."""
+    wl = mi.WORKLOADS[name] if name in mi.WORKLOADS else mi.workload("tiny", **SMALL[name])
+    say(f"[replay_own_choice] {name}")
+    inp = gpu_inputs(wl)
+    ws = moe.workspace(wl.cfg, wl.T)
+    out, ids, w, counts = run_layer(wl, inp, ws=ws)
+    w2 = moe.moe_route_replay(wl.cfg, inp["x"], inp["w_router"], ids, ws=ws)
+    out2, w3, counts2 = run_routed(wl, inp, ids, ws=ws)
+    assert torch.equal(w, w2) and torch.equal(w, w3)
+    assert torch.equal(counts, counts2)
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("name", REPLAY_SMALL)
+def test_layer_replay_small(name):
+    """A replayed choice that is not the router's (random distinct experts;
+    on two tokens also a duplicate and out-of-range ids, which are clamped):
+    weights and outputs on every token against the oracle's replay."""
+    wl = mi.workload("tiny", **SMALL[name])
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    say(f"[layer_replay_small] {name} T={T}")
+    inp = gpu_inputs(wl)
+    ids = mi.random_expert_ids(wl, seed=11)
+    if k >= 2:
+        ids[0, 1] = ids[0, 0]
+    if T >= 2:
+        ids[T - 1, 0] = -3
+        ids[T - 1, k - 1] = E + 7
+    out, w, counts = run_routed(wl, inp, ids.to(DEV))
+    ref = orc.layer(cfg, host(inp), ids_in=ids)
+    check_weights(w.cpu().numpy(), ref["w"])
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(ref["ids"].reshape(-1), minlength=E))
+    err, rms = max_err_over_rms(out.float().cpu().numpy(), ref["out"])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_BF16
+
+
+def test_layer_replay_fp8_small():
+    wl = fp8_workload("fp8_ragged_130_tokens_20_experts")
+    say("[layer_replay_fp8_small]")
+    inp = gpu_inputs(wl)
+    ids = mi.random_expert_ids(wl, seed=12)
+    out, w, counts = run_routed(wl, inp, ids.to(DEV))
+    ref = orc.layer(wl.cfg, host(inp), ids_in=ids)
+    check_weights(w.cpu().numpy(), ref["w"])
+    err, rms = max_err_over_rms(out.float().cpu().numpy(), ref["out"])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_FP8
+
+
+@pytest.mark.parametrize("T,k,E", [(8192, 8, 288), (64, 8, 288), (8192, 8, 352), (7, 3, 5), (1, 1, 1),
+                                   (300_000, 8, 64)])
+def test_balanced_ids_bit_exact(T, k, E):
+    wl = mi.workload("tiny", T=T, top_k=k, num_experts=E)
+    ids = moe.moe_balanced_ids(wl.cfg, T)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), orc.balanced_ids(T, k, E))
+
+
+@pytest.mark.parametrize("name", ["step5_prefill", "step5_decode"])
+def test_layer_balanced_full_size(name):
+    """The static balanced routing at full size, as the benchmark's
+    balanced line runs it: ids bit-exact, counts exact, weights on every
+    token, outputs on a seeded sample."""
+    wl = mi.WORKLOADS[name]
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    say(f"[layer_balanced_full] {name} T={T}")
+    inp = gpu_inputs(wl)
+    ids = moe.moe_balanced_ids(cfg, T)
+    out, w, counts = run_routed(wl, inp, ids)
+    o_ids = orc.balanced_ids(T, k, E)
+    assert np.array_equal(ids.cpu().numpy(), o_ids)
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(o_ids.reshape(-1), minlength=E))
+    say("  gpu done; copying inputs to host")
+    h = host(inp)
+    del inp
+    torch.cuda.empty_cache()
+    _, o_w = orc.route(cfg, h["x"], h["w_router"], None, ids_in=o_ids)
+    check_weights(w.cpu().numpy(), o_w)
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, min(N_SAMPLE, T), replace=False)]))
+    ref = orc.layer(cfg, h, tokens=sample, ids_in=o_ids)
+    err, rms = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
+    say(f"  sampled {sample.size} tokens: max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------------------
 # full-size workloads through moe_layer_forward
 
 FULL = ["step35_prefill", "step5_prefill", "step5_decode", "step5_decode_half"]
