@@ -178,6 +178,21 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0,
     return out
 
 
+RMS_NORM_EPS = 1e-5
+
+
+def block_inputs(wl: Workload, device="cpu", seed: int = 0) -> Dict[str, object]:
+    """The residual stream in front of the layer: resid [T,H] fp32, N(0,1)
+    rows each scaled by 2^U(-2, 4) (rows of very different size, as the
+    residual stream grows with depth), the stored zero-centred norm weight
+    norm_weight [H] fp32 ~ N(0, 0.1), and eps."""
+    T, H = wl.T, wl.cfg.hidden_size
+    row = torch.exp2(_uniform((T, 1), -2.0, 4.0, device, seed, "resid_row_scale"))
+    resid = (_normal((T, H), 1.0, device, seed, "resid") * row).contiguous()
+    g = _normal((H,), 0.1, device, seed, "norm_weight").contiguous()
+    return {"resid": resid, "norm_weight": g, "eps": RMS_NORM_EPS}
+
+
 def random_expert_ids(wl: Workload, device="cpu", seed: int = 0) -> torch.Tensor:
     """A seeded stand-in for a replayed expert choice: [T,k] int32, k distinct
     experts per token drawn uniformly (the first k of a random permutation)."""

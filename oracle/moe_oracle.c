@@ -360,6 +360,42 @@ int orc_permute(int64_t T, int32_t k, int32_t E, const int32_t* ids, int32_t* co
     return 0;
 }
 
+/* ---- the steps either side of the layer --------------------------------- */
+
+/* fp32 -> bf16 bit pattern, round to nearest, ties to even (NaN stays NaN) */
+uint16_t orc_bf16_round(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Zero-centred RMSNorm in front of the MoE layer (MAX page, the model
+ * overview and the weight-adaptation notes: the block's norms are
+ * zero-centred RMSNorms with weight_offset 1, i.e. the stored weight g is
+ * used as 1 + g; the AutoModel page's benchmark table keeps norms and the
+ * residual stream in FP32).  Per row of the fp32 residual r [T,H]:
+ *   x[h] = r[h] / sqrt(mean_h r^2 + eps) * (1 + g[h])
+ * with the mean in double, the result rounded to fp32 and then to bf16 (the
+ * layer's input dtype).  eps is not printed on the pages; it is an input. */
+int orc_rmsnorm(int64_t T, int32_t H, const float* r, const float* g, float eps, uint16_t* x) {
+    if (T < 0 || H < 1) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float* rt = r + t * H;
+        double ss = 0.0;
+        for (int h = 0; h < H; ++h) ss += (double)rt[h] * (double)rt[h];
+        double inv = 1.0 / sqrt(ss / (double)H + (double)eps);
+        for (int h = 0; h < H; ++h) {
+            float y = (float)((double)rt[h] * inv * (1.0 + (double)g[h]));
+            x[t * H + h] = orc_bf16_round(y);
+        }
+    }
+    return 0;
+}
+
 /* Static balanced routing (AutoModel page, benchmark table: the Step-5
  * benchmark runs with a fake, balanced, static expert routing).  The page
  * gives no rule; this oracle's reading is the round-robin that deals the T*k

@@ -49,6 +49,9 @@ def lib():
         L.orc_layer.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P, P,
                                 P, P, P, P, P, P, P]
         L.orc_balanced_ids.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
+        L.orc_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_float, P]
+        L.orc_bf16_round.argtypes = [ctypes.c_float]
+        L.orc_bf16_round.restype = ctypes.c_uint16
         L.orc_permute.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
         L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_decode.restype = ctypes.c_double
@@ -177,6 +180,39 @@ def balanced_ids(T, top_k, num_experts):
     rc = lib().orc_balanced_ids(T, top_k, num_experts, _p(ids))
     assert rc == 0, rc
     return ids
+
+
+def bf16_round(v: float) -> int:
+    """bf16 bit pattern of an fp32 value, round to nearest even."""
+    return lib().orc_bf16_round(v)
+
+
+def rmsnorm(resid, norm_weight, eps):
+    """Zero-centred RMSNorm of the fp32 residual rows: bf16 x [T,H] (as a
+    torch bfloat16 tensor, the layer's input)."""
+    import torch
+    r = _np(resid, np.float32)
+    g = _np(norm_weight, np.float32)
+    T, H = r.shape
+    assert g.shape == (H,)
+    x = np.zeros((T, H), np.uint16)
+    rc = lib().orc_rmsnorm(T, H, _p(r), _p(g), float(eps), _p(x))
+    assert rc == 0, rc
+    return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+
+
+def block(cfg, inp, tokens=None, ids_in=None):
+    """The MoE sub-block around the layer: x = rmsnorm(resid), then
+    resid_out = resid + layer(x) in fp32.  inp holds the layer's tensors
+    plus resid [T,H] fp32, norm_weight [H] fp32 and eps.  Returns the
+    layer's dict with x (bf16 [T,H]) and resid_out [n,H] added."""
+    x = rmsnorm(inp["resid"], inp["norm_weight"], inp["eps"])
+    res = layer(cfg, dict(inp, x=x), tokens=tokens, ids_in=ids_in)
+    r = _np(inp["resid"], np.float32)
+    rows = r if tokens is None else r[np.asarray(tokens, dtype=np.int64)]
+    res["x"] = x
+    res["resid_out"] = (rows + res["out"]).astype(np.float32)
+    return res
 
 
 def e4m3_decode(code: int) -> float:

@@ -402,6 +402,79 @@ def test_balanced_ids_are_balanced_and_distinct(orc, T, k, E):
 
 
 # --------------------------------------------------------------------------
+# the steps either side of the layer: zero-centred RMSNorm, fp32 residual
+
+
+def test_bf16_round_matches_torch_cast(orc):
+    """Round to nearest even against torch's own fp32 -> bfloat16 cast, on
+    exact ties (half-way between two bf16 values, both parities), values
+    just off them, subnormals, the overflow edge, infinities and random."""
+    ties = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -130 * 3, 3.0e38]
+    vals = np.array(ties + [np.nextafter(np.float32(t), np.float32(0)) for t in ties[:3]] +
+                    [np.nextafter(np.float32(t), np.float32(np.inf)) for t in ties[:3]] +
+                    [0.0, -0.0, 1e-40, -3e-39, 3.3895e38, 3.4e38, np.inf, -np.inf], np.float32)
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([vals, (rng.standard_normal(4000) * np.exp2(rng.integers(-60, 60, 4000))).astype(np.float32)])
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.bf16_round(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, want)
+    assert orc.bf16_round(float("nan")) & 0x7FFF > 0x7F80
+
+
+def test_rmsnorm_matches_torch_rms_norm(orc):
+    """torch.nn.functional.rms_norm in float64 with weight 1 + g, then
+    torch's casts to fp32 and bf16, is the same definition."""
+    wl = tiny(T=200, hidden_size=320)
+    b = mi.block_inputs(wl)
+    x = orc.rmsnorm(b["resid"], b["norm_weight"], b["eps"])
+    H = wl.cfg.hidden_size
+    ref = F.rms_norm(b["resid"].double(), (H,), weight=1.0 + b["norm_weight"].double(), eps=b["eps"])
+    ref = ref.float().bfloat16()
+    assert torch.equal(x.view(torch.int16), ref.view(torch.int16))
+
+
+def test_rmsnorm_closed_forms(orc):
+    H = 256
+    g = mi.block_inputs(tiny())["norm_weight"]
+    # a constant row c with eps = 0 normalises to sign(c) (1 + g)
+    r = torch.tensor([[3.0] * H, [-0.25] * H], dtype=torch.float32)
+    x = orc.rmsnorm(r, g, 0.0)
+    assert torch.equal(x[0], (1.0 + g).bfloat16()) and torch.equal(x[1], (-(1.0 + g)).bfloat16())
+    # scaling a row by a power of two changes nothing when eps = 0
+    r = mi.block_inputs(tiny())["resid"]
+    x0 = orc.rmsnorm(r, g, 0.0)
+    for j in (-20, -3, 5, 40):
+        assert torch.equal(orc.rmsnorm(r * 2.0 ** j, g, 0.0), x0)
+    # g = 0: every row has mean square 1 up to bf16 rounding
+    x1 = orc.rmsnorm(r, torch.zeros(H), 0.0).double()
+    assert (x1.pow(2).mean(1) - 1.0).abs().max() < 1e-2
+    # eps: a zero row stays zero; a tiny row is damped, not blown up
+    z = orc.rmsnorm(torch.zeros(1, H), g, 1e-5)
+    assert (z.float() == 0).all()
+    small = orc.rmsnorm(torch.full((1, H), 1e-4), torch.zeros(H), 1e-5).float()
+    assert torch.allclose(small, torch.full((1, H), 1e-4 / math.sqrt(1e-8 + 1e-5)), rtol=1e-2)
+
+
+def test_block_is_residual_plus_layer_of_normed_input(orc):
+    """resid_out = resid + layer(rmsnorm(resid)), the add in fp32: checked
+    against the brute-force layer on the normalised rows."""
+    wl = tiny()
+    inp = dict(_inputs(wl), **mi.block_inputs(wl))
+    toks = [0, 7, 63]
+    res = orc.block(wl.cfg, inp, tokens=toks)
+    x = res["x"]
+    f = lambda t: t.double().tolist()
+    args = (f(inp["w_router"]), f(inp["router_bias"]), f(inp["w13"]), f(inp["w2"]), f(inp["ws13"]), f(inp["ws2"]))
+    for r, t in enumerate(toks):
+        ids, _, out, c = brute.token_forward(wl.cfg, f(x[t]), *args)
+        srt = sorted(c, reverse=True)
+        assert srt[wl.cfg.top_k - 1] - srt[wl.cfg.top_k] > 1e-6
+        want = inp["resid"][t].double().numpy() + np.array(out)
+        scale = np.abs(np.array(out)).max()
+        assert np.abs(res["resid_out"][r] - want).max() <= 1e-5 * scale + 4e-7 * np.abs(want).max()
+
+
+# --------------------------------------------------------------------------
 # permutation
 
 
