@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--fp8-workload", default="step5_fp8_prefill", help="'' to skip the FP8 report")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-balanced", action="store_true", help="skip the static balanced routing report")
+    ap.add_argument("--no-block", action="store_true", help="skip the RMSNorm + residual block report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -186,6 +187,10 @@ def main():
             "mfma_frac": layer_flops(wl, rb["touched"]) / (rb["ms_step"] * 1e-3) / BF16_PEAK,
             "hbm_frac": layer_bytes(wl, rb["touched"]) / (rb["ms_step"] * 1e-3) / HBM_PEAK}
 
+    if not args.no_block:
+        note(f"{wl.name} as a block: RMSNorm in front, fp32 residual add in the combine")
+        res["block"] = time_block(args, wl, moe, torch, mi)
+
     if not args.no_decode:
         note(f"decode workload {args.decode_workload}")
         res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
@@ -295,6 +300,40 @@ def time_balanced(args, wl, moe, torch, mi):
     del inp, ws, out
     torch.cuda.empty_cache()
     return {"ms_step": ms, "touched": touched}
+
+
+def time_block(args, wl, moe, torch, mi):
+    """moe_block_forward (zero-centred RMSNorm, the layer, fp32 residual add
+    in the combine) and the RMSNorm kernel alone, each over args.steps
+    launches bracketed by HIP events on the stream."""
+    cfg, T, H = wl.cfg, wl.T, wl.cfg.hidden_size
+    inp = dict(mi.make_inputs(wl, "cuda", seed=0), **mi.block_inputs(wl, "cuda", seed=0))
+    ws = moe.workspace(cfg, T)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(args.warmup):
+        moe.moe_block_forward(cfg, inp, resid_out=out, ws=ws, stream=stream)
+        moe.moe_rmsnorm(cfg, inp["resid"], inp["norm_weight"], inp["eps"], x=x, stream=stream)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        moe.moe_block_forward(cfg, inp, resid_out=out, ws=ws, stream=stream)
+    ev[1].record(stream)
+    ev[2].record(stream)
+    for _ in range(args.steps):
+        moe.moe_rmsnorm(cfg, inp["resid"], inp["norm_weight"], inp["eps"], x=x, stream=stream)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    norm_us = ev[2].elapsed_time(ev[3]) * 1e3 / args.steps
+    norm_bytes = T * H * 4 + T * H * 2 + H * 4          # fp32 rows in, bf16 rows out, the weight
+    del inp, ws, out, x
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "rmsnorm_us": norm_us,
+            "rmsnorm_gbs": norm_bytes / (norm_us * 1e-6) / 1e9,
+            "rmsnorm_hbm_frac": norm_bytes / (norm_us * 1e-6) / HBM_PEAK}
 
 
 def bench_decode(args, wl, moe, torch):

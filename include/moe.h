@@ -166,11 +166,25 @@ moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x,
  * routed experts.  The shared term s is y_shared (fp32 [T,H], from
  * moe_shared_ffn) or shared_rows (fp16 [T,H], the shared expert's rows
  * written by moe_expert_down, i.e. y_rows + T*k*H), or absent when both
- * are NULL; passing both is MOE_ERR_INVALID_ARGUMENT.  out [T,H] in
- * out_dtype (fp32 or bf16). */
+ * are NULL; passing both is MOE_ERR_INVALID_ARGUMENT.  residual (fp32
+ * [T,H], optional): the block's fp32 residual stream (AutoModel page,
+ * benchmark table), added last, out[t] = residual[t] + (the sum above); out
+ * may then be the residual buffer itself when out_dtype is fp32 (in-place
+ * update; with bf16 output that aliasing is MOE_ERR_INVALID_ARGUMENT).
+ * out [T,H] in out_dtype (fp32 or bf16). */
 moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows,
                          const int32_t* pair_to_row, const float* topk_w,
-                         const float* y_shared, const void* shared_rows, void* out, hipStream_t stream);
+                         const float* y_shared, const void* shared_rows, const float* residual,
+                         void* out, hipStream_t stream);
+
+/* Zero-centred RMSNorm in front of the layer (MAX page: the block's norms
+ * are zero-centred RMSNorms with weight_offset 1, the stored weight g scaling
+ * by 1 + g; AutoModel page, benchmark table: norms in FP32):
+ *   x[t,h] = bf16_rne( resid[t,h] / sqrt(mean_h resid[t,:]^2 + eps) * (1 + g[h]) )
+ * computed in fp32.  resid [T,H] fp32, norm_weight g [H] fp32, x [T,H] bf16
+ * (the layer's input).  eps >= 0 and finite (the pages print no value). */
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const float* resid, const float* norm_weight,
+                         float eps, void* x, hipStream_t stream);
 
 /* The whole layer: route, permute, routed experts, shared expert, combine.
  * Inputs as above (ws13/ws2 may be NULL when share_expert_dim == 0).
@@ -181,6 +195,24 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
                                const void* w13, const float* w13_scale,
                                const void* w2, const float* w2_scale,
                                const void* ws13, const void* ws2, void* out,
+                               int32_t* topk_ids_out, float* topk_w_out,
+                               int32_t* expert_counts_out,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The MoE sub-block of a decoder layer (MAX page: each layer has a norm in
+ * front of the MLP/MoE and a residual connection around it; AutoModel page,
+ * benchmark table: FP32 norms and residual stream):
+ *   x = moe_rmsnorm(resid_in);  resid_out = resid_in + moe_layer_forward(x)
+ * with the add fused into the combine.  resid_in, resid_out [T,H] fp32;
+ * resid_out may be resid_in (in-place).  cfg->out_dtype must be MOE_FP32.
+ * Other arguments as for moe_layer_forward and moe_rmsnorm; x lives in the
+ * workspace (moe_workspace_size covers it). */
+moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* resid_in,
+                               const float* norm_weight, float eps,
+                               const void* w_router, const float* router_bias,
+                               const void* w13, const float* w13_scale,
+                               const void* w2, const float* w2_scale,
+                               const void* ws13, const void* ws2, float* resid_out,
                                int32_t* topk_ids_out, float* topk_w_out,
                                int32_t* expert_counts_out,
                                void* ws, size_t ws_bytes, hipStream_t stream);

@@ -23,7 +23,8 @@ MOE_BF16, MOE_FP32, MOE_FP8_E4M3_B128 = range(3)
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_expert_up",
             "moe_expert_down", "moe_hidden_bytes", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
-            "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_status_string")
+            "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_rmsnorm", "moe_block_forward",
+            "moe_status_string")
 
 
 class MoEError(RuntimeError):
@@ -65,7 +66,9 @@ def load(path: Optional[str] = None):
         "moe_expert_down": [C, I64, P, P, P, P, P, P, P, SZ, P],
         "moe_hidden_bytes": [C, I64, ctypes.POINTER(SZ)],
         "moe_shared_ffn": [C, I64, P, P, P, P, P, SZ, P],
-        "moe_combine": [C, I64, P, P, P, P, P, P, P],
+        "moe_combine": [C, I64, P, P, P, P, P, P, P, P],
+        "moe_rmsnorm": [C, I64, P, P, ctypes.c_float, P, P],
+        "moe_block_forward": [C, I64, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_layer_forward": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_route_replay": [C, I64, P, P, P, P, P, SZ, P],
         "moe_balanced_ids": [C, I64, P, P],
@@ -303,9 +306,11 @@ def _out_dtype(cfg):
     return torch.bfloat16 if getattr(cfg, "out_dtype", "fp32") == "bf16" else torch.float32
 
 
-def moe_combine(cfg, y_rows, pair_to_row, topk_w, y_shared=None, out=None, stream=None, shared_rows=None):
+def moe_combine(cfg, y_rows, pair_to_row, topk_w, y_shared=None, out=None, stream=None, shared_rows=None,
+                residual=None):
     """y_rows: at least T*k rows of [H] fp16 (the routed rows come first);
-    the shared term is y_shared (fp32 [T, H]) or shared_rows (fp16 [T, H])."""
+    the shared term is y_shared (fp32 [T, H]) or shared_rows (fp16 [T, H]);
+    residual (fp32 [T, H]) is added last and may also be ``out``."""
     T, H, k = topk_w.shape[0], cfg.hidden_size, cfg.top_k
     if y_rows.dim() != 2 or y_rows.shape[0] < T * k or y_rows.shape[1] != H:
         raise ValueError(f"y_rows must be [>= {T * k}, {H}] (got {tuple(y_rows.shape)})")
@@ -316,6 +321,7 @@ def moe_combine(cfg, y_rows, pair_to_row, topk_w, y_shared=None, out=None, strea
                             _ptr(topk_w, torch.float32, (T, k), "topk_w"),
                             _ptr(y_shared, torch.float32, (T, H), "y_shared"),
                             _ptr(shared_rows, torch.float16, (T, H), "shared_rows"),
+                            _ptr(residual, torch.float32, (T, H), "residual"),
                             _ptr(out, _out_dtype(cfg), (T, H), "out"), _stream(stream))
     _check(st, "moe_combine")
     return out
@@ -382,3 +388,50 @@ def moe_layer_forward_routed(cfg, inp: dict, topk_ids, out=None, ws=None, topk_w
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_layer_forward_routed")
     return out
+
+
+def moe_rmsnorm(cfg, resid, norm_weight, eps, x=None, stream=None):
+    """Zero-centred RMSNorm of the fp32 residual rows resid [T,H] with the
+    stored weight norm_weight [H] fp32 (used as 1 + g): returns x [T,H] bf16."""
+    T, H = resid.shape[0], cfg.hidden_size
+    x = x if x is not None else torch.empty((T, H), dtype=torch.bfloat16, device=resid.device)
+    c = make_config(cfg)
+    st = load().moe_rmsnorm(ctypes.byref(c), T, _ptr(resid, torch.float32, (T, H), "resid"),
+                            _ptr(norm_weight, torch.float32, (H,), "norm_weight"), float(eps),
+                            _ptr(x, torch.bfloat16, (T, H), "x"), _stream(stream))
+    _check(st, "moe_rmsnorm")
+    return x
+
+
+def moe_block_forward(cfg, inp: dict, resid_out=None, ws=None, topk_ids=None, topk_w=None, expert_counts=None,
+                      stream=None):
+    """The MoE sub-block: resid_out = resid + layer(rmsnorm(resid)).  inp
+    holds the layer's weights (as for moe_layer_forward, without x) plus
+    resid [T,H] fp32, norm_weight [H] fp32 and eps.  resid_out may be
+    inp["resid"] (in-place).  Returns resid_out."""
+    resid = inp["resid"]
+    T, H, E, k, I, Is = (resid.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size,
+                         cfg.share_expert_dim)
+    wdt = _weights_dtype(cfg)
+    fp8 = cfg.expert_dtype == "fp8"
+    resid_out = resid_out if resid_out is not None else torch.empty((T, H), dtype=torch.float32,
+                                                                    device=resid.device)
+    ws = ws if ws is not None else workspace(cfg, T, resid.device)
+    c = make_config(cfg)
+    st = load().moe_block_forward(
+        ctypes.byref(c), T, _ptr(resid, torch.float32, (T, H), "resid"),
+        _ptr(inp["norm_weight"], torch.float32, (H,), "norm_weight"), float(inp["eps"]),
+        _ptr(inp["w_router"], torch.bfloat16, (E, H), "w_router"),
+        _ptr(inp["router_bias"], torch.float32, (E,), "router_bias"),
+        _ptr(inp["w13"], wdt, (E, 2 * I, H), "w13"),
+        _ptr(inp.get("w13_scale"), torch.float32, (E, 2 * I // 128, H // 128) if fp8 else None, "w13_scale"),
+        _ptr(inp["w2"], wdt, (E, H, I), "w2"),
+        _ptr(inp.get("w2_scale"), torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
+        _ptr(inp.get("ws13") if Is else None, torch.bfloat16, (2 * Is, H), "ws13"),
+        _ptr(inp.get("ws2") if Is else None, torch.bfloat16, (H, Is), "ws2"),
+        _ptr(resid_out, torch.float32, (T, H), "resid_out"),
+        _ptr(topk_ids, torch.int32, (T, k), "topk_ids"), _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+        _ptr(expert_counts, torch.int32, (E,), "expert_counts"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "moe_block_forward")
+    return resid_out

@@ -4,6 +4,10 @@
 // mixture plus the shared expert's output):
 //   out[t, :] = sum_j w[t, j] * y_rows[pair_to_row[t*k + j], :] + y_shared[t, :]
 // fp32 accumulation, in slot order j = 0..k-1, so results are deterministic.
+// With a residual (the block's fp32 residual stream, AutoModel page benchmark
+// table) the layer output is added to it last: out = resid + (the sum above);
+// out may be the residual buffer itself (each thread reads its 8 values
+// before it writes them).
 // The shared expert's output comes as fp32 rows (y_shared) or, when it ran
 // inside the grouped expert launches, as fp16 rows (shared_rows).
 // One block of 256 threads per (token, 2048-column slice); each thread moves
@@ -19,7 +23,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ y_shared,
                                                       const _Float16* __restrict__ shared_rows,
-                                                      void* __restrict__ out, int H, int k) {
+                                                      const float* resid, void* out, int H, int k) {
     const int t = blockIdx.x;
     const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
     if (col >= H) return;
@@ -61,6 +65,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
                 for (int i = 0; i < 8; ++i) acc[i] += wj[j] * (float)v[j][i];
             }
     }
+    if (resid) {
+        const float4* rs = (const float4*)(resid + (int64_t)t * H + col);
+        const float4 a = rs[0], b = rs[1];
+        acc[0] = a.x + acc[0]; acc[1] = a.y + acc[1]; acc[2] = a.z + acc[2]; acc[3] = a.w + acc[3];
+        acc[4] = b.x + acc[4]; acc[5] = b.y + acc[5]; acc[6] = b.z + acc[6]; acc[7] = b.w + acc[7];
+    }
     if (OUT_BF16) {
         uint4 o;
         o.x = pack_bf16x2(acc[0], acc[1]);
@@ -76,16 +86,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
 }
 
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
-                          const float* y_shared, const void* shared_rows, void* out, bool out_bf16, int T, int H,
-                          int k, hipStream_t s) {
+                          const float* y_shared, const void* shared_rows, const float* resid, void* out,
+                          bool out_bf16, int T, int H, int k, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     dim3 grid(T, (H + 2047) / 2048);
     if (out_bf16)
         combine_kernel<true><<<grid, 256, 0, s>>>((const _Float16*)y_rows, pair_to_row, topk_w, y_shared,
-                                                  (const _Float16*)shared_rows, out, H, k);
+                                                  (const _Float16*)shared_rows, resid, out, H, k);
     else
         combine_kernel<false><<<grid, 256, 0, s>>>((const _Float16*)y_rows, pair_to_row, topk_w, y_shared,
-                                                   (const _Float16*)shared_rows, out, H, k);
+                                                   (const _Float16*)shared_rows, resid, out, H, k);
     return hipGetLastError();
 }
 

@@ -77,7 +77,7 @@ size_t shared_ws(const Dims& d) { return align_up((size_t)d.T * d.Is * 2); }
 
 // the whole layer: its own buffers followed by each step's scratch
 struct LayerWs {
-    size_t ids, w, counts, offsets, r2p, p2r, plan, y_rows, y_sh, step, total;
+    size_t ids, w, counts, offsets, r2p, p2r, plan, x, y_rows, y_sh, step, total;
 };
 
 LayerWs layer_ws(const Dims& d) {
@@ -92,6 +92,7 @@ LayerWs layer_ws(const Dims& d) {
     L.r2p = o;     o += align_up((size_t)d.P * 4);
     L.p2r = o;     o += align_up((size_t)d.P * 4);
     L.plan = o;    o += plan_ws(d);
+    L.x = o;       o += align_up((size_t)d.T * d.H * 2);    // the normalised input (moe_block_forward)
     L.y_rows = o;  o += align_up((size_t)rows * d.H * 2);
     L.y_sh = o;    o += (d.Is > 0 && !fuse) ? align_up((size_t)d.T * d.H * 4) : 0;
     L.step = o;
@@ -283,7 +284,7 @@ moe_status_t check_layer(const moe_config_t* cfg, int64_t T, const void* x, cons
 moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs& L, char* base, const void* x,
                            const int32_t* ids, const float* w, const void* w13, const float* w13_scale,
                            const void* w2, const float* w2_scale, const void* ws13, const void* ws2, void* out,
-                           int32_t* expert_counts_out, hipStream_t stream) {
+                           int32_t* expert_counts_out, hipStream_t stream, const float* resid = nullptr) {
     const int T = (int)d.T;
     int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)(base + L.counts);
     int32_t* offsets = (int32_t*)(base + L.offsets);
@@ -302,15 +303,15 @@ moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs
                                          tile_start, stream));
         HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, ws13), stream));
         HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, stream));
-        HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * d.H * 2, out, out_bf16, T,
-                                    d.H, d.k, stream));
+        HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * d.H * 2, resid, out,
+                                    out_bf16, T, d.H, d.k, stream));
         return MOE_OK;
     }
     HIP_TRY(moe::launch_permute(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
     float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
     MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w13_scale, w2, w2_scale, y_rows, step, stream));
     if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
-    HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, nullptr, out, out_bf16, T, d.H, d.k, stream));
+    HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, nullptr, resid, out, out_bf16, T, d.H, d.k, stream));
     return MOE_OK;
 }
 
@@ -407,14 +408,24 @@ moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x, c
 }
 
 moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows, const int32_t* pair_to_row,
-                         const float* topk_w, const float* y_shared, const void* shared_rows, void* out,
-                         hipStream_t stream) {
+                         const float* topk_w, const float* y_shared, const void* shared_rows, const float* residual,
+                         void* out, hipStream_t stream) {
     MOE_TRY(check_config(cfg, T));
     if (y_shared && shared_rows) return MOE_ERR_INVALID_ARGUMENT;
     if (T == 0) return MOE_OK;
     if (!y_rows || !pair_to_row || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
-    return hip_status(moe::launch_combine(y_rows, pair_to_row, topk_w, y_shared, shared_rows, out,
+    if (residual && cfg->out_dtype != MOE_FP32 && (const void*)residual == out) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_combine(y_rows, pair_to_row, topk_w, y_shared, shared_rows, residual, out,
                                           cfg->out_dtype == MOE_BF16, (int)T, cfg->hidden_size, cfg->top_k, stream));
+}
+
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const float* resid, const float* norm_weight, float eps,
+                         void* x, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!resid || !norm_weight || !x) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_rmsnorm(resid, norm_weight, eps, x, (int)T, cfg->hidden_size, stream));
 }
 
 moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
@@ -468,6 +479,29 @@ moe_status_t moe_layer_forward_routed(const moe_config_t* cfg, int64_t T, const 
     MOE_TRY(do_replay(cfg, d, x, w_router, topk_ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, topk_ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
                          expert_counts_out, stream);
+}
+
+moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* resid_in, const float* norm_weight,
+                               float eps, const void* w_router, const float* router_bias, const void* w13,
+                               const float* w13_scale, const void* w2, const float* w2_scale, const void* ws13,
+                               const void* ws2, float* resid_out, int32_t* topk_ids_out, float* topk_w_out,
+                               int32_t* expert_counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_layer(cfg, T, resid_in, w_router, w13, w13_scale, w2, w2_scale, ws13, ws2, resid_out, ws,
+                        ws_bytes));
+    if (cfg->out_dtype != MOE_FP32) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!norm_weight || !router_bias) return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    LayerWs L = layer_ws(d);
+    char* base = (char*)ws;
+    void* x = base + L.x;
+    HIP_TRY(moe::launch_rmsnorm(resid_in, norm_weight, eps, x, (int)T, d.H, stream));
+    int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+    float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+    MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
+    return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, resid_out,
+                         expert_counts_out, stream, resid_in);
 }
 
 const char* moe_status_string(moe_status_t status) {

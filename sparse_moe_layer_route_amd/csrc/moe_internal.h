@@ -87,8 +87,12 @@ hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows,
 
 // ---- combine --------------------------------------------------------------
 // shared expert output: y_shared fp32 [T, H], or shared_rows fp16 [T, H], or neither
+// zero-centred RMSNorm of fp32 rows -> bf16 rows (H % 4 == 0)
+hipError_t launch_rmsnorm(const float* resid, const float* norm_weight, float eps, void* x, int T, int H,
+                          hipStream_t s);
+// resid (optional, fp32 [T,H]) is added last; out may be the same buffer
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
-                          const float* y_shared, const void* shared_rows, void* out, bool out_bf16, int T, int H,
-                          int k, hipStream_t s);
+                          const float* y_shared, const void* shared_rows, const float* resid, void* out,
+                          bool out_bf16, int T, int H, int k, hipStream_t s);
 
 }  // namespace moe

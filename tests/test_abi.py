@@ -93,7 +93,7 @@ def test_entry_points_reject_null_pointers(lib):
     assert lib.moe_grouped_swiglu(c, 4, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 30,
                                   None) == 1
     assert lib.moe_shared_ffn(c, 4, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert lib.moe_combine(c, 4, FAKE, FAKE, None, None, None, FAKE, None) == 1
+    assert lib.moe_combine(c, 4, FAKE, FAKE, None, None, None, None, FAKE, None) == 1
     assert lib.moe_layer_forward(c, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, None,
                                  None, None, FAKE, 1 << 30, None) == 1   # shared weights missing
     assert lib.moe_route_replay(c, 4, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1    # ids missing
@@ -133,7 +133,7 @@ def test_zero_tokens_is_a_noop(lib):
     c = ctypes.byref(cfg_of())
     assert lib.moe_route(c, 0, None, None, None, None, None, None, 0, None) == 0
     assert lib.moe_grouped_swiglu(c, 0, None, None, None, None, None, None, None, None, None, 0, None) == 0
-    assert lib.moe_combine(c, 0, None, None, None, None, None, None, None) == 0
+    assert lib.moe_combine(c, 0, None, None, None, None, None, None, None, None) == 0
     assert lib.moe_layer_forward(c, 0, None, None, None, None, None, None, None, None, None, None, None,
                                  None, None, None, 0, None) == 0
     assert lib.moe_route_replay(c, 0, None, None, None, None, None, 0, None) == 0
@@ -196,7 +196,7 @@ def test_shared_rows_rules(lib):
     fp8 = ctypes.byref(cfg_of(expert_dtype="fp8"))
     assert lib.moe_expert_up(fp8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     # combine takes one shared term at most
-    assert lib.moe_combine(ok, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_combine(ok, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
 
 
 def test_hidden_bytes_cover_shared_rows(lib):
@@ -208,3 +208,24 @@ def test_hidden_bytes_cover_shared_rows(lib):
     c = cfg_of(share_expert_dim=0)
     assert lib.moe_hidden_bytes(ctypes.byref(c), T, ctypes.byref(n)) == 0
     assert n.value == T * c.top_k * c.moe_intermediate_size * 2
+
+
+def test_norm_and_block_argument_rules(lib):
+    c = ctypes.byref(cfg_of())
+    st, need = ws_size(cfg_of(), 64)
+    # rmsnorm: eps must be >= 0 and finite; null pointers refused; T = 0 is a no-op
+    assert lib.moe_rmsnorm(c, 4, FAKE, FAKE, -1e-5, FAKE, None) == 1
+    assert lib.moe_rmsnorm(c, 4, FAKE, FAKE, float("nan"), FAKE, None) == 1
+    assert lib.moe_rmsnorm(c, 4, FAKE, None, 1e-5, FAKE, None) == 1
+    assert lib.moe_rmsnorm(c, 0, None, None, 1e-5, None, None) == 0
+    # block: fp32 residual only, norm weight and bias required, workspace checked
+    bf = ctypes.byref(cfg_of(out_dtype="bf16"))
+    # w_router, router_bias, w13, w13_scale, w2, w2_scale, ws13, ws2, resid_out, ids, w, counts, ws
+    args = (FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE)
+    assert lib.moe_block_forward(bf, 64, FAKE, FAKE, 1e-5, *args, 1 << 30, None) == 1
+    assert lib.moe_block_forward(c, 64, FAKE, None, 1e-5, *args, 1 << 30, None) == 1
+    assert lib.moe_block_forward(c, 64, FAKE, FAKE, float("inf"), *args, 1 << 30, None) == 1
+    assert lib.moe_block_forward(c, 64, FAKE, FAKE, 1e-5, *args, need - 1, None) == 3
+    assert lib.moe_block_forward(c, 0, None, None, 1e-5, *((None,) * 13), 0, None) == 0
+    # combine: a bf16 output may not overwrite the fp32 residual it reads
+    assert lib.moe_combine(bf, 4, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 1
