@@ -126,8 +126,12 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         const int mt = p.tile_start[g + 1] - p.tile_start[g];
         const int local = w - p.tile_start[g] * p.n_tiles;
         n_tile = local / mt;
-        row0 = p.offsets[g] + (local % mt) * BM;
-        row_end = p.offsets[g + 1];
+        // rows split evenly over the group's mt tiles (each <= BM rows): the
+        // m-tiles of one weight panel stay in step and share it in L2
+        const int m_tile = local % mt;
+        const int cnt = p.offsets[g + 1] - p.offsets[g];
+        row0 = p.offsets[g] + (int)(((int64_t)m_tile * cnt) / mt);
+        row_end = p.offsets[g] + (int)(((int64_t)(m_tile + 1) * cnt) / mt);
     }
     const int valid = min(row_end - row0, BM);
     const int K = p.K, KB = K / BKB;

@@ -162,8 +162,14 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         const int local = w - p.tile_start[g] * p.n_tiles;
         n_tile = local / mt;
         m_tile = local % mt;
-        row0 = p.offsets[g] + m_tile * BM;
-        row_end = g < p.groups ? p.offsets[g + 1] : p.offsets[g] + p.extra_rows;
+        // the group's rows are split evenly over its mt tiles (each at most
+        // BM rows, as mt = ceil(rows / BM)): the m-tiles of one weight panel
+        // then do the same work and stream the panel in step, so they share
+        // it in L2 instead of each reading it from HBM
+        const int base = p.offsets[g];
+        const int cnt = (g < p.groups ? p.offsets[g + 1] : base + p.extra_rows) - base;
+        row0 = base + (int)(((int64_t)m_tile * cnt) / mt);
+        row_end = base + (int)(((int64_t)(m_tile + 1) * cnt) / mt);
     } else {
         const int mt = (p.M + BM - 1) / BM;
         n_tile = w / mt;
