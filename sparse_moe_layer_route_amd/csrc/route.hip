@@ -28,8 +28,9 @@ __device__ __forceinline__ uint32_t order_key(float c) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);      // >= 0x007fffff for numbers
 }
 
-// BATCH: splits loaded at once (1 when the logits come whole)
-template <int BATCH>
+// BATCH: splits loaded at once (1 when the logits come whole); NPL: scores
+// per lane (E <= 64 * NPL), so the lane-local scans cover only real experts
+template <int BATCH, int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit,
                                                    const float* __restrict__ bias, int T, int E, int k,
                                                    float scale, int norm, int32_t* __restrict__ ids,
@@ -39,30 +40,30 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (t >= T) return;                            // whole wave leaves together
     const float* lg = logits + (int64_t)t * E;
 
-    uint32_t key[TOPK_MAX_PER_LANE];
-    float sc[TOPK_MAX_PER_LANE];
-    float a[TOPK_MAX_PER_LANE];
+    uint32_t key[NPL];
+    float sc[NPL];
+    float a[NPL];
     // partial logits, added in split order.  They were just written by other
     // XCDs, so every read misses this XCD's L2: BATCH splits are loaded at
     // once, then added, so the latency is paid once per BATCH splits.
 #pragma unroll
-    for (int i = 0; i < TOPK_MAX_PER_LANE; ++i) a[i] = 0.f;
+    for (int i = 0; i < NPL; ++i) a[i] = 0.f;
     for (int z0 = 0; z0 < nsplit; z0 += BATCH) {
-        float part[BATCH][TOPK_MAX_PER_LANE];
+        float part[BATCH][NPL];
 #pragma unroll
         for (int z = 0; z < BATCH; ++z)
 #pragma unroll
-            for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
+            for (int i = 0; i < NPL; ++i)
                 part[z][i] = (z0 + z < nsplit && lane + 64 * i < E)
                                  ? lg[(int64_t)(z0 + z) * T * E + lane + 64 * i] : 0.f;
 #pragma unroll
         for (int z = 0; z < BATCH; ++z)
 #pragma unroll
-            for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
+            for (int i = 0; i < NPL; ++i)
                 if (z0 + z < nsplit) a[i] += part[z][i];
     }
 #pragma unroll
-    for (int i = 0; i < TOPK_MAX_PER_LANE; ++i) {
+    for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
         key[i] = 0u;
         sc[i] = 0.f;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         int bi = 0;
         float bs = 0.f;
 #pragma unroll
-        for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
+        for (int i = 0; i < NPL; ++i)
             if (key[i] > bk) { bk = key[i]; bi = i; bs = sc[i]; }
         const uint32_t wmax = wave_max_u32(bk);
         const uint32_t cand = (bk == wmax) ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         const float s_win = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(bs), owner));
         if (lane == owner) {
 #pragma unroll
-            for (int i = 0; i < TOPK_MAX_PER_LANE; ++i)
+            for (int i = 0; i < NPL; ++i)
                 if (64 * i + lane == e) key[i] = 0u;
         }
         if (lane == j) my_w = s_win;
@@ -157,13 +158,29 @@ hipError_t launch_balanced_ids(int32_t* ids, int64_t P, int E, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BATCH, int NPL>
+static void launch_topk_n(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
+                          int norm, int32_t* ids, float* w, hipStream_t s) {
+    topk_kernel<BATCH, NPL><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, bias, T, E, k, scale, norm, ids, w);
+}
+
+template <int BATCH>
+static void launch_topk_b(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
+                          int norm, int32_t* ids, float* w, hipStream_t s) {
+    if (E <= 128) launch_topk_n<BATCH, 2>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+    else if (E <= 256) launch_topk_n<BATCH, 4>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+    else if (E <= 384) launch_topk_n<BATCH, 6>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+    else if (E <= 512) launch_topk_n<BATCH, 8>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+    else launch_topk_n<BATCH, TOPK_MAX_PER_LANE>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+}
+
 hipError_t launch_topk(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
                        int norm, int32_t* ids, float* w, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     if (nsplit > 1)
-        topk_kernel<8><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, bias, T, E, k, scale, norm, ids, w);
+        launch_topk_b<8>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
     else
-        topk_kernel<1><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, bias, T, E, k, scale, norm, ids, w);
+        launch_topk_b<1>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
     return hipGetLastError();
 }
 
