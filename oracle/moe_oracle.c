@@ -408,6 +408,298 @@ int orc_balanced_ids(int64_t T, int32_t k, int32_t E, int32_t* ids) {
     return 0;
 }
 
+/* ---- backward of the layer (bf16 experts) -------------------------------
+ *
+ * The gradient of the forward above with respect to x, the router weight and
+ * every expert weight, given dL/dout (the trainer's side of the method: the
+ * AutoModel page's benchmark and the miles page's BF16 trainer run forward,
+ * backward and optimizer).  The expert choice is a discrete function of the
+ * scores and passes no gradient; the routing bias only steers that choice,
+ * so it has none.  Everything here is computed in double from the bf16
+ * inputs (the forward's fp32 roundings are not repeated), so the result is
+ * the exact gradient up to double rounding:
+ *   w_j = scale * s_j / S (S = sum of the k chosen raw scores; S -> 1 without
+ *         normalisation), s_j = sigmoid(a_j)
+ *   dy_j = w_j dout;  dw_j = dout . y_j
+ *   dh_j = W2_e^T dy_j;  (dg, du) = act'(g, u) dh_j;  dx += W13_e^T dgu_j
+ *   dW2_e += dy_j h_j^T;  dW13_e += dgu_j x^T
+ *   ds_j = scale/S (dw_j - sum_j' dw_j' s_j' / S)   (scale dw_j without norm)
+ *   da_j = ds_j s_j (1 - s_j);  dW_router[e_j] += da_j x;  dx += da_j W_router[e_j]
+ *   shared: dhs = Ws2^T dout, (dgs, dus) = act'(gs, us) dhs, dx += Ws13^T dgus,
+ *           dWs2 += dout hs^T, dWs13 += dgus x^T
+ * act'(g, u, L): with L = 0, dg = u silu'(g), du = silu(g); with L > 0 each
+ * clamp passes the gradient where its input lies in the clamp's range, ends
+ * included (the convention of torch's clamp), else none:
+ *   dg = clamp(u) silu'(g) [silu(g) <= L],  du = min(silu(g), L) [|u| <= L].
+ * silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
+ * Slots are treated one by one, so a replayed choice holding an expert twice
+ * gets the sum of both slots' terms.
+ */
+static double sigm(double a) { return 1.0 / (1.0 + exp(-a)); }
+
+void orc_act_grad(double g, double u, double L, double* dg, double* du) {
+    double sg = sigm(g);
+    double silu = g * sg, dsilu = sg * (1.0 + g * (1.0 - sg));
+    if (L == 0.0) {
+        *dg = u * dsilu;
+        *du = silu;
+        return;
+    }
+    double uc = u > L ? L : (u < -L ? -L : u);
+    double sc = silu > L ? L : silu;
+    *dg = silu <= L ? uc * dsilu : 0.0;
+    *du = (u >= -L && u <= L) ? sc : 0.0;
+}
+
+/* per token: everything the weight gradients need, and dx */
+typedef struct {
+    double *dgu, *h, *w, *da, *dgus, *hs, *dx;   /* [k,2I], [k,I], [k], [k], [2Is], [Is], [H] */
+} tok_grads;
+
+static void token_backward(const orc_cfg* c, const double* x, const uint16_t* wg, const int32_t* ids,
+                           const uint16_t* w13, const uint16_t* w2, const uint16_t* ws13, const uint16_t* ws2,
+                           const float* dout, tok_grads* o, double* buf) {
+    const int H = c->H, k = c->k, I = c->I, Is = c->Is;
+    double* s = buf;               /* k */
+    double* dw = s + k;            /* k */
+    double* gu = dw + k;           /* 2 max(I, Is) */
+    double* dh = gu + 2 * (I > Is ? I : Is);
+    double* y = dh + (I > Is ? I : Is);   /* H */
+    double S = 0.0;
+    for (int j = 0; j < k; ++j) {
+        const uint16_t* we = wg + (size_t)ids[j] * H;
+        double a = 0.0;
+        for (int h = 0; h < H; ++h) a += x[h] * (double)bf16_val(we[h]);
+        s[j] = sigm(a);
+        S += s[j];
+    }
+    if (!c->norm) S = 1.0;
+    for (int h = 0; h < H; ++h) o->dx[h] = 0.0;
+    for (int j = 0; j < k; ++j) {
+        const int e = ids[j];
+        const uint16_t* W13 = w13 + (size_t)e * 2 * I * H;
+        const uint16_t* W2 = w2 + (size_t)e * H * I;
+        double* hj = o->h + (size_t)j * I;
+        double* dgu = o->dgu + (size_t)j * 2 * I;
+        o->w[j] = (double)c->scale * s[j] / S;
+        for (int n = 0; n < 2 * I; ++n) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += (double)bf16_val(W13[(size_t)n * H + h]) * x[h];
+            gu[n] = acc;
+        }
+        for (int i = 0; i < I; ++i) hj[i] = orc_act(gu[i], gu[I + i], (double)c->limit);
+        double d = 0.0;
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int i = 0; i < I; ++i) acc += (double)bf16_val(W2[(size_t)h * I + i]) * hj[i];
+            y[h] = acc;
+            d += (double)dout[h] * acc;
+        }
+        dw[j] = d;
+        for (int i = 0; i < I; ++i) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += (double)bf16_val(W2[(size_t)h * I + i]) * (double)dout[h];
+            dh[i] = o->w[j] * acc;
+        }
+        for (int i = 0; i < I; ++i) {
+            double dg, du;
+            orc_act_grad(gu[i], gu[I + i], (double)c->limit, &dg, &du);
+            dgu[i] = dh[i] * dg;
+            dgu[I + i] = dh[i] * du;
+        }
+        for (int n = 0; n < 2 * I; ++n) {
+            if (dgu[n] == 0.0) continue;
+            const uint16_t* row = W13 + (size_t)n * H;
+            for (int h = 0; h < H; ++h) o->dx[h] += dgu[n] * (double)bf16_val(row[h]);
+        }
+    }
+    /* router */
+    double sdw = 0.0;
+    for (int j = 0; j < k; ++j) sdw += dw[j] * s[j] / S;
+    for (int j = 0; j < k; ++j) {
+        double ds = c->norm ? (double)c->scale / S * (dw[j] - sdw) : (double)c->scale * dw[j];
+        o->da[j] = ds * s[j] * (1.0 - s[j]);
+        const uint16_t* we = wg + (size_t)ids[j] * H;
+        for (int h = 0; h < H; ++h) o->dx[h] += o->da[j] * (double)bf16_val(we[h]);
+    }
+    /* shared expert */
+    if (Is > 0) {
+        for (int n = 0; n < 2 * Is; ++n) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += (double)bf16_val(ws13[(size_t)n * H + h]) * x[h];
+            gu[n] = acc;
+        }
+        for (int i = 0; i < Is; ++i) o->hs[i] = orc_act(gu[i], gu[Is + i], (double)c->limit_shared);
+        for (int i = 0; i < Is; ++i) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += (double)bf16_val(ws2[(size_t)h * Is + i]) * (double)dout[h];
+            double dg, du;
+            orc_act_grad(gu[i], gu[Is + i], (double)c->limit_shared, &dg, &du);
+            o->dgus[i] = acc * dg;
+            o->dgus[Is + i] = acc * du;
+        }
+        for (int n = 0; n < 2 * Is; ++n) {
+            if (o->dgus[n] == 0.0) continue;
+            const uint16_t* row = ws13 + (size_t)n * H;
+            for (int h = 0; h < H; ++h) o->dx[h] += o->dgus[n] * (double)bf16_val(row[h]);
+        }
+    }
+}
+
+/*
+ * Backward for selected outputs.  ids: the expert choice (ids_in if given,
+ * else the forward's own routing of x).  dout [T,H] fp32.
+ *   dx [n_tok, H] for the tokens tok_sel[0..n_tok-1];
+ *   dwg [n_exp, H], dw13 [n_exp, 2I, H], dw2 [n_exp, H, I] for the experts
+ *     exp_sel[0..n_exp-1] (any of them may be NULL);
+ *   dws13 [2Is, H], dws2 [H, Is] if want_shared (they need every token).
+ * ids_out [T,k] (optional) receives the choice used.  Sums over tokens run
+ * in ascending token order.
+ */
+int orc_backward(const orc_cfg* c, int64_t T, const uint16_t* x, const uint16_t* wg, const float* bias,
+                 const int32_t* ids_in, const uint16_t* w13, const uint16_t* w2, const uint16_t* ws13,
+                 const uint16_t* ws2, const float* dout, const int64_t* tok_sel, int64_t n_tok,
+                 const int32_t* exp_sel, int32_t n_exp, int32_t want_shared, float* dx, float* dwg,
+                 float* dw13, float* dw2, float* dws13, float* dws2, int32_t* ids_out) {
+    if (!c || c->fp8 || c->k < 1 || c->k > c->E || T < 0) return 1;
+    if (want_shared && c->Is == 0) return 1;
+    const int H = c->H, E = c->E, k = c->k, I = c->I, Is = c->Is;
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k > 0 ? T * k : 1));
+    float* wdummy = (float*)malloc(sizeof(float) * (size_t)(T * k > 0 ? T * k : 1));
+    if (orc_route(c, T, x, wg, bias, ids_in, ids, wdummy, NULL, NULL)) return 1;
+    free(wdummy);
+    if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)(T * k));
+    int32_t* esel = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    for (int e = 0; e < E; ++e) esel[e] = -1;
+    for (int i = 0; i < n_exp; ++i) esel[exp_sel[i]] = i;
+    /* tokens whose backward is needed, in ascending order */
+    int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+    for (int64_t t = 0; t < T; ++t) slot[t] = want_shared ? 1 : 0;
+    for (int64_t i = 0; i < n_tok; ++i) slot[tok_sel[i]] = 1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j)
+            if (esel[ids[t * k + j]] >= 0) slot[t] = 1;
+    int64_t n_need = 0;
+    for (int64_t t = 0; t < T; ++t) slot[t] = slot[t] ? n_need++ : -1;
+    const size_t per = (size_t)k * 2 * I + (size_t)k * I + 2 * (size_t)k + 3 * (size_t)Is + (size_t)H;
+    double* store = (double*)calloc((size_t)(n_need > 0 ? n_need : 1) * per, sizeof(double));
+    tok_grads* tg = (tok_grads*)malloc(sizeof(tok_grads) * (size_t)(n_need > 0 ? n_need : 1));
+    for (int64_t i = 0; i < n_need; ++i) {
+        double* b = store + (size_t)i * per;
+        tg[i].dgu = b; b += (size_t)k * 2 * I;
+        tg[i].h = b; b += (size_t)k * I;
+        tg[i].w = b; b += k;
+        tg[i].da = b; b += k;
+        tg[i].dgus = b; b += 2 * (size_t)Is;
+        tg[i].hs = b; b += Is;
+        tg[i].dx = b;
+    }
+    const int wide = I > Is ? I : Is;
+#pragma omp parallel
+    {
+        double* xb = (double*)malloc(sizeof(double) * (size_t)H);
+        double* buf = (double*)malloc(sizeof(double) * ((size_t)2 * k + 3 * (size_t)wide + (size_t)H));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            if (slot[t] < 0) continue;
+            for (int h = 0; h < H; ++h) xb[h] = bf16_val(x[t * H + h]);
+            token_backward(c, xb, wg, ids + t * k, w13, w2, ws13, ws2, dout + t * H, &tg[slot[t]], buf);
+        }
+        free(xb);
+        free(buf);
+    }
+    if (dx)
+        for (int64_t i = 0; i < n_tok; ++i)
+            for (int h = 0; h < H; ++h) dx[i * H + h] = (float)tg[slot[tok_sel[i]]].dx[h];
+    /* weight gradients of the selected experts: one output row per task */
+    if (n_exp > 0 && (dw13 || dw2 || dwg)) {
+#pragma omp parallel
+        {
+            double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+            double* acc2 = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t task = 0; task < (int64_t)n_exp * (2 * I + H + 1); ++task) {
+                const int q = (int)(task / (2 * I + H + 1));
+                const int r = (int)(task % (2 * I + H + 1));
+                const int e = exp_sel[q];
+                if (r < 2 * I) {                 /* dW13_e row r */
+                    if (!dw13) continue;
+                    for (int h = 0; h < H; ++h) acc[h] = 0.0;
+                    for (int64_t t = 0; t < T; ++t)
+                        for (int j = 0; j < k; ++j)
+                            if (ids[t * k + j] == e) {
+                                const double gv = tg[slot[t]].dgu[(size_t)j * 2 * I + r];
+                                if (gv == 0.0) continue;
+                                for (int h = 0; h < H; ++h) acc[h] += gv * (double)bf16_val(x[t * H + h]);
+                            }
+                    float* o = dw13 + ((size_t)q * 2 * I + r) * H;
+                    for (int h = 0; h < H; ++h) o[h] = (float)acc[h];
+                } else if (r < 2 * I + H) {      /* dW2_e row h */
+                    if (!dw2) continue;
+                    const int hh = r - 2 * I;
+                    for (int i = 0; i < I; ++i) acc2[i] = 0.0;
+                    for (int64_t t = 0; t < T; ++t)
+                        for (int j = 0; j < k; ++j)
+                            if (ids[t * k + j] == e) {
+                                const double dy = tg[slot[t]].w[j] * (double)dout[t * H + hh];
+                                const double* hv = tg[slot[t]].h + (size_t)j * I;
+                                for (int i = 0; i < I; ++i) acc2[i] += dy * hv[i];
+                            }
+                    float* o = dw2 + ((size_t)q * H + hh) * I;
+                    for (int i = 0; i < I; ++i) o[i] = (float)acc2[i];
+                } else {                         /* router row e */
+                    if (!dwg) continue;
+                    for (int h = 0; h < H; ++h) acc[h] = 0.0;
+                    for (int64_t t = 0; t < T; ++t)
+                        for (int j = 0; j < k; ++j)
+                            if (ids[t * k + j] == e) {
+                                const double d = tg[slot[t]].da[j];
+                                for (int h = 0; h < H; ++h) acc[h] += d * (double)bf16_val(x[t * H + h]);
+                            }
+                    for (int h = 0; h < H; ++h) dwg[(size_t)q * H + h] = (float)acc[h];
+                }
+            }
+            free(acc);
+            free(acc2);
+        }
+    }
+    if (want_shared) {
+#pragma omp parallel
+        {
+            double* acc = (double*)malloc(sizeof(double) * (size_t)(H > Is ? H : Is));
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t task = 0; task < 2 * (int64_t)Is + H; ++task) {
+                if (task < 2 * Is) {
+                    const int n = (int)task;
+                    for (int h = 0; h < H; ++h) acc[h] = 0.0;
+                    for (int64_t t = 0; t < T; ++t) {
+                        const double gv = tg[slot[t]].dgus[n];
+                        if (gv == 0.0) continue;
+                        for (int h = 0; h < H; ++h) acc[h] += gv * (double)bf16_val(x[t * H + h]);
+                    }
+                    for (int h = 0; h < H; ++h) dws13[(size_t)n * H + h] = (float)acc[h];
+                } else {
+                    const int hh = (int)(task - 2 * Is);
+                    for (int i = 0; i < Is; ++i) acc[i] = 0.0;
+                    for (int64_t t = 0; t < T; ++t) {
+                        const double d = (double)dout[t * H + hh];
+                        const double* hv = tg[slot[t]].hs;
+                        for (int i = 0; i < Is; ++i) acc[i] += d * hv[i];
+                    }
+                    for (int i = 0; i < Is; ++i) dws2[(size_t)hh * Is + i] = (float)acc[i];
+                }
+            }
+            free(acc);
+        }
+    }
+    free(store);
+    free(tg);
+    free(slot);
+    free(esel);
+    free(ids);
+    return 0;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -49,6 +49,10 @@ def lib():
         L.orc_layer.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P, P,
                                 P, P, P, P, P, P, P]
         L.orc_balanced_ids.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
+        L.orc_backward.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P, P, P,
+                                   ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P]
+        L.orc_act_grad.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
         L.orc_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_float, P]
         L.orc_bf16_round.argtypes = [ctypes.c_float]
         L.orc_bf16_round.restype = ctypes.c_uint16
@@ -180,6 +184,49 @@ def balanced_ids(T, top_k, num_experts):
     rc = lib().orc_balanced_ids(T, top_k, num_experts, _p(ids))
     assert rc == 0, rc
     return ids
+
+
+def act_grad(g: float, u: float, limit: float):
+    """(d act/d g, d act/d u) of the clipped SwiGLU at (g, u)."""
+    dg, du = ctypes.c_double(), ctypes.c_double()
+    lib().orc_act_grad(g, u, limit, ctypes.byref(dg), ctypes.byref(du))
+    return dg.value, du.value
+
+
+def backward(cfg, inp, dout, tokens=None, experts=None, shared=None, ids_in=None):
+    """Gradients of the layer (bf16 experts) for the loss sum(out * dout).
+
+    dout [T,H] fp32.  Returns a dict: dx [n_tok,H] for ``tokens`` (all if
+    None), dw_router [n_exp,H], dw13 [n_exp,2I,H], dw2 [n_exp,H,I] for
+    ``experts`` (all if None), dws13 [2Is,H] and dws2 [H,Is] (when ``shared``,
+    default: when there is a shared expert), and ids [T,k], the choice used."""
+    assert cfg.expert_dtype == "bf16"
+    x = _np(inp["x"], np.uint16)
+    T = x.shape[0]
+    H, E, k, I, Is = cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size, cfg.share_expert_dim
+    shared = Is > 0 if shared is None else shared
+    tok = np.arange(T, dtype=np.int64) if tokens is None else np.ascontiguousarray(np.asarray(tokens, np.int64))
+    exp = np.arange(E, dtype=np.int32) if experts is None else np.ascontiguousarray(np.asarray(experts, np.int32))
+    d = _np(dout, np.float32)
+    assert d.shape == (T, H)
+    ids_in = None if ids_in is None else _np(ids_in, np.int32)
+    out = {"dx": np.zeros((tok.size, H), np.float32), "dw_router": np.zeros((exp.size, H), np.float32),
+           "dw13": np.zeros((exp.size, 2 * I, H), np.float32), "dw2": np.zeros((exp.size, H, I), np.float32),
+           "ids": np.zeros((T, k), np.int32)}
+    if shared:
+        out["dws13"] = np.zeros((2 * Is, H), np.float32)
+        out["dws2"] = np.zeros((H, Is), np.float32)
+    c = _cfg(cfg)
+    rc = lib().orc_backward(ctypes.byref(c), T, _p(x), _p(_np(inp["w_router"], np.uint16)),
+                            _p(_np(inp["router_bias"], np.float32)), _p(ids_in),
+                            _p(_np(inp["w13"], np.uint16)), _p(_np(inp["w2"], np.uint16)),
+                            _p(_np(inp["ws13"], np.uint16) if Is else None),
+                            _p(_np(inp["ws2"], np.uint16) if Is else None), _p(d),
+                            _p(tok), tok.size, _p(exp), exp.size, int(bool(shared)),
+                            _p(out["dx"]), _p(out["dw_router"]), _p(out["dw13"]), _p(out["dw2"]),
+                            _p(out.get("dws13")), _p(out.get("dws2")), _p(out["ids"]))
+    assert rc == 0, rc
+    return out
 
 
 def bf16_round(v: float) -> int:

@@ -475,6 +475,159 @@ def test_block_is_residual_plus_layer_of_normed_input(orc):
 
 
 # --------------------------------------------------------------------------
+# backward (bf16 experts)
+
+
+def _torch_layer64(cfg, inp, ids):
+    """The layer in float64 with torch ops, the expert choice ``ids`` held
+    fixed; returns out and the leaf tensors (x, router, experts, shared)."""
+    leaf = lambda t: t.double().clone().requires_grad_(True)
+    x, wg, w13, w2 = leaf(inp["x"]), leaf(inp["w_router"]), leaf(inp["w13"]), leaf(inp["w2"])
+    Is, I, L = cfg.share_expert_dim, cfg.moe_intermediate_size, cfg.swiglu_limit
+    ws13 = leaf(inp["ws13"]) if Is else None
+    ws2 = leaf(inp["ws2"]) if Is else None
+    ids_t = torch.as_tensor(ids, dtype=torch.long)
+
+    def mlp(xr, a, b, n, lim):
+        gu = F.linear(xr, a)
+        g, u = gu[..., :n], gu[..., n:]
+        sg = F.silu(g)
+        if lim:
+            sg = torch.clamp(sg, max=lim)
+            u = torch.clamp(u, -lim, lim)
+        return F.linear(sg * u, b)
+
+    s = torch.sigmoid(F.linear(x, wg))
+    sc = torch.gather(s, 1, ids_t)
+    w = sc / sc.sum(1, keepdim=True) if cfg.norm_expert_weight else sc
+    w = w * cfg.router_scaling_factor
+    rows = []
+    for t in range(x.shape[0]):
+        acc = 0.0
+        for j in range(ids_t.shape[1]):
+            e = int(ids_t[t, j])
+            acc = acc + w[t, j] * mlp(x[t], w13[e], w2[e], I, L)
+        rows.append(acc)
+    out = torch.stack(rows)
+    if Is:
+        out = out + mlp(x, ws13, ws2, Is, cfg.swiglu_limit_shared)
+    return out, dict(x=x, w_router=wg, w13=w13, w2=w2, ws13=ws13, ws2=ws2)
+
+
+def _dout(wl, seed=3):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((wl.T, wl.cfg.hidden_size), generator=g, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("over", [dict(), dict(x_scale=40.0), dict(norm_expert_weight=False, router_scaling_factor=2.5),
+                                  dict(share_expert_dim=0), dict(swiglu_limit=0.0, swiglu_limit_shared=0.0),
+                                  dict(T=24, num_experts=6, top_k=6)])
+def test_backward_matches_torch_autograd(orc, over):
+    """torch's autograd of the same layer in float64 (library routines:
+    F.linear, F.silu, torch.clamp, torch.sigmoid), choice held fixed."""
+    wl = tiny(**over)
+    inp = _inputs(wl)
+    dout = _dout(wl)
+    res = orc.backward(wl.cfg, inp, dout)
+    out, leaves = _torch_layer64(wl.cfg, inp, res["ids"])
+    (out * dout.double()).sum().backward()
+    pairs = [("dx", "x"), ("dw_router", "w_router"), ("dw13", "w13"), ("dw2", "w2")]
+    if wl.cfg.share_expert_dim:
+        pairs += [("dws13", "ws13"), ("dws2", "ws2")]
+    for mine, name in pairs:
+        want = leaves[name].grad.numpy()
+        got = res[mine].astype(np.float64)
+        scale = np.abs(want).max()
+        assert scale > 0, name
+        assert np.abs(got - want).max() <= 1e-6 * scale, (mine, np.abs(got - want).max() / scale)
+
+
+def test_backward_matches_finite_differences(orc):
+    """Central differences of the brute-force forward (pure Python doubles,
+    none of the oracle's code) on single weights and inputs."""
+    wl = tiny(T=4, x_scale=3.0)
+    inp = _inputs(wl)
+    dout = _dout(wl)
+    res = orc.backward(wl.cfg, inp, dout)
+    f = lambda t: t.double().tolist()
+    base = {k: f(inp[k]) for k in ("x", "w_router", "router_bias", "w13", "w2", "ws13", "ws2")}
+    d = dout.double().tolist()
+
+    def loss(p):
+        tot = 0.0
+        for t in range(wl.T):
+            ids, _, out, _ = brute.token_forward(wl.cfg, p["x"][t], p["w_router"], p["router_bias"], p["w13"],
+                                                 p["w2"], p["ws13"], p["ws2"], ids=res["ids"][t].tolist())
+            tot += math.fsum(o * g for o, g in zip(out, d[t]))
+        return tot
+
+    e0 = int(res["ids"][1, 0])
+    probes = [("x", (1, 5), res["dx"][1, 5]), ("x", (2, 100), res["dx"][2, 100]),
+              ("w_router", (e0, 7), res["dw_router"][e0, 7]),
+              ("w13", (e0, 3, 11), res["dw13"][e0, 3, 11]), ("w13", (e0, 128 + 3, 11), res["dw13"][e0, 131, 11]),
+              ("w2", (e0, 9, 4), res["dw2"][e0, 9, 4]), ("ws13", (5, 6), res["dws13"][5, 6]),
+              ("ws2", (6, 5), res["dws2"][6, 5])]
+    eps = 1e-5
+    for name, idx, got in probes:
+        vals = []
+        for sgn in (1, -1):
+            p = {k: v for k, v in base.items()}
+            p[name] = json.loads(json.dumps(base[name]))
+            ref = p[name]
+            for i in idx[:-1]:
+                ref = ref[i]
+            ref[idx[-1]] += sgn * eps
+            vals.append(loss(p))
+        fd = (vals[0] - vals[1]) / (2 * eps)
+        assert abs(fd - got) <= 1e-5 * max(1.0, abs(fd)), (name, idx, fd, got)
+
+
+def test_backward_is_linear_in_dout(orc):
+    wl = tiny()
+    inp = _inputs(wl)
+    d = _dout(wl)
+    a = orc.backward(wl.cfg, inp, d)
+    b = orc.backward(wl.cfg, inp, d * 2.0)
+    z = orc.backward(wl.cfg, inp, torch.zeros_like(d))
+    for key in ("dx", "dw_router", "dw13", "dw2", "dws13", "dws2"):
+        assert np.array_equal(b[key], 2.0 * a[key]), key
+        assert not z[key].any(), key
+
+
+def test_backward_selections_and_replay(orc):
+    """Token and expert selections return the rows of the full result, and
+    replaying the router's own choice changes nothing."""
+    wl = tiny()
+    inp = _inputs(wl)
+    d = _dout(wl)
+    full = orc.backward(wl.cfg, inp, d)
+    sub = orc.backward(wl.cfg, inp, d, tokens=[3, 40], experts=[2, 9], shared=False)
+    assert np.array_equal(sub["dx"], full["dx"][[3, 40]])
+    for key in ("dw_router", "dw13", "dw2"):
+        assert np.array_equal(sub[key], full[key][[2, 9]]), key
+    rep = orc.backward(wl.cfg, inp, d, ids_in=full["ids"])
+    for key in ("dx", "dw_router", "dw13", "dw2", "dws13", "dws2"):
+        assert np.array_equal(rep[key], full[key]), key
+
+
+def test_act_grad_closed_forms_and_clamp_convention(orc):
+    # no clip: d/dg silu(g) u at g = 0 is u/2; d/du is silu(g)
+    assert orc.act_grad(0.0, 3.0, 0.0) == pytest.approx((1.5, 0.0))
+    g = 1.3
+    sg = 1 / (1 + math.exp(-g))
+    assert orc.act_grad(g, 2.0, 0.0) == pytest.approx((2.0 * sg * (1 + g * (1 - sg)), g * sg), rel=1e-14)
+    # clipped factors pass nothing; the clamp's ends pass the gradient (as torch's clamp does)
+    assert orc.act_grad(20.0, 1.0, 7.0)[0] == 0.0           # silu(20) > 7
+    assert orc.act_grad(1.0, 9.0, 7.0)[1] == 0.0            # |u| > 7
+    assert orc.act_grad(1.0, -9.0, 7.0)[1] == 0.0
+    for u in (7.0, -7.0):
+        t = torch.tensor(u, dtype=torch.float64, requires_grad=True)
+        torch.clamp(t, -7.0, 7.0).backward()
+        assert float(t.grad) == 1.0
+        assert orc.act_grad(1.0, u, 7.0)[1] == pytest.approx(1.0 / (1 + math.exp(-1.0)))
+
+
+# --------------------------------------------------------------------------
 # permutation
 
 
