@@ -66,6 +66,8 @@ typedef struct {
 
 /* ---- scalar helpers --------------------------------------------------- */
 
+uint16_t orc_bf16_round(float f);
+
 static float bf16_val(uint16_t v) {
     uint32_t u = ((uint32_t)v) << 16;
     float f;
@@ -434,6 +436,11 @@ int orc_balanced_ids(int64_t T, int32_t k, int32_t E, int32_t* ids) {
  * silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
  * Slots are treated one by one, so a replayed choice holding an expert twice
  * gets the sum of both slots' terms.
+ * round_gu: the pre-activations (g, u) are rounded to bf16 before the
+ * activation and its derivative, as a training forward that keeps them in
+ * bf16 computes; the gradient then passes through the rounding as through
+ * the identity.  The clamps' pass/stop decisions are taken on those bf16
+ * values on both sides.
  */
 static double sigm(double a) { return 1.0 / (1.0 + exp(-a)); }
 
@@ -456,9 +463,14 @@ typedef struct {
     double *dgu, *h, *w, *da, *dgus, *hs, *dx;   /* [k,2I], [k,I], [k], [k], [2Is], [Is], [H] */
 } tok_grads;
 
+static double round_bf16_d(double v) {
+    const uint16_t b = orc_bf16_round((float)v);
+    return (double)bf16_val(b);
+}
+
 static void token_backward(const orc_cfg* c, const double* x, const uint16_t* wg, const int32_t* ids,
                            const uint16_t* w13, const uint16_t* w2, const uint16_t* ws13, const uint16_t* ws2,
-                           const float* dout, tok_grads* o, double* buf) {
+                           const float* dout, tok_grads* o, double* buf, int round_gu) {
     const int H = c->H, k = c->k, I = c->I, Is = c->Is;
     double* s = buf;               /* k */
     double* dw = s + k;            /* k */
@@ -485,7 +497,7 @@ static void token_backward(const orc_cfg* c, const double* x, const uint16_t* wg
         for (int n = 0; n < 2 * I; ++n) {
             double acc = 0.0;
             for (int h = 0; h < H; ++h) acc += (double)bf16_val(W13[(size_t)n * H + h]) * x[h];
-            gu[n] = acc;
+            gu[n] = round_gu ? round_bf16_d(acc) : acc;
         }
         for (int i = 0; i < I; ++i) hj[i] = orc_act(gu[i], gu[I + i], (double)c->limit);
         double d = 0.0;
@@ -527,7 +539,7 @@ static void token_backward(const orc_cfg* c, const double* x, const uint16_t* wg
         for (int n = 0; n < 2 * Is; ++n) {
             double acc = 0.0;
             for (int h = 0; h < H; ++h) acc += (double)bf16_val(ws13[(size_t)n * H + h]) * x[h];
-            gu[n] = acc;
+            gu[n] = round_gu ? round_bf16_d(acc) : acc;
         }
         for (int i = 0; i < Is; ++i) o->hs[i] = orc_act(gu[i], gu[Is + i], (double)c->limit_shared);
         for (int i = 0; i < Is; ++i) {
@@ -559,8 +571,8 @@ static void token_backward(const orc_cfg* c, const double* x, const uint16_t* wg
 int orc_backward(const orc_cfg* c, int64_t T, const uint16_t* x, const uint16_t* wg, const float* bias,
                  const int32_t* ids_in, const uint16_t* w13, const uint16_t* w2, const uint16_t* ws13,
                  const uint16_t* ws2, const float* dout, const int64_t* tok_sel, int64_t n_tok,
-                 const int32_t* exp_sel, int32_t n_exp, int32_t want_shared, float* dx, float* dwg,
-                 float* dw13, float* dw2, float* dws13, float* dws2, int32_t* ids_out) {
+                 const int32_t* exp_sel, int32_t n_exp, int32_t want_shared, int32_t round_gu, float* dx,
+                 float* dwg, float* dw13, float* dw2, float* dws13, float* dws2, int32_t* ids_out) {
     if (!c || c->fp8 || c->k < 1 || c->k > c->E || T < 0) return 1;
     if (want_shared && c->Is == 0) return 1;
     const int H = c->H, E = c->E, k = c->k, I = c->I, Is = c->Is;
@@ -603,7 +615,7 @@ int orc_backward(const orc_cfg* c, int64_t T, const uint16_t* x, const uint16_t*
         for (int64_t t = 0; t < T; ++t) {
             if (slot[t] < 0) continue;
             for (int h = 0; h < H; ++h) xb[h] = bf16_val(x[t * H + h]);
-            token_backward(c, xb, wg, ids + t * k, w13, w2, ws13, ws2, dout + t * H, &tg[slot[t]], buf);
+            token_backward(c, xb, wg, ids + t * k, w13, w2, ws13, ws2, dout + t * H, &tg[slot[t]], buf, round_gu);
         }
         free(xb);
         free(buf);

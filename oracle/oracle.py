@@ -50,7 +50,8 @@ def lib():
                                 P, P, P, P, P, P, P]
         L.orc_balanced_ids.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
         L.orc_backward.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P, P, P,
-                                   ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P]
+                                   ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   P, P, P, P, P, P, P]
         L.orc_act_grad.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
         L.orc_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_float, P]
@@ -193,13 +194,15 @@ def act_grad(g: float, u: float, limit: float):
     return dg.value, du.value
 
 
-def backward(cfg, inp, dout, tokens=None, experts=None, shared=None, ids_in=None):
+def backward(cfg, inp, dout, tokens=None, experts=None, shared=None, ids_in=None, round_gu=False):
     """Gradients of the layer (bf16 experts) for the loss sum(out * dout).
 
     dout [T,H] fp32.  Returns a dict: dx [n_tok,H] for ``tokens`` (all if
     None), dw_router [n_exp,H], dw13 [n_exp,2I,H], dw2 [n_exp,H,I] for
     ``experts`` (all if None), dws13 [2Is,H] and dws2 [H,Is] (when ``shared``,
-    default: when there is a shared expert), and ids [T,k], the choice used."""
+    default: when there is a shared expert), and ids [T,k], the choice used.
+    round_gu: the pre-activations are rounded to bf16 before the activation
+    and its derivative (a training forward that keeps them in bf16)."""
     assert cfg.expert_dtype == "bf16"
     x = _np(inp["x"], np.uint16)
     T = x.shape[0]
@@ -222,7 +225,7 @@ def backward(cfg, inp, dout, tokens=None, experts=None, shared=None, ids_in=None
                             _p(_np(inp["w13"], np.uint16)), _p(_np(inp["w2"], np.uint16)),
                             _p(_np(inp["ws13"], np.uint16) if Is else None),
                             _p(_np(inp["ws2"], np.uint16) if Is else None), _p(d),
-                            _p(tok), tok.size, _p(exp), exp.size, int(bool(shared)),
+                            _p(tok), tok.size, _p(exp), exp.size, int(bool(shared)), int(bool(round_gu)),
                             _p(out["dx"]), _p(out["dw_router"]), _p(out["dw13"]), _p(out["dw2"]),
                             _p(out.get("dws13")), _p(out.get("dws2")), _p(out["ids"]))
     assert rc == 0, rc

@@ -478,9 +478,11 @@ def test_block_is_residual_plus_layer_of_normed_input(orc):
 # backward (bf16 experts)
 
 
-def _torch_layer64(cfg, inp, ids):
+def _torch_layer64(cfg, inp, ids, round_gu=False):
     """The layer in float64 with torch ops, the expert choice ``ids`` held
-    fixed; returns out and the leaf tensors (x, router, experts, shared)."""
+    fixed; returns out and the leaf tensors (x, router, experts, shared).
+    round_gu: the pre-activations take their bf16-rounded values (torch's
+    cast) with the gradient passed straight through the rounding."""
     leaf = lambda t: t.double().clone().requires_grad_(True)
     x, wg, w13, w2 = leaf(inp["x"]), leaf(inp["w_router"]), leaf(inp["w13"]), leaf(inp["w2"])
     Is, I, L = cfg.share_expert_dim, cfg.moe_intermediate_size, cfg.swiglu_limit
@@ -490,6 +492,8 @@ def _torch_layer64(cfg, inp, ids):
 
     def mlp(xr, a, b, n, lim):
         gu = F.linear(xr, a)
+        if round_gu:
+            gu = gu + (gu.float().bfloat16().double() - gu).detach()
         g, u = gu[..., :n], gu[..., n:]
         sg = F.silu(g)
         if lim:
@@ -540,6 +544,23 @@ def test_backward_matches_torch_autograd(orc, over):
         scale = np.abs(want).max()
         assert scale > 0, name
         assert np.abs(got - want).max() <= 1e-6 * scale, (mine, np.abs(got - want).max() / scale)
+
+
+@pytest.mark.parametrize("x_scale", [1.0, 40.0])
+def test_backward_with_bf16_preactivations_matches_autograd(orc, x_scale):
+    wl = tiny(x_scale=x_scale)
+    inp = _inputs(wl)
+    dout = _dout(wl)
+    res = orc.backward(wl.cfg, inp, dout, round_gu=True)
+    plain = orc.backward(wl.cfg, inp, dout)
+    out, leaves = _torch_layer64(wl.cfg, inp, res["ids"], round_gu=True)
+    (out * dout.double()).sum().backward()
+    for mine, name in [("dx", "x"), ("dw_router", "w_router"), ("dw13", "w13"), ("dw2", "w2"), ("dws13", "ws13"),
+                       ("dws2", "ws2")]:
+        want = leaves[name].grad.numpy()
+        got = res[mine].astype(np.float64)
+        assert np.abs(got - want).max() <= 1e-6 * np.abs(want).max(), mine
+    assert not np.array_equal(res["dw13"], plain["dw13"])      # the rounding is really applied
 
 
 def test_backward_matches_finite_differences(orc):
