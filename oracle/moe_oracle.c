@@ -254,9 +254,11 @@ static float wval(const void* W, const float* Ws, int K, int n, int kk, int fp8)
     return (float)orc_e4m3_decode(q) * s;
 }
 
-/* y[H] = W2 act(W13 xin, L), xin fp32 [H]; W13 [2N,H], W2 [H,N] */
+/* y[H] = W2 act(W13 xin, L), xin fp32 [H]; W13 [2N,H], W2 [H,N].
+ * round_gu: g and u are rounded to bf16 before the activation (a training
+ * forward that keeps them in bf16 for its backward). */
 static void mlp(const orc_cfg* c, int N, const float* xin, const void* W13, const float* S13,
-                const void* W2, const float* S2, float L, int fp8, float* hbuf, float* y) {
+                const void* W2, const float* S2, float L, int fp8, float* hbuf, float* y, int round_gu) {
     const int H = c->H;
     for (int i = 0; i < N; ++i) {
         double g = 0.0, u = 0.0;
@@ -265,6 +267,10 @@ static void mlp(const orc_cfg* c, int N, const float* xin, const void* W13, cons
             u += (double)wval(W13, S13, H, N + i, h, fp8) * (double)xin[h];
         }
         float gf = (float)g, uf = (float)u;
+        if (round_gu) {
+            gf = bf16_val(orc_bf16_round(gf));
+            uf = bf16_val(orc_bf16_round(uf));
+        }
         hbuf[i] = (float)orc_act((double)gf, (double)uf, (double)L);
     }
     if (fp8) quant_row_fp8(hbuf, N);
@@ -287,7 +293,7 @@ static void mlp(const orc_cfg* c, int N, const float* xin, const void* W13, cons
 int orc_layer(const orc_cfg* c, int64_t n, const int64_t* tok, const uint16_t* x,
               const uint16_t* wg, const float* bias, const int32_t* ids_in, const void* w13, const float* w13s,
               const void* w2, const float* w2s, const uint16_t* ws13, const uint16_t* ws2,
-              float* out, int32_t* ids, float* w, float* y_routed, float* y_shared) {
+              float* out, int32_t* ids, float* w, float* y_routed, float* y_shared, int32_t round_gu) {
     if (!c || c->k < 1 || c->k > c->E) return 1;
     const int H = c->H, E = c->E, k = c->k, I = c->I, Is = c->Is;
     const size_t esz = c->fp8 ? 1 : 2;
@@ -319,12 +325,12 @@ int orc_layer(const orc_cfg* c, int64_t n, const int64_t* tok, const uint16_t* x
                 const char* W2e = (const char*)w2 + (size_t)e * H * I * esz;
                 const float* S13 = c->fp8 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : NULL;
                 const float* S2 = c->fp8 ? w2s + (size_t)e * (H / 128) * (I / 128) : NULL;
-                mlp(c, I, xq, W13e, S13, W2e, S2, c->limit, c->fp8, hbuf, y);
+                mlp(c, I, xq, W13e, S13, W2e, S2, c->limit, c->fp8, hbuf, y, round_gu);
                 if (y_routed) memcpy(y_routed + (r * k + j) * H, y, sizeof(float) * (size_t)H);
                 for (int h = 0; h < H; ++h) acc[h] += (double)wt[j] * (double)y[h];
             }
             if (Is > 0) {
-                mlp(c, Is, xin, ws13, NULL, ws2, NULL, c->limit_shared, 0, hbuf, y);
+                mlp(c, Is, xin, ws13, NULL, ws2, NULL, c->limit_shared, 0, hbuf, y, round_gu);
                 if (y_shared) memcpy(y_shared + r * H, y, sizeof(float) * (size_t)H);
                 for (int h = 0; h < H; ++h) acc[h] += (double)y[h];
             } else if (y_shared) {

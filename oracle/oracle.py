@@ -47,7 +47,7 @@ def lib():
         P = ctypes.c_void_p
         L.orc_route.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P]
         L.orc_layer.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P, P,
-                                P, P, P, P, P, P, P]
+                                P, P, P, P, P, P, P, ctypes.c_int32]
         L.orc_balanced_ids.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
         L.orc_backward.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -127,13 +127,14 @@ def route(cfg, x, w_router, router_bias, want_scores=False, ids_in=None):
     return ids, w
 
 
-def layer(cfg, inp, tokens=None, want_parts=False, ids_in=None):
+def layer(cfg, inp, tokens=None, want_parts=False, ids_in=None, round_gu=False):
     """Layer output for the given token rows (all rows if tokens is None).
 
     inp holds the tensors of ``moe_inputs.make_inputs``.  Returns a dict with
     out [n,H] fp32, ids [n,k], w [n,k] and, if want_parts, y_routed [n,k,H]
     and y_shared [n,H].  ids_in [T,k] (rows indexed like x) replays the given
-    expert choices instead of selecting them."""
+    expert choices instead of selecting them.  round_gu: the pre-activations
+    are rounded to bf16 before the activation (the training forward)."""
     x = _np(inp["x"], np.uint16)
     T = x.shape[0]
     tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
@@ -158,7 +159,8 @@ def layer(cfg, inp, tokens=None, want_parts=False, ids_in=None):
     if ids_in is not None:
         assert ids_in.shape == (T, k), ids_in.shape
     rc = lib().orc_layer(ctypes.byref(c), n, _p(tok), _p(x), _p(wg), _p(b), _p(ids_in), _p(w13), _p(w13s),
-                         _p(w2), _p(w2s), _p(ws13), _p(ws2), _p(out), _p(ids), _p(w), _p(yr), _p(ys))
+                         _p(w2), _p(w2s), _p(ws13), _p(ws2), _p(out), _p(ids), _p(w), _p(yr), _p(ys),
+                         int(bool(round_gu)))
     assert rc == 0, rc
     res = {"out": out, "ids": ids, "w": w}
     if want_parts:

@@ -561,6 +561,9 @@ def test_backward_with_bf16_preactivations_matches_autograd(orc, x_scale):
         got = res[mine].astype(np.float64)
         assert np.abs(got - want).max() <= 1e-6 * np.abs(want).max(), mine
     assert not np.array_equal(res["dw13"], plain["dw13"])      # the rounding is really applied
+    fwd = orc.layer(wl.cfg, inp, ids_in=res["ids"], round_gu=True)["out"]
+    want = out.detach().numpy()
+    assert np.abs(fwd - want).max() <= 1e-6 * np.abs(want).max()
 
 
 def test_backward_matches_finite_differences(orc):
