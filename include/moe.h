@@ -256,6 +256,53 @@ moe_status_t moe_layer_forward_routed(const moe_config_t* cfg, int64_t T, const 
                                       float* topk_w_out, int32_t* expert_counts_out,
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- training: forward that keeps its state, and the backward ----------
+ *
+ * The trainer's side of the method (AutoModel page, benchmark table: BF16
+ * forward, backward and optimizer over the whole backbone; miles page: a BF16
+ * trainer that replays the rollout's expert choices).  bf16 experts only, and
+ * the shared expert, if any, must have the routed experts' width (Is == I,
+ * as in both models); other configurations return MOE_ERR_UNSUPPORTED. */
+
+/* Bytes of the state moe_layer_forward_train keeps for T tokens, and of the
+ * scratch moe_layer_backward needs.  Pure host functions. */
+moe_status_t moe_saved_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes);
+moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes);
+
+/* moe_layer_forward for training: the same layer, and in `saved` (caller-
+ * owned device memory of moe_saved_bytes, to be passed unchanged to
+ * moe_layer_backward) the expert choice, the weights, the chosen raw scores,
+ * the permutation, the first projection's pre-activations (bf16), h (bf16)
+ * and the expert output rows (fp16).  The activation is applied to the
+ * bf16-rounded pre-activations it keeps, so the backward differentiates the
+ * function that ran.  topk_ids_in [T,k] int32 (optional): a replayed choice
+ * (see moe_route_replay; router_bias may then be NULL).  ws: moe_workspace_size. */
+moe_status_t moe_layer_forward_train(const moe_config_t* cfg, int64_t T, const void* x,
+                                     const void* w_router, const float* router_bias,
+                                     const int32_t* topk_ids_in,
+                                     const void* w13, const void* w2,
+                                     const void* ws13, const void* ws2, void* out,
+                                     void* saved, size_t saved_bytes,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gradients of the loss sum(out * dout) through the layer that
+ * moe_layer_forward_train ran on the same x and weights:
+ *   dout [T,H] fp32 in;  dx [T,H], dw_router [E,H], dw13 [E,2I,H],
+ *   dw2 [E,H,I], dws13 [2Is,H], dws2 [H,Is] fp32 out (overwritten; experts
+ *   without tokens get zeros; dws13/dws2 may be NULL without a shared expert).
+ * The expert choice passes no gradient and the routing bias gets none.  Each
+ * clamp of the clipped SwiGLU passes the gradient where its input lies in its
+ * range, ends included.  Products run on bf16 operands (dout times the
+ * weights rounded to bf16, the saved activations) with fp32 accumulation.
+ * ws: moe_backward_workspace_size bytes. */
+moe_status_t moe_layer_backward(const moe_config_t* cfg, int64_t T, const void* x,
+                                const void* w_router, const void* w13, const void* w2,
+                                const void* ws13, const void* ws2,
+                                const void* saved, size_t saved_bytes, const float* dout,
+                                float* dx, float* dw_router, float* dw13, float* dw2,
+                                float* dws13, float* dws2,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status_t status);
 

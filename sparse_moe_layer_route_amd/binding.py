@@ -24,6 +24,7 @@ MOE_BF16, MOE_FP32, MOE_FP8_E4M3_B128 = range(3)
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_expert_up",
             "moe_expert_down", "moe_hidden_bytes", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
             "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_rmsnorm", "moe_block_forward",
+            "moe_saved_bytes", "moe_backward_workspace_size", "moe_layer_forward_train", "moe_layer_backward",
             "moe_status_string")
 
 
@@ -68,6 +69,10 @@ def load(path: Optional[str] = None):
         "moe_shared_ffn": [C, I64, P, P, P, P, P, SZ, P],
         "moe_combine": [C, I64, P, P, P, P, P, P, P, P],
         "moe_rmsnorm": [C, I64, P, P, ctypes.c_float, P, P],
+        "moe_saved_bytes": [C, I64, ctypes.POINTER(SZ)],
+        "moe_backward_workspace_size": [C, I64, ctypes.POINTER(SZ)],
+        "moe_layer_forward_train": [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P, SZ, P],
+        "moe_layer_backward": [C, I64, P, P, P, P, P, P, P, SZ, P, P, P, P, P, P, P, P, SZ, P],
         "moe_block_forward": [C, I64, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_layer_forward": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_route_replay": [C, I64, P, P, P, P, P, SZ, P],
@@ -435,3 +440,79 @@ def moe_block_forward(cfg, inp: dict, resid_out=None, ws=None, topk_ids=None, to
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_block_forward")
     return resid_out
+
+
+def _size(fn, cfg, T):
+    n = ctypes.c_size_t(0)
+    c = make_config(cfg)
+    _check(getattr(load(), fn)(ctypes.byref(c), T, ctypes.byref(n)), fn)
+    return n.value
+
+
+def moe_saved_bytes(cfg, T: int) -> int:
+    return _size("moe_saved_bytes", cfg, T)
+
+
+def moe_backward_workspace_size(cfg, T: int) -> int:
+    return _size("moe_backward_workspace_size", cfg, T)
+
+
+def moe_layer_forward_train(cfg, inp: dict, out=None, saved=None, ws=None, topk_ids=None, stream=None):
+    """The layer's forward for training (bf16 experts): also keeps what
+    moe_layer_backward needs in ``saved`` (uint8, moe_saved_bytes).  With
+    topk_ids [T,k] int32 the expert choice is replayed.  Returns (out, saved)."""
+    x = inp["x"]
+    T, H, E, k, I, Is = (x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size,
+                         cfg.share_expert_dim)
+    out = out if out is not None else torch.empty((T, H), dtype=_out_dtype(cfg), device=x.device)
+    saved = saved if saved is not None else torch.empty(moe_saved_bytes(cfg, T), dtype=torch.uint8,
+                                                       device=x.device)
+    ws = ws if ws is not None else workspace(cfg, T, x.device)
+    c = make_config(cfg)
+    st = load().moe_layer_forward_train(
+        ctypes.byref(c), T, _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(inp["w_router"], torch.bfloat16, (E, H), "w_router"),
+        _ptr(inp["router_bias"], torch.float32, (E,), "router_bias"),
+        _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+        _ptr(inp["w13"], torch.bfloat16, (E, 2 * I, H), "w13"), _ptr(inp["w2"], torch.bfloat16, (E, H, I), "w2"),
+        _ptr(inp.get("ws13") if Is else None, torch.bfloat16, (2 * Is, H), "ws13"),
+        _ptr(inp.get("ws2") if Is else None, torch.bfloat16, (H, Is), "ws2"),
+        _ptr(out, _out_dtype(cfg), (T, H), "out"), _ptr(saved, torch.uint8, None, "saved"), saved.numel(),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "moe_layer_forward_train")
+    return out, saved
+
+
+def moe_layer_backward(cfg, inp: dict, saved, dout, grads=None, ws=None, stream=None):
+    """Gradients for the loss sum(out * dout) (dout [T,H] fp32) from the
+    state ``saved`` by moe_layer_forward_train on the same inputs.  Returns a
+    dict of fp32 tensors: dx [T,H], dw_router [E,H], dw13 [E,2I,H],
+    dw2 [E,H,I] and, with a shared expert, dws13 [2Is,H], dws2 [H,Is]."""
+    x = inp["x"]
+    T, H, E, k, I, Is = (x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size,
+                         cfg.share_expert_dim)
+    dev = x.device
+    f32 = torch.float32
+    if grads is None:
+        grads = {"dx": torch.empty((T, H), dtype=f32, device=dev),
+                 "dw_router": torch.empty((E, H), dtype=f32, device=dev),
+                 "dw13": torch.empty((E, 2 * I, H), dtype=f32, device=dev),
+                 "dw2": torch.empty((E, H, I), dtype=f32, device=dev)}
+        if Is:
+            grads["dws13"] = torch.empty((2 * Is, H), dtype=f32, device=dev)
+            grads["dws2"] = torch.empty((H, Is), dtype=f32, device=dev)
+    ws = ws if ws is not None else torch.empty(moe_backward_workspace_size(cfg, T), dtype=torch.uint8, device=dev)
+    c = make_config(cfg)
+    st = load().moe_layer_backward(
+        ctypes.byref(c), T, _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(inp["w_router"], torch.bfloat16, (E, H), "w_router"),
+        _ptr(inp["w13"], torch.bfloat16, (E, 2 * I, H), "w13"), _ptr(inp["w2"], torch.bfloat16, (E, H, I), "w2"),
+        _ptr(inp.get("ws13") if Is else None, torch.bfloat16, (2 * Is, H), "ws13"),
+        _ptr(inp.get("ws2") if Is else None, torch.bfloat16, (H, Is), "ws2"),
+        _ptr(saved, torch.uint8, None, "saved"), saved.numel(), _ptr(dout, torch.float32, (T, H), "dout"),
+        _ptr(grads["dx"], f32, (T, H), "dx"), _ptr(grads["dw_router"], f32, (E, H), "dw_router"),
+        _ptr(grads["dw13"], f32, (E, 2 * I, H), "dw13"), _ptr(grads["dw2"], f32, (E, H, I), "dw2"),
+        _ptr(grads.get("dws13"), f32, (2 * Is, H), "dws13"), _ptr(grads.get("dws2"), f32, (H, Is), "dws2"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "moe_layer_backward")
+    return grads

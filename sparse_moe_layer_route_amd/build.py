@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
 SOURCES = ["moe_api.cpp", "router.hip", "route.hip", "permute.hip", "tile_plan.hip", "grouped_gemm.hip", "fp8_gemm.hip",
-           "combine.hip", "norm.hip"]
+           "combine.hip", "norm.hip", "bwd_gemm.hip", "bwd.hip"]
 
 # Packed fp32 VALU ops are disabled for the device code (hipcc-only flag).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,0 +1,403 @@
+// bwd_gemm.hip -- the grouped GEMMs of the layer's backward on gfx950.
+//
+//   C[m, n] = sum_k A(m, k) * B(k, n)
+//
+// The backward's products read operands that the forward reads the other way
+// round: the expert weights W2 [H][I] and W13 [2I][H] are contracted over
+// their row index (data gradients), and the saved activations are
+// contracted over the token rows (weight gradients).  Both land in LDS
+// K-major -- rows of k, the m or n index contiguous -- and reach the MFMA
+// through ds_read_b64_tr_b16, gfx950's transposing LDS read: in each group of
+// 16 lanes, lane i receives element i & 3 of the 8 bytes that lane
+// 4j + (i >> 2) addressed, for j = 0..3.  Lane s reading row k0 + (s >> 2),
+// columns c0 + 4 (s & 3) .. +3 therefore hands lane i the 4 values
+// B[k0 .. k0+3][c0 + i], half of a 16x16x32 MFMA fragment.
+//
+// Instances:
+//   * DGRAD (groups partition the rows M, like the forward): A is K-
+//     contiguous rows (the output gradient rows dy, or dgu), B is the group's
+//     weight [K][N].  Epilogues: ACT -- the clipped SwiGLU's backward with
+//     the saved pre-activations gu, giving dgu (bf16 [rows][2N]); F32 --
+//     plain fp32 rows.
+//   * WGRAD (groups partition the contraction K = the group's rows): A and
+//     B are K-major row sets (dy or dgu, and h or the gathered x rows); every
+//     group, empty ones included, writes its full fp32 [M][N] gradient.
+//
+// Block tile 256 x 256, K slices of 32, 8 waves as 4 along M x 2 along N
+// (64 x 128 each), 16x16x32 bf16 MFMA, direct global -> LDS DMA (inline asm,
+// explicit vmcnt waits), 4 LDS stages, fragments of slice k+1 read while
+// slice k multiplies -- the forward kernel's scheme.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace bg {
+
+constexpr int BK = 32;
+constexpr int NW = 8;
+constexpr int NT = NW * 64;
+constexpr int BM = 256, BN = 256;
+constexpr int WM = 4, WN = 2;           // waves along M, N
+constexpr int TM = 4, TN = 8;           // 16-row / 16-col tiles per wave
+constexpr int NXCD = 8;
+// K-contiguous operand (16 rows x 64 B per DMA block), as in the forward
+// kernel: the 4 blocks of a 64-row group at bank groups 0, 2, 16, 18
+__device__ constexpr int BLK_OFF[4] = {0, 1024 + 32, 2048 + 256, 3072 + 288};
+constexpr int GROUP = 3072 + 288 + 1024;
+constexpr int KC_BYTES = 4 * GROUP;     // 256 rows x one K slice
+// K-major operand: 4 slabs of 64 columns x 4 blocks of 8 k-rows (1 KiB,
+// 128 B per row); odd blocks have their 16-byte chunks swapped in pairs of
+// pairs (chunk q at q ^ 2) so that a 32-lane pass of a transposing read,
+// which touches rows of two neighbouring blocks, hits distinct banks
+constexpr int KM_BYTES = 16 * 1024;
+constexpr int STAGES = 4;
+
+enum { ACT = 0, F32 = 1 };
+
+struct Params {
+    const uint16_t* A;          // DGRAD: [rows][K] K-contiguous; WGRAD: [rows][M] K-major
+    int64_t lda;
+    const uint16_t* B;          // DGRAD: weights [groups][K][N]; WGRAD: [rows][N] K-major
+    int64_t ldb;
+    int64_t b_group_stride;
+    const uint16_t* B_extra;    // DGRAD: the extra group's weight [K][N]
+    const int32_t* b_rows;      // WGRAD: B row of activation row r is b_rows[r] / b_div (r < rows of
+    int b_div;                  //   the groups), r - offsets[groups] (extra rows); nullptr: row r
+    const uint16_t* zero_row;   // WGRAD: >= max(M, N) zero values, read for k rows past a group's end
+    void* C;
+    int64_t ldc;
+    int64_t c_group_stride;     // WGRAD: per-group output stride
+    void* C_extra;              // WGRAD: the extra group's output
+    const uint16_t* gu;         // ACT: saved pre-activations [rows][2N], gate then up
+    float limit, limit_extra;
+    int M, N, K;                // DGRAD: N, K (M from the groups); WGRAD: M, N (K from the groups)
+    const int32_t* offsets;     // [groups+1]
+    const int32_t* tile_start;  // DGRAD: 256-row tile plan [groups+2]
+    int groups;
+    int extra_rows;             // rows of the extra group after offsets[groups] (0: none)
+    int m_tiles, n_tiles;
+};
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma_frag(const void* g, unsigned lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g) : "memory");
+}
+
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// LDS byte offset, inside a K-major operand, of the 8 bytes that lane s (of
+// its 16-lane group g) reads for the 16-column tile starting at column c0,
+// k rows 8g + 4 half + (s >> 2)
+__device__ __forceinline__ unsigned km_off(int c0, int g, int half, int s) {
+    const int c = (c0 & 63) + 4 * (s & 3);
+    const int q = (c >> 3) ^ ((g & 1) << 1);
+    return (unsigned)((c0 >> 6) * 4096 + g * 1024 + (4 * half + (s >> 2)) * 128 + q * 16 + (c & 4) * 2);
+}
+
+// a 16x16x32 fragment from a K-major operand: two transposing reads
+__device__ __forceinline__ bf16x8 km_frag(const unsigned char* base, int c0, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
+        (lds_u8*)(base + km_off(c0, g, 0, s))));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
+        (lds_u8*)(base + km_off(c0, g, 1, s))));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool WGRAD, int EPI>
+__device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* smem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    // ---- the work item -------------------------------------------------
+    int g, m_tile, n_tile;
+    int row0 = 0, valid = BM;        // DGRAD: the tile's rows
+    int k_begin = 0, k_end = p.K;    // WGRAD: the group's rows
+    {
+        if (WGRAD) {
+            const int per_g = p.m_tiles * p.n_tiles;
+            g = w / per_g;
+            const int local = w - g * per_g;
+            n_tile = local / p.m_tiles;
+            m_tile = local % p.m_tiles;
+            k_begin = p.offsets[g];
+            k_end = g < p.groups ? p.offsets[g + 1] : k_begin + p.extra_rows;
+        } else {
+            int lo = 0, hi = p.groups + (p.extra_rows > 0 ? 1 : 0) - 1;
+            while (lo < hi) {
+                int mid = (lo + hi + 1) >> 1;
+                if (p.tile_start[mid] * p.n_tiles <= w) lo = mid; else hi = mid - 1;
+            }
+            g = lo;
+            const int mt = p.tile_start[g + 1] - p.tile_start[g];
+            const int local = w - p.tile_start[g] * p.n_tiles;
+            n_tile = local / mt;
+            m_tile = local % mt;
+            const int base = p.offsets[g];
+            const int cnt = (g < p.groups ? p.offsets[g + 1] : base + p.extra_rows) - base;
+            row0 = base + (int)(((int64_t)m_tile * cnt) / mt);
+            valid = base + (int)(((int64_t)(m_tile + 1) * cnt) / mt) - row0;
+        }
+    }
+    const bool extra = g == p.groups;
+    const int nk = WGRAD ? (k_end - k_begin + BK - 1) / BK : p.K / BK;
+
+    // ---- DMA sources: 2 A blocks and 2 B blocks per wave and slice ------
+    const uint16_t* Bg = WGRAD ? p.B : (extra ? p.B_extra : p.B + (int64_t)g * p.b_group_stride);
+    // K-contiguous A (DGRAD): block b = 2 wave + q of the 16 (rows 16-row groups)
+    const int quad = lane >> 2, chunk = lane & 3;
+    auto block_row = [&](int blk) { return 64 * (blk >> 2) + 16 * (quad >> 2) + 4 * (blk & 3) + (quad & 3); };
+    // K-major blocks: block b = 2 wave + q: slab b >> 2, k block b & 3; lane
+    // l: k row 8 (b & 3) + (l >> 3), chunk position l & 7 holds chunk
+    // (l & 7) ^ (2 * (b & 1))
+    const uint16_t* a_src[2];       // DGRAD: A row source (the slice offset is added per slice)
+    int a_col[2], b_col[2];         // K-major sources: column of this lane's 16 bytes
+    unsigned a_lds[2], b_lds[2];
+    int kmrow[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int blk = 2 * wave + q;
+        const int kb = blk & 3, slab = blk >> 2;
+        kmrow[q] = 8 * kb + (lane >> 3);
+        const int qc = (lane & 7) ^ (2 * (kb & 1));
+        b_lds[q] = slab * 4096 + kb * 1024 + 16 * lane;
+        b_col[q] = min(n_tile * BN + slab * 64, p.N - 64) + qc * 8;
+        a_col[q] = 0;
+        a_src[q] = p.A;
+        if (WGRAD) {
+            a_col[q] = min(m_tile * BM + slab * 64, p.M - 64) + qc * 8;
+            a_lds[q] = b_lds[q];
+        } else {
+            const int ar = row0 + min(block_row(blk), valid - 1);
+            a_src[q] = p.A + (int64_t)ar * p.lda + chunk * 8;
+            a_lds[q] = (blk >> 2) * GROUP + BLK_OFF[blk & 3];
+        }
+    }
+    constexpr int A_BYTES = WGRAD ? KM_BYTES : KC_BYTES;
+    constexpr int STAGE_BYTES = A_BYTES + KM_BYTES;
+    const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
+    // row r of the K-major sources (WGRAD: the group's rows, zeros past the end)
+    auto b_row = [&](int r) -> const uint16_t* {
+        if (!WGRAD) return Bg + (int64_t)r * p.ldb;
+        if (r >= k_end) return p.zero_row;
+        int br = r;
+        if (p.b_rows) br = extra ? r - p.offsets[p.groups] : p.b_rows[r] / p.b_div;
+        return p.B + (int64_t)br * p.ldb;
+    };
+    auto issue = [&](int kt, int stage) {
+        const unsigned sb = lds_base + stage * STAGE_BYTES;
+        const int k0 = k_begin + kt * BK;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int r = k0 + kmrow[q];
+            const uint16_t* bs = b_row(r) + b_col[q];
+            if (WGRAD) {
+                const uint16_t* as = (r < k_end ? p.A + (int64_t)r * p.lda : p.zero_row) + a_col[q];
+                dma_frag(as, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
+            } else {
+                dma_frag(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
+            }
+            dma_frag(bs, __builtin_amdgcn_readfirstlane(sb + A_BYTES + b_lds[q]));
+        }
+    };
+
+    // fragment offsets of the K-contiguous A (DGRAD)
+    const int fr = lane & 15;
+    const unsigned lane_off = BLK_OFF[fr >> 2] + 64 * (fr & 3) + 16 * (lane >> 4);
+    auto tile_off = [&](int tau) { return (unsigned)((tau >> 2) * GROUP + 256 * (tau & 3)) + lane_off; };
+
+    // DGRAD: 16-row tiles past the tile's valid rows skip their MFMAs
+    int n_i = TM;
+    if (!WGRAD) {
+        const int ntile_valid = (valid + 15) >> 4;
+        n_i = 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) n_i += (wm + WM * i < ntile_valid) ? 1 : 0;
+        n_i = __builtin_amdgcn_readfirstlane(n_i);
+    }
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (nk > 0) {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) issue(min(s, nk - 1), s);
+
+        bf16x8 fa[2][TM], fb[2][TN];
+        auto read_frags = [&](int stage, bf16x8* a, bf16x8* b) {
+            const unsigned char* st = smem + stage * STAGE_BYTES;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) b[j] = km_frag(st + A_BYTES, (128 * wn + 16 * j), lane);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int tau = wm + WM * i;      // 16-row tile of the block
+                if (WGRAD) a[i] = km_frag(st, 16 * tau, lane);
+                else a[i] = *(const bf16x8*)(st + tile_off(tau));
+            }
+        };
+        auto mfmas = [&](const bf16x8* a, const bf16x8* b) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if (i < n_i) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        };
+        auto step = [&](int kt, const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb) {
+            wait_vm<4 * (STAGES - 3)>();
+            __builtin_amdgcn_s_barrier();
+            issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
+            read_frags((kt + 1 < nk ? kt + 1 : kt) % STAGES, na, nb);
+            mfmas(ca, cb);
+        };
+        wait_vm<4 * (STAGES - 2)>();
+        __builtin_amdgcn_s_barrier();
+        read_frags(0, fa[0], fb[0]);
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            step(kt, fa[0], fb[0], fa[1], fb[1]);
+            step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
+        }
+        if (kt < nk) step(kt, fa[0], fb[0], fa[1], fb[1]);
+        wait_vm<0>();
+    }
+
+    // ---- epilogue: lane holds column (lane & 15), rows 4 (lane >> 4) + v ---
+    const int ccol = lane & 15, crow = (lane >> 4) * 4;
+    if (WGRAD) {
+        float* C = (float*)(extra ? p.C_extra : (float*)p.C + (int64_t)g * p.c_group_stride);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = n_tile * BN + (128 * wn + 16 * j) + ccol;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = m_tile * BM + 16 * (wm + WM * i) + crow + v;
+                    if (m < p.M && col < p.N) C[(int64_t)m * p.ldc + col] = acc[i][j][v];
+                }
+            }
+    } else if (EPI == ACT) {
+        // dh (this tile's columns i of the N = I hidden units) -> dgu
+        const float L = extra ? p.limit_extra : p.limit;
+        uint16_t* D = (uint16_t*)p.C;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i >= n_i) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = n_tile * BN + (128 * wn + 16 * j) + ccol;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int lr = 16 * (wm + WM * i) + crow + v;
+                    if (lr < valid && col < p.N) {
+                        const int64_t r = row0 + lr;
+                        const float gv = bf16_to_f32(p.gu[r * 2 * p.N + col]);
+                        const float uv = bf16_to_f32(p.gu[r * 2 * p.N + p.N + col]);
+                        float dg, du;
+                        swiglu_clip_grad(gv, uv, L, dg, du);
+                        const float dh = acc[i][j][v];
+                        D[r * 2 * p.N + col] = f32_to_bf16(dh * dg);
+                        D[r * 2 * p.N + p.N + col] = f32_to_bf16(dh * du);
+                    }
+                }
+            }
+        }
+    } else {
+        float* C = (float*)p.C;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i >= n_i) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = n_tile * BN + (128 * wn + 16 * j) + ccol;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int lr = 16 * (wm + WM * i) + crow + v;
+                    if (lr < valid && col < p.N) C[(int64_t)(row0 + lr) * p.ldc + col] = acc[i][j][v];
+                }
+            }
+        }
+    }
+}
+
+// Work items: WGRAD (group, n-tile, m-tile); DGRAD (group, n-tile, m-tile)
+// from the tile plan.  Each XCD (blocks b with b % 8 == x) takes a
+// contiguous range, so the blocks that share an operand share an L2.
+template <bool WGRAD, int EPI>
+__global__ __launch_bounds__(NT, 1) void kernel(Params p) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * ((WGRAD ? KM_BYTES : KC_BYTES) + KM_BYTES)];
+    int total;
+    if (WGRAD) total = (p.groups + (p.extra_rows > 0 ? 1 : 0)) * p.m_tiles * p.n_tiles;
+    else total = p.tile_start[p.groups + (p.extra_rows > 0 ? 1 : 0)] * p.n_tiles;
+    const int per = (total + NXCD - 1) / NXCD;
+    const int xcd = blockIdx.x % NXCD, slots = gridDim.x / NXCD;
+    for (int s = blockIdx.x / NXCD; s < per; s += slots) {
+        const int w = xcd * per + s;
+        if (w >= total) break;
+        run_item<WGRAD, EPI>(p, w, smem);
+        __syncthreads();
+    }
+}
+
+template <bool WGRAD, int EPI>
+static hipError_t launch(const BwdArgs& a, hipStream_t s) {
+    Params p{};
+    p.A = (const uint16_t*)a.A;
+    p.lda = a.lda;
+    p.B = (const uint16_t*)a.B;
+    p.ldb = a.ldb;
+    p.b_group_stride = a.b_group_stride;
+    p.B_extra = (const uint16_t*)a.B_extra;
+    p.b_rows = a.b_rows;
+    p.b_div = a.b_div > 0 ? a.b_div : 1;
+    p.zero_row = (const uint16_t*)a.zero_row;
+    p.C = a.C;
+    p.ldc = a.ldc;
+    p.c_group_stride = a.c_group_stride;
+    p.C_extra = a.C_extra;
+    p.gu = (const uint16_t*)a.gu;
+    p.limit = a.limit;
+    p.limit_extra = a.limit_extra;
+    p.M = a.M;
+    p.N = a.N;
+    p.K = a.K;
+    p.offsets = a.offsets;
+    p.tile_start = a.tile_start;
+    p.groups = a.groups;
+    p.extra_rows = a.extra_rows;
+    p.n_tiles = (a.N + BN - 1) / BN;
+    p.m_tiles = (a.M + BM - 1) / BM;
+    int64_t items = WGRAD ? (int64_t)(a.groups + (a.extra_rows > 0 ? 1 : 0)) * p.m_tiles * p.n_tiles
+                          : (int64_t)a.max_tiles * p.n_tiles;
+    if (items <= 0) return hipSuccess;
+    const int64_t blocks = (items + NXCD - 1) / NXCD * NXCD;
+    kernel<WGRAD, EPI><<<(unsigned)blocks, NT, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace bg
+
+hipError_t launch_bwd_dgrad(const BwdArgs& a, bool act, hipStream_t s) {
+    return act ? bg::launch<false, bg::ACT>(a, s) : bg::launch<false, bg::F32>(a, s);
+}
+
+hipError_t launch_bwd_wgrad(const BwdArgs& a, hipStream_t s) { return bg::launch<true, bg::F32>(a, s); }
+
+}  // namespace moe

@@ -97,6 +97,7 @@ struct Params {
     int extra_rows;
     const uint16_t* W_extra;
     float limit_extra;
+    uint16_t* gu_out;           // SWIGLU (optional): the pre-activations [rows][2N] bf16, gate then up
 };
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -337,9 +338,19 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int lr = 16 * (wm + S::WM * i) + crow + v;
-                    if (lr < valid && hcol < p.N)
-                        H[(int64_t)(row0 + lr) * p.N + hcol] =
-                            f32_to_bf16(swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit));
+                    if (lr < valid && hcol < p.N) {
+                        const int64_t r = row0 + lr;
+                        if (p.gu_out) {
+                            // kept for the backward; the activation uses the same rounded values
+                            const uint16_t gq = f32_to_bf16(acc[i][j][v]);
+                            const uint16_t uq = f32_to_bf16(acc[i][j + TN / 2][v]);
+                            p.gu_out[r * 2 * p.N + hcol] = gq;
+                            p.gu_out[r * 2 * p.N + p.N + hcol] = uq;
+                            H[r * p.N + hcol] = f32_to_bf16(swiglu_clip(bf16_to_f32(gq), bf16_to_f32(uq), limit));
+                        } else {
+                            H[r * p.N + hcol] = f32_to_bf16(swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit));
+                        }
+                    }
                 }
             }
         }
@@ -433,6 +444,7 @@ hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s) {
     p.extra_rows = a.extra_rows;
     p.W_extra = (const uint16_t*)a.W_extra;
     p.limit_extra = a.limit_extra;
+    p.gu_out = (uint16_t*)a.gu_out;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
     if (a.bm == 64) gg::launch<gg::SWIGLU, 64, 256>(p, tiles, s);

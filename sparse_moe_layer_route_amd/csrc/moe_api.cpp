@@ -315,6 +315,54 @@ moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs
     return MOE_OK;
 }
 
+// ---- training: what the forward keeps, the backward's scratch -------------
+
+// The backward runs the shared expert as one more group of the routed
+// experts' launches, so it needs bf16 experts and Is == I (or no shared expert).
+bool train_ok(const Dims& d) { return !d.fp8 && (d.Is == 0 || d.Is == d.I); }
+int64_t train_rows(const Dims& d) { return d.P + (d.Is > 0 ? d.T : 0); }
+
+struct SavedWs {
+    size_t ids, w, s, counts, offsets, r2p, p2r, gu, h, y, total;
+};
+SavedWs saved_ws(const Dims& d) {
+    const int64_t rows = train_rows(d);
+    SavedWs S;
+    size_t o = 0;
+    S.ids = o;     o += align_up((size_t)d.P * 4);
+    S.w = o;       o += align_up((size_t)d.P * 4);
+    S.s = o;       o += align_up((size_t)d.P * 4);
+    S.counts = o;  o += align_up((size_t)d.E * 4);
+    S.offsets = o; o += align_up((size_t)(d.E + 1) * 4);
+    S.r2p = o;     o += align_up((size_t)d.P * 4);
+    S.p2r = o;     o += align_up((size_t)d.P * 4);
+    S.gu = o;      o += align_up((size_t)rows * 2 * d.I * 2);
+    S.h = o;       o += align_up((size_t)rows * d.I * 2);
+    S.y = o;       o += align_up((size_t)rows * d.H * 2);
+    S.total = o;
+    return S;
+}
+
+struct BwdWs {
+    size_t plan, zero, dy, dgu, dxr, da, total;
+};
+BwdWs bwd_ws(const Dims& d) {
+    const int64_t rows = train_rows(d);
+    BwdWs B;
+    size_t o = 0;
+    B.plan = o;  o += plan_ws(d);
+    B.zero = o;  o += align_up((size_t)std::max(d.H, 2 * d.I) * 2);
+    B.dy = o;    o += align_up((size_t)rows * d.H * 2);
+    B.dgu = o;   o += align_up((size_t)rows * 2 * d.I * 2);
+    B.dxr = o;   o += align_up((size_t)rows * d.H * 4);
+    B.da = o;    o += align_up((size_t)d.P * 4);
+    B.total = o;
+    return B;
+}
+int bwd_max_tiles(const Dims& d) {
+    return (int)((d.P + 255) / 256) + d.E + (d.Is > 0 ? (int)((d.T + 255) / 256) + 1 : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -502,6 +550,181 @@ moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* 
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, resid_out,
                          expert_counts_out, stream, resid_in);
+}
+
+moe_status_t moe_saved_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_config(cfg, T));
+    Dims d = dims(cfg, T);
+    if (!train_ok(d)) return MOE_ERR_UNSUPPORTED;
+    *bytes = saved_ws(d).total;
+    return MOE_OK;
+}
+
+moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_config(cfg, T));
+    Dims d = dims(cfg, T);
+    if (!train_ok(d)) return MOE_ERR_UNSUPPORTED;
+    *bytes = bwd_ws(d).total;
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_forward_train(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                                     const float* router_bias, const int32_t* topk_ids_in, const void* w13,
+                                     const void* w2, const void* ws13,
+                                     const void* ws2, void* out, void* saved, size_t saved_bytes, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_layer(cfg, T, x, w_router, w13, nullptr, w2, nullptr, ws13, ws2, out, ws, ws_bytes));
+    Dims d = dims(cfg, T);
+    if (!train_ok(d)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if ((!router_bias && !topk_ids_in) || !saved) return MOE_ERR_INVALID_ARGUMENT;
+    const SavedWs S = saved_ws(d);
+    if (saved_bytes < S.total) return MOE_ERR_WORKSPACE;
+    const LayerWs L = layer_ws(d);
+    char* base = (char*)ws;
+    char* sv = (char*)saved;
+    char* step = base + L.step;
+    int32_t* ids = (int32_t*)(sv + S.ids);
+    float* w = (float*)(sv + S.w);
+    int32_t* offsets = (int32_t*)(sv + S.offsets);
+    int32_t* r2p = (int32_t*)(sv + S.r2p);
+    int32_t* p2r = (int32_t*)(sv + S.p2r);
+    const bool shared = d.Is > 0;
+    HIP_TRY(moe::launch_router_logits(x, w_router, (float*)step, (int)T, d.E, d.H, stream));
+    if (topk_ids_in)
+        HIP_TRY(moe::launch_replay_weights((const float*)step, moe::router_splits(d.T, d.H), topk_ids_in, (int)T,
+                                           d.E, d.k, cfg->router_scaling_factor, cfg->norm_expert_weight, w, stream,
+                                           ids, (float*)(sv + S.s)));
+    else
+        HIP_TRY(moe::launch_topk((const float*)step, moe::router_splits(d.T, d.H), router_bias, (int)T, d.E, d.k,
+                                 cfg->router_scaling_factor, cfg->norm_expert_weight, ids, w, stream,
+                                 (float*)(sv + S.s)));
+    int32_t* tile_start = (int32_t*)(base + L.plan);
+    HIP_TRY(moe::launch_permute_plan(ids, (int)T, d.k, d.E, (int32_t*)(sv + S.counts), offsets, r2p, p2r, step,
+                                     tile_m(d), shared ? (int)T : 0, tile_start, stream));
+    moe::GroupedArgs up = up_args(cfg, d, x, offsets, r2p, w13, sv + S.h, tile_start, shared ? ws13 : nullptr);
+    up.gu_out = sv + S.gu;
+    HIP_TRY(moe::launch_grouped_up(up, stream));
+    HIP_TRY(moe::launch_grouped_down(down_args(d, sv + S.h, offsets, w2, sv + S.y, tile_start,
+                                               shared ? ws2 : nullptr), false, stream));
+    HIP_TRY(moe::launch_combine(sv + S.y, p2r, w, nullptr, shared ? sv + S.y + (size_t)d.P * d.H * 2 : nullptr,
+                                nullptr, out, cfg->out_dtype == MOE_BF16, (int)T, d.H, d.k, stream));
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_backward(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                                const void* w13, const void* w2, const void* ws13, const void* ws2,
+                                const void* saved, size_t saved_bytes, const float* dout, float* dx,
+                                float* dw_router, float* dw13, float* dw2, float* dws13, float* dws2, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    Dims d = dims(cfg, T);
+    if (!train_ok(d)) return MOE_ERR_UNSUPPORTED;
+    const bool shared = d.Is > 0;
+    if (!dw_router || !dw13 || !dw2 || (shared && (!dws13 || !dws2))) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) {
+        // no rows: every weight gradient is zero
+        HIP_TRY(moe::launch_zero_u32(dw2, (int64_t)d.E * d.H * d.I, stream));
+        HIP_TRY(moe::launch_zero_u32(dw13, (int64_t)d.E * 2 * d.I * d.H, stream));
+        HIP_TRY(moe::launch_zero_u32(dw_router, (int64_t)d.E * d.H, stream));
+        if (shared) {
+            HIP_TRY(moe::launch_zero_u32(dws2, (int64_t)d.H * d.I, stream));
+            HIP_TRY(moe::launch_zero_u32(dws13, (int64_t)2 * d.I * d.H, stream));
+        }
+        return MOE_OK;
+    }
+    if (!x || !w_router || !w13 || !w2 || !saved || !dout || !dx || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    if (shared && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARGUMENT;
+    const SavedWs S = saved_ws(d);
+    const BwdWs B = bwd_ws(d);
+    if (saved_bytes < S.total || ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    const char* sv = (const char*)saved;
+    const int32_t* ids = (const int32_t*)(sv + S.ids);
+    const int32_t* offsets = (const int32_t*)(sv + S.offsets);
+    const int32_t* r2p = (const int32_t*)(sv + S.r2p);
+    const int32_t* p2r = (const int32_t*)(sv + S.p2r);
+    int32_t* tile_start = (int32_t*)(base + B.plan);
+    float* da = (float*)(base + B.da);
+    const int extra = shared ? (int)T : 0;
+    {
+        HIP_TRY(moe::launch_zero_u32(base + B.zero, (int64_t)std::max(d.H, 2 * d.I) / 2, stream));
+        HIP_TRY(moe::launch_tile_plan(offsets, d.E, 256, extra, tile_start, stream));
+        HIP_TRY(moe::launch_bwd_prep(dout, sv + S.y, p2r, (const float*)(sv + S.w), (const float*)(sv + S.s),
+                                     cfg->router_scaling_factor, cfg->norm_expert_weight, shared, base + B.dy, da,
+                                     (int)T, d.H, d.k, stream));
+        // dh -> dgu: dy [rows][H] against W2 [H][I] (contracted over H)
+        moe::BwdArgs a2;
+        a2.A = base + B.dy;
+        a2.lda = d.H;
+        a2.B = w2;
+        a2.ldb = d.I;
+        a2.b_group_stride = (int64_t)d.H * d.I;
+        a2.B_extra = ws2;
+        a2.C = base + B.dgu;
+        a2.gu = sv + S.gu;
+        a2.limit = cfg->swiglu_limit;
+        a2.limit_extra = cfg->swiglu_limit_shared;
+        a2.N = d.I;
+        a2.K = d.H;
+        a2.offsets = offsets;
+        a2.tile_start = tile_start;
+        a2.groups = d.E;
+        a2.extra_rows = extra;
+        a2.max_tiles = bwd_max_tiles(d);
+        HIP_TRY(moe::launch_bwd_dgrad(a2, true, stream));
+        // dx rows: dgu [rows][2I] against W13 [2I][H]
+        moe::BwdArgs a1 = a2;
+        a1.A = base + B.dgu;
+        a1.lda = 2 * d.I;
+        a1.B = w13;
+        a1.ldb = d.H;
+        a1.b_group_stride = (int64_t)2 * d.I * d.H;
+        a1.B_extra = ws13;
+        a1.C = base + B.dxr;
+        a1.ldc = d.H;
+        a1.gu = nullptr;
+        a1.N = d.H;
+        a1.K = 2 * d.I;
+        HIP_TRY(moe::launch_bwd_dgrad(a1, false, stream));
+        HIP_TRY(moe::launch_bwd_dx((const float*)(base + B.dxr), p2r, da, ids, w_router, shared, dx, (int)T, d.H,
+                                   d.k, stream));
+    }
+    // weight gradients (every expert; those without rows get zeros)
+    moe::BwdArgs g2;
+    g2.A = base + B.dy;
+    g2.lda = d.H;
+    g2.B = sv + S.h;
+    g2.ldb = d.I;
+    g2.zero_row = base + B.zero;
+    g2.C = dw2;
+    g2.ldc = d.I;
+    g2.c_group_stride = (int64_t)d.H * d.I;
+    g2.C_extra = dws2;
+    g2.M = d.H;
+    g2.N = d.I;
+    g2.offsets = offsets;
+    g2.groups = d.E;
+    g2.extra_rows = extra;
+    moe::BwdArgs g1 = g2;
+    g1.A = base + B.dgu;
+    g1.lda = 2 * d.I;
+    g1.B = x;
+    g1.ldb = d.H;
+    g1.b_rows = r2p;
+    g1.b_div = d.k;
+    g1.C = dw13;
+    g1.ldc = d.H;
+    g1.c_group_stride = (int64_t)2 * d.I * d.H;
+    g1.C_extra = dws13;
+    g1.M = 2 * d.I;
+    g1.N = d.H;
+    HIP_TRY(moe::launch_bwd_wgrad(g2, stream));
+    HIP_TRY(moe::launch_bwd_wgrad(g1, stream));
+    HIP_TRY(moe::launch_bwd_router_wgrad(da, offsets, r2p, x, dw_router, d.E, d.H, d.k, stream));
+    return MOE_OK;
 }
 
 const char* moe_status_string(moe_status_t status) {

@@ -51,6 +51,22 @@ __device__ __forceinline__ float swiglu_clip(float g, float u, float L) {
     return sg * u;
 }
 
+// Derivatives of swiglu_clip with respect to g and u.  Each clamp passes the
+// gradient where its input lies in its range, ends included, else none.
+__device__ __forceinline__ void swiglu_clip_grad(float g, float u, float L, float& dg, float& du) {
+    const float sg = 1.0f / (1.0f + __expf(-g));
+    const float sl = g * sg;
+    const float dsl = sg * (1.0f + g * (1.0f - sg));
+    if (L > 0.0f) {
+        const float uc = fminf(fmaxf(u, -L), L);
+        dg = sl <= L ? uc * dsl : 0.0f;
+        du = (u >= -L && u <= L) ? fminf(sl, L) : 0.0f;
+    } else {
+        dg = u * dsl;
+        du = sl;
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -16,10 +16,11 @@ hipError_t launch_router_logits(const void* x, const void* w_router, float* logi
                                 int T, int E, int H, hipStream_t s);
 // per-token sigmoid + bias + top-k + weights (partial logits summed in order)
 hipError_t launch_topk(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
-                       int norm, int32_t* ids, float* w, hipStream_t s);
+                       int norm, int32_t* ids, float* w, hipStream_t s, float* s_out = nullptr);
 // weights of caller-supplied expert ids from the same partial logits
 hipError_t launch_replay_weights(const float* logits, int nsplit, const int32_t* ids, int T, int E, int k,
-                                 float scale, int norm, float* w, hipStream_t s);
+                                 float scale, int norm, float* w, hipStream_t s, int32_t* ids_out = nullptr,
+                                 float* s_out = nullptr);
 // ids[p] = p mod E for the P = T*k pairs
 hipError_t launch_balanced_ids(int32_t* ids, int64_t P, int E, hipStream_t s);
 
@@ -63,6 +64,7 @@ struct GroupedArgs {
     int extra_rows = 0;
     const void* W_extra = nullptr;
     float limit_extra = 0.f;
+    void* gu_out = nullptr;          // first projection: also keep the pre-activations (bf16 [rows][2N])
 };
 int grouped_tile_m(int64_t rows, int groups);
 hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s);
@@ -94,5 +96,49 @@ hipError_t launch_rmsnorm(const float* resid, const float* norm_weight, float ep
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
                           const float* y_shared, const void* shared_rows, const float* resid, void* out,
                           bool out_bf16, int T, int H, int k, hipStream_t s);
+
+// ---- backward ------------------------------------------------------------
+
+// grouped GEMMs of the backward (bwd_gemm.hip); see Params there
+struct BwdArgs {
+    const void* A = nullptr;
+    int64_t lda = 0;
+    const void* B = nullptr;
+    int64_t ldb = 0;
+    int64_t b_group_stride = 0;
+    const void* B_extra = nullptr;
+    const int32_t* b_rows = nullptr;
+    int b_div = 1;
+    const void* zero_row = nullptr;
+    void* C = nullptr;
+    int64_t ldc = 0;
+    int64_t c_group_stride = 0;
+    void* C_extra = nullptr;
+    const void* gu = nullptr;
+    float limit = 0.f, limit_extra = 0.f;
+    int M = 0, N = 0, K = 0;
+    const int32_t* offsets = nullptr;
+    const int32_t* tile_start = nullptr;
+    int groups = 0;
+    int extra_rows = 0;
+    int max_tiles = 0;
+};
+// DGRAD: rows grouped, B = the group's weight [K][N]; act: the SwiGLU
+// backward epilogue writing dgu [rows][2N] bf16, else fp32 rows
+hipError_t launch_bwd_dgrad(const BwdArgs& a, bool act, hipStream_t s);
+// WGRAD: the contraction runs over each group's rows; fp32 [M][N] per group
+hipError_t launch_bwd_wgrad(const BwdArgs& a, hipStream_t s);
+// per token: dw_j = dout . y_j, dy rows (w_j dout; the shared rows dout) in
+// bf16, and the router's da_j from the saved raw scores (bwd.hip)
+hipError_t launch_bwd_prep(const float* dout, const void* y_rows, const int32_t* p2r, const float* w,
+                           const float* s_raw, float scale, int norm, bool shared, void* dy, float* da, int T,
+                           int H, int k, hipStream_t s);
+// dx[t] = sum_j dxr[p2r[t,j]] + dxr[P + t] (shared) + sum_j da[t,j] Wg[ids[t,j]]
+hipError_t launch_bwd_dx(const float* dxr, const int32_t* p2r, const float* da, const int32_t* ids,
+                         const void* w_router, bool shared, float* dx, int T, int H, int k, hipStream_t s);
+// dWg[e] = sum over e's rows r of da[pair r] x[token r]
+hipError_t launch_bwd_router_wgrad(const float* da, const int32_t* offsets, const int32_t* r2p, const void* x,
+                                   float* dwg, int E, int H, int k, hipStream_t s);
+hipError_t launch_zero_u32(void* p, int64_t words, hipStream_t s);
 
 }  // namespace moe

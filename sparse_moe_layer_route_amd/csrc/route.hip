@@ -34,7 +34,7 @@ template <int BATCH, int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit,
                                                    const float* __restrict__ bias, int T, int E, int k,
                                                    float scale, int norm, int32_t* __restrict__ ids,
-                                                   float* __restrict__ wout) {
+                                                   float* __restrict__ wout, float* __restrict__ s_out) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;                            // whole wave leaves together
@@ -99,6 +99,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const float sum = wave_sum(lane < k ? my_w : 0.f);
     const float w = norm ? my_w / sum : my_w;
     if (lane < k) wout[(int64_t)t * k + lane] = w * scale;
+    if (s_out && lane < k) s_out[(int64_t)t * k + lane] = my_w;
 }
 
 // Routing replay (miles page "Step-5-Preview", section 5.2 Algorithm: the
@@ -111,13 +112,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // lane j < k owns slot j.
 __global__ __launch_bounds__(256) void replay_kernel(const float* __restrict__ logits, int nsplit,
                                                      const int32_t* __restrict__ ids_in, int T, int E, int k,
-                                                     float scale, int norm, float* __restrict__ wout) {
+                                                     float scale, int norm, float* __restrict__ wout,
+                                                     int32_t* __restrict__ ids_out, float* __restrict__ s_out) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     float s = 0.f;
     if (lane < k) {
         const int e = min(max(ids_in[(int64_t)t * k + lane], 0), E - 1);
+        if (ids_out) ids_out[(int64_t)t * k + lane] = e;
         const float* lg = logits + (int64_t)t * E + e;
         float part[8];
         float a = 0.f;
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(256) void replay_kernel(const float* __restrict__ l
     const float sum = wave_sum(lane < k ? s : 0.f);
     const float w = norm ? s / sum : s;
     if (lane < k) wout[(int64_t)t * k + lane] = w * scale;
+    if (s_out && lane < k) s_out[(int64_t)t * k + lane] = s;
 }
 
 // Static balanced routing (AutoModel page, benchmark table): pair
@@ -144,9 +148,9 @@ __global__ __launch_bounds__(256) void balanced_ids_kernel(int32_t* __restrict__
 }
 
 hipError_t launch_replay_weights(const float* logits, int nsplit, const int32_t* ids, int T, int E, int k,
-                                 float scale, int norm, float* w, hipStream_t s) {
+                                 float scale, int norm, float* w, hipStream_t s, int32_t* ids_out, float* s_out) {
     if (T <= 0) return hipSuccess;
-    replay_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, ids, T, E, k, scale, norm, w);
+    replay_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, ids, T, E, k, scale, norm, w, ids_out, s_out);
     return hipGetLastError();
 }
 
@@ -160,27 +164,27 @@ hipError_t launch_balanced_ids(int32_t* ids, int64_t P, int E, hipStream_t s) {
 
 template <int BATCH, int NPL>
 static void launch_topk_n(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
-                          int norm, int32_t* ids, float* w, hipStream_t s) {
-    topk_kernel<BATCH, NPL><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, bias, T, E, k, scale, norm, ids, w);
+                          int norm, int32_t* ids, float* w, hipStream_t s, float* s_out) {
+    topk_kernel<BATCH, NPL><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s_out);
 }
 
 template <int BATCH>
 static void launch_topk_b(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
-                          int norm, int32_t* ids, float* w, hipStream_t s) {
-    if (E <= 128) launch_topk_n<BATCH, 2>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
-    else if (E <= 256) launch_topk_n<BATCH, 4>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
-    else if (E <= 384) launch_topk_n<BATCH, 6>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
-    else if (E <= 512) launch_topk_n<BATCH, 8>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
-    else launch_topk_n<BATCH, TOPK_MAX_PER_LANE>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+                          int norm, int32_t* ids, float* w, hipStream_t s, float* s_out) {
+    if (E <= 128) launch_topk_n<BATCH, 2>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s, s_out);
+    else if (E <= 256) launch_topk_n<BATCH, 4>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s, s_out);
+    else if (E <= 384) launch_topk_n<BATCH, 6>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s, s_out);
+    else if (E <= 512) launch_topk_n<BATCH, 8>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s, s_out);
+    else launch_topk_n<BATCH, TOPK_MAX_PER_LANE>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s, s_out);
 }
 
 hipError_t launch_topk(const float* logits, int nsplit, const float* bias, int T, int E, int k, float scale,
-                       int norm, int32_t* ids, float* w, hipStream_t s) {
+                       int norm, int32_t* ids, float* w, hipStream_t s, float* s_out) {
     if (T <= 0) return hipSuccess;
     if (nsplit > 1)
-        launch_topk_b<8>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+        launch_topk_b<8>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s, s_out);
     else
-        launch_topk_b<1>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s);
+        launch_topk_b<1>(logits, nsplit, bias, T, E, k, scale, norm, ids, w, s, s_out);
     return hipGetLastError();
 }
 

@@ -229,3 +229,29 @@ def test_norm_and_block_argument_rules(lib):
     assert lib.moe_block_forward(c, 0, None, None, 1e-5, *((None,) * 13), 0, None) == 0
     # combine: a bf16 output may not overwrite the fp32 residual it reads
     assert lib.moe_combine(bf, 4, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 1
+
+
+def test_training_entry_points_rules(lib):
+    n = ctypes.c_size_t(0)
+    c = cfg_of()                                                   # tiny: Is == I, bf16
+    assert lib.moe_saved_bytes(ctypes.byref(c), 64, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(c), 64, ctypes.byref(n)) == 0 and n.value > 0
+    for bad in (cfg_of(expert_dtype="fp8"), cfg_of(share_expert_dim=64)):
+        assert lib.moe_saved_bytes(ctypes.byref(bad), 64, ctypes.byref(n)) == 2
+        assert lib.moe_backward_workspace_size(ctypes.byref(bad), 64, ctypes.byref(n)) == 2
+    assert lib.moe_saved_bytes(ctypes.byref(cfg_of(share_expert_dim=0)), 64, ctypes.byref(n)) == 0
+    cr = ctypes.byref(c)
+    # training forward: no saved buffer; saved too small
+    st, need = ws_size(cfg_of(), 64)
+    assert lib.moe_layer_forward_train(cr, 64, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
+                                       need, None) == 1
+    assert lib.moe_layer_forward_train(cr, 64, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE,
+                                       need, None) == 3
+    # backward: missing gradient buffers; small state or scratch
+    grads = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert lib.moe_layer_backward(cr, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, FAKE, None, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_layer_backward(cr, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, *grads, FAKE,
+                                  1 << 30, None) == 3
+    assert lib.moe_layer_backward(cr, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, *grads, FAKE,
+                                  16, None) == 3
