@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-balanced", action="store_true", help="skip the static balanced routing report")
     ap.add_argument("--no-block", action="store_true", help="skip the RMSNorm + residual block report")
+    ap.add_argument("--no-train", action="store_true", help="skip the forward + backward training report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -191,6 +192,10 @@ def main():
         note(f"{wl.name} as a block: RMSNorm in front, fp32 residual add in the combine")
         res["block"] = time_block(args, wl, moe, torch, mi)
 
+    if not args.no_train:
+        note(f"{wl.name} training step: moe_layer_forward_train + moe_layer_backward")
+        res["train"] = time_train(args, wl, moe, torch, mi)
+
     if not args.no_decode:
         note(f"decode workload {args.decode_workload}")
         res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
@@ -334,6 +339,56 @@ def time_block(args, wl, moe, torch, mi):
     return {"workload": wl.name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "rmsnorm_us": norm_us,
             "rmsnorm_gbs": norm_bytes / (norm_us * 1e-6) / 1e9,
             "rmsnorm_hbm_frac": norm_bytes / (norm_us * 1e-6) / HBM_PEAK}
+
+
+def time_train(args, wl, moe, torch, mi):
+    """One training step of the layer: moe_layer_forward_train then
+    moe_layer_backward (dL/dout given), each bracketed by HIP events."""
+    cfg, T, H, E, k, I = (wl.cfg, wl.T, wl.cfg.hidden_size, wl.cfg.num_experts, wl.cfg.top_k,
+                          wl.cfg.moe_intermediate_size)
+    inp = mi.make_inputs(wl, "cuda", seed=0)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    dout = torch.randn((T, H), generator=g, device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    ws = moe.workspace(cfg, T)
+    bws = torch.empty(moe.moe_backward_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(moe.moe_saved_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    grads = None
+    for _ in range(args.warmup):
+        moe.moe_layer_forward_train(cfg, inp, out=out, saved=saved, ws=ws, stream=stream)
+        grads = moe.moe_layer_backward(cfg, inp, saved, dout, grads=grads, ws=bws, stream=stream)
+    torch.cuda.synchronize()
+    P = T * k
+    ids = saved[:P * 4].view(torch.int32)
+    touched = int(torch.unique(ids).numel())
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        moe.moe_layer_forward_train(cfg, inp, out=out, saved=saved, ws=ws, stream=stream)
+        ev[i][1].record(stream)
+        moe.moe_layer_backward(cfg, inp, saved, dout, grads=grads, ws=bws, stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    fwd = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    # backward FLOPs: data and weight gradients of both projections, routed
+    # rows and the shared expert's (two forward GEMMs' worth each)
+    rows = P + (T if cfg.share_expert_dim else 0)
+    bwd_flops = 2 * (2 * rows * 3 * I * H)
+    # HBM floor of the backward: fp32 weight gradients of every expert written
+    # once, the touched experts' bf16 weights read once
+    grad_bytes = 4 * (E * 3 * I * H + E * H + (3 * cfg.share_expert_dim * H))
+    w_bytes = 2 * (touched * 3 * I * H + 3 * cfg.share_expert_dim * H)
+    del inp, ws, bws, saved, out, grads, dout
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "forward_train_ms": fwd, "backward_ms": bwd, "step_ms": fwd + bwd,
+            "tokens_per_s": T / ((fwd + bwd) * 1e-3), "experts_touched": touched,
+            "backward_tflops": bwd_flops / (bwd * 1e-3) / 1e12,
+            "backward_mfma_frac": bwd_flops / (bwd * 1e-3) / BF16_PEAK,
+            "backward_floor_bytes": grad_bytes + w_bytes,
+            "backward_hbm_frac": (grad_bytes + w_bytes) / (bwd * 1e-3) / HBM_PEAK}
 
 
 def bench_decode(args, wl, moe, torch):

@@ -132,6 +132,17 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(const float* __re
     o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+// one block per row: 16 bytes per thread and step
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ r2p, uint16_t* __restrict__ out,
+                                                          int64_t P, int H, int k) {
+    const int64_t r = blockIdx.x;
+    const int64_t src = r < P ? r2p[r] / k : r - P;
+    const uint4* from = (const uint4*)(x + src * H);
+    uint4* to = (uint4*)(out + r * H);
+    for (int i = threadIdx.x; i < H / 8; i += 256) to[i] = from[i];
+}
+
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -157,6 +168,15 @@ hipError_t launch_bwd_router_wgrad(const float* da, const int32_t* offsets, cons
                                    float* dwg, int E, int H, int k, hipStream_t s) {
     bwd_router_wgrad_kernel<<<dim3(E, (H + 2047) / 2048), 256, 0, s>>>(da, offsets, r2p, (const uint16_t*)x, dwg,
                                                                        H, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* r2p, bool shared, void* out, int T, int H, int k,
+                              hipStream_t s) {
+    const int64_t P = (int64_t)T * k;
+    const int64_t rows = P + (shared ? T : 0);
+    if (rows <= 0) return hipSuccess;
+    gather_rows_kernel<<<(unsigned)rows, 256, 0, s>>>((const uint16_t*)x, r2p, (uint16_t*)out, P, H, k);
     return hipGetLastError();
 }
 

@@ -20,13 +20,16 @@
 //     the saved pre-activations gu, giving dgu (bf16 [rows][2N]); F32 --
 //     plain fp32 rows.
 //   * WGRAD (groups partition the contraction K = the group's rows): A and
-//     B are K-major row sets (dy or dgu, and h or the gathered x rows); every
-//     group, empty ones included, writes its full fp32 [M][N] gradient.
+//     B are K-major row sets (dy or dgu, and h or the x rows in row order);
+//     every group, empty ones included, writes its full fp32 [M][N] gradient.
 //
-// Block tile 256 x 256, K slices of 32, 8 waves as 4 along M x 2 along N
-// (64 x 128 each), 16x16x32 bf16 MFMA, direct global -> LDS DMA (inline asm,
-// explicit vmcnt waits), 4 LDS stages, fragments of slice k+1 read while
-// slice k multiplies -- the forward kernel's scheme.
+// Each wave computes 64 x 128 of the output with 16x16x32 bf16 MFMA; operands
+// go global -> LDS by direct DMA (inline asm, explicit vmcnt waits) and the
+// fragments of slice k+1 are read while slice k multiplies -- the forward
+// kernel's scheme.  Block tile 256 x 256, 8 waves (4 along M x 2 along N),
+// 4 LDS stages, one block per CU.  (A 128 x 256 weight-gradient tile with 4
+// waves, two blocks per CU, measured slower: 21.9 against 18.0 ms for the
+// Step-5 prefill backward.)
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -35,23 +38,44 @@ namespace moe {
 namespace bg {
 
 constexpr int BK = 32;
-constexpr int NW = 8;
-constexpr int NT = NW * 64;
-constexpr int BM = 256, BN = 256;
-constexpr int WM = 4, WN = 2;           // waves along M, N
-constexpr int TM = 4, TN = 8;           // 16-row / 16-col tiles per wave
+constexpr int BN = 256;
+constexpr int TM = 4, TN = 8;           // 16-row / 16-col tiles per wave (64 x 128)
 constexpr int NXCD = 8;
 // K-contiguous operand (16 rows x 64 B per DMA block), as in the forward
 // kernel: the 4 blocks of a 64-row group at bank groups 0, 2, 16, 18
 __device__ constexpr int BLK_OFF[4] = {0, 1024 + 32, 2048 + 256, 3072 + 288};
 constexpr int GROUP = 3072 + 288 + 1024;
 constexpr int KC_BYTES = 4 * GROUP;     // 256 rows x one K slice
-// K-major operand: 4 slabs of 64 columns x 4 blocks of 8 k-rows (1 KiB,
-// 128 B per row); odd blocks have their 16-byte chunks swapped in pairs of
-// pairs (chunk q at q ^ 2) so that a 32-lane pass of a transposing read,
-// which touches rows of two neighbouring blocks, hits distinct banks
-constexpr int KM_BYTES = 16 * 1024;
-constexpr int STAGES = 4;
+// K-major operand: 4 slabs of 64 columns x 4 blocks of 8 k-rows (one DMA
+// block each: 128 B per row, lane-consecutive).  The blocks of a slab sit
+// 1056 B apart, not 1024: a 32-lane pass of a transposing read touches 4
+// rows of two neighbouring blocks, and the 32-byte skew puts them on
+// distinct banks.
+constexpr int KB_PITCH = 1024 + 32;
+constexpr int SLAB = 4 * KB_PITCH;
+constexpr int KM_BYTES = 4 * SLAB;
+// epilogue staging: rows of 256 fp32 with a 16-byte skew per row, so the 4
+// row groups of an MFMA store land on distinct banks
+constexpr int EPI_PITCH = 256 + 4;
+
+template <bool WGRAD>
+struct Tile {
+    static constexpr int NW = 8;                        // waves per block
+    static constexpr int BM = 256;
+    static constexpr int WM = BM / 64;                  // waves along M
+    static constexpr int WN = NW / WM;                  // waves along N (2)
+    static constexpr int NA = BM / 16;                  // A DMA blocks per slice
+    static constexpr int NB = BN / 16;                  // B DMA blocks per slice
+    static constexpr int A_PER_WAVE = NA / NW;
+    static constexpr int B_PER_WAVE = NB / NW;
+    static constexpr int A_BYTES = WGRAD ? (BM / 64) * SLAB : KC_BYTES;
+    static constexpr int STAGE_BYTES = A_BYTES + KM_BYTES;
+    static constexpr int STAGES = 4;
+    static constexpr int EPI_ROWS = 128;                // rows per staging pass
+    static constexpr int SMEM = STAGES * STAGE_BYTES > EPI_ROWS * EPI_PITCH * 4 ? STAGES * STAGE_BYTES
+                                                                                 : EPI_ROWS * EPI_PITCH * 4;
+    static_assert(WN == 2 && NA % NW == 0 && NB % NW == 0, "tile shape");
+};
 
 enum { ACT = 0, F32 = 1 };
 
@@ -62,8 +86,6 @@ struct Params {
     int64_t ldb;
     int64_t b_group_stride;
     const uint16_t* B_extra;    // DGRAD: the extra group's weight [K][N]
-    const int32_t* b_rows;      // WGRAD: B row of activation row r is b_rows[r] / b_div (r < rows of
-    int b_div;                  //   the groups), r - offsets[groups] (extra rows); nullptr: row r
     const uint16_t* zero_row;   // WGRAD: >= max(M, N) zero values, read for k rows past a group's end
     void* C;
     int64_t ldc;
@@ -96,9 +118,7 @@ __device__ __forceinline__ void wait_vm() {
 // its 16-lane group g) reads for the 16-column tile starting at column c0,
 // k rows 8g + 4 half + (s >> 2)
 __device__ __forceinline__ unsigned km_off(int c0, int g, int half, int s) {
-    const int c = (c0 & 63) + 4 * (s & 3);
-    const int q = (c >> 3) ^ ((g & 1) << 1);
-    return (unsigned)((c0 >> 6) * 4096 + g * 1024 + (4 * half + (s >> 2)) * 128 + q * 16 + (c & 4) * 2);
+    return (unsigned)((c0 >> 6) * SLAB + g * KB_PITCH + (4 * half + (s >> 2)) * 128 + (c0 & 63) * 2 + (s & 3) * 8);
 }
 
 // a 16x16x32 fragment from a K-major operand: two transposing reads
@@ -115,6 +135,9 @@ __device__ __forceinline__ bf16x8 km_frag(const unsigned char* base, int c0, int
 
 template <bool WGRAD, int EPI>
 __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* smem) {
+    using S = Tile<WGRAD>;
+    constexpr int NW = S::NW, BM = S::BM, WM = S::WM, WN = S::WN, STAGES = S::STAGES;
+    constexpr int A_PER_WAVE = S::A_PER_WAVE, B_PER_WAVE = S::B_PER_WAVE, D = A_PER_WAVE + B_PER_WAVE;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -153,63 +176,66 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     const bool extra = g == p.groups;
     const int nk = WGRAD ? (k_end - k_begin + BK - 1) / BK : p.K / BK;
 
-    // ---- DMA sources: 2 A blocks and 2 B blocks per wave and slice ------
+    // ---- DMA sources ----------------------------------------------------
     const uint16_t* Bg = WGRAD ? p.B : (extra ? p.B_extra : p.B + (int64_t)g * p.b_group_stride);
-    // K-contiguous A (DGRAD): block b = 2 wave + q of the 16 (rows 16-row groups)
+    // K-contiguous A (DGRAD): block b of the 16 (16 rows x 64 B), rows as in
+    // the forward kernel
     const int quad = lane >> 2, chunk = lane & 3;
     auto block_row = [&](int blk) { return 64 * (blk >> 2) + 16 * (quad >> 2) + 4 * (blk & 3) + (quad & 3); };
-    // K-major blocks: block b = 2 wave + q: slab b >> 2, k block b & 3; lane
-    // l: k row 8 (b & 3) + (l >> 3), chunk position l & 7 holds chunk
-    // (l & 7) ^ (2 * (b & 1))
-    const uint16_t* a_src[2];       // DGRAD: A row source (the slice offset is added per slice)
-    int a_col[2], b_col[2];         // K-major sources: column of this lane's 16 bytes
-    unsigned a_lds[2], b_lds[2];
-    int kmrow[2];
+    // K-major blocks b: slab b >> 2, k block b & 3; lane l: k row
+    // 8 (b & 3) + (l >> 3), 16-byte chunk l & 7 of the slab's row
+    const uint16_t* a_src[A_PER_WAVE];   // DGRAD: A row source (the slice offset is added per slice)
+    int a_col[A_PER_WAVE], a_row[A_PER_WAVE];
+    unsigned a_lds[A_PER_WAVE];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int blk = 2 * wave + q;
+    for (int q = 0; q < A_PER_WAVE; ++q) {
+        const int blk = A_PER_WAVE * wave + q;
         const int kb = blk & 3, slab = blk >> 2;
-        kmrow[q] = 8 * kb + (lane >> 3);
-        const int qc = (lane & 7) ^ (2 * (kb & 1));
-        b_lds[q] = slab * 4096 + kb * 1024 + 16 * lane;
-        b_col[q] = min(n_tile * BN + slab * 64, p.N - 64) + qc * 8;
+        a_row[q] = 8 * kb + (lane >> 3);
         a_col[q] = 0;
         a_src[q] = p.A;
         if (WGRAD) {
-            a_col[q] = min(m_tile * BM + slab * 64, p.M - 64) + qc * 8;
-            a_lds[q] = b_lds[q];
+            a_col[q] = min(m_tile * BM + slab * 64, p.M - 64) + (lane & 7) * 8;
+            a_lds[q] = slab * SLAB + kb * KB_PITCH + 16 * lane;
         } else {
             const int ar = row0 + min(block_row(blk), valid - 1);
             a_src[q] = p.A + (int64_t)ar * p.lda + chunk * 8;
             a_lds[q] = (blk >> 2) * GROUP + BLK_OFF[blk & 3];
         }
     }
-    constexpr int A_BYTES = WGRAD ? KM_BYTES : KC_BYTES;
-    constexpr int STAGE_BYTES = A_BYTES + KM_BYTES;
+    int b_col[B_PER_WAVE], b_row_k[B_PER_WAVE];
+    unsigned b_lds[B_PER_WAVE];
+#pragma unroll
+    for (int q = 0; q < B_PER_WAVE; ++q) {
+        const int blk = B_PER_WAVE * wave + q;
+        const int kb = blk & 3, slab = blk >> 2;
+        b_row_k[q] = 8 * kb + (lane >> 3);
+        b_col[q] = min(n_tile * BN + slab * 64, p.N - 64) + (lane & 7) * 8;
+        b_lds[q] = S::A_BYTES + slab * SLAB + kb * KB_PITCH + 16 * lane;
+    }
     const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
     // row r of the K-major sources (WGRAD: the group's rows, zeros past the end)
     auto b_row = [&](int r) -> const uint16_t* {
         if (!WGRAD) return Bg + (int64_t)r * p.ldb;
         if (r >= k_end) return p.zero_row;
-        int br = r;
-        if (p.b_rows) br = extra ? r - p.offsets[p.groups] : p.b_rows[r] / p.b_div;
-        return p.B + (int64_t)br * p.ldb;
+        return p.B + (int64_t)r * p.ldb;
     };
     auto issue = [&](int kt, int stage) {
-        const unsigned sb = lds_base + stage * STAGE_BYTES;
+        const unsigned sb = lds_base + stage * S::STAGE_BYTES;
         const int k0 = k_begin + kt * BK;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int r = k0 + kmrow[q];
-            const uint16_t* bs = b_row(r) + b_col[q];
+        for (int q = 0; q < A_PER_WAVE; ++q) {
             if (WGRAD) {
+                const int r = k0 + a_row[q];
                 const uint16_t* as = (r < k_end ? p.A + (int64_t)r * p.lda : p.zero_row) + a_col[q];
                 dma_frag(as, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
             } else {
                 dma_frag(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
             }
-            dma_frag(bs, __builtin_amdgcn_readfirstlane(sb + A_BYTES + b_lds[q]));
         }
+#pragma unroll
+        for (int q = 0; q < B_PER_WAVE; ++q)
+            dma_frag(b_row(k0 + b_row_k[q]) + b_col[q], __builtin_amdgcn_readfirstlane(sb + b_lds[q]));
     };
 
     // fragment offsets of the K-contiguous A (DGRAD)
@@ -239,9 +265,9 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 
         bf16x8 fa[2][TM], fb[2][TN];
         auto read_frags = [&](int stage, bf16x8* a, bf16x8* b) {
-            const unsigned char* st = smem + stage * STAGE_BYTES;
+            const unsigned char* st = smem + stage * S::STAGE_BYTES;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) b[j] = km_frag(st + A_BYTES, (128 * wn + 16 * j), lane);
+            for (int j = 0; j < TN; ++j) b[j] = km_frag(st + S::A_BYTES, (128 * wn + 16 * j), lane);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int tau = wm + WM * i;      // 16-row tile of the block
@@ -260,13 +286,13 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
             }
         };
         auto step = [&](int kt, const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb) {
-            wait_vm<4 * (STAGES - 3)>();
+            wait_vm<D * (STAGES - 3)>();
             __builtin_amdgcn_s_barrier();
             issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
             read_frags((kt + 1 < nk ? kt + 1 : kt) % STAGES, na, nb);
             mfmas(ca, cb);
         };
-        wait_vm<4 * (STAGES - 2)>();
+        wait_vm<D * (STAGES - 2)>();
         __builtin_amdgcn_s_barrier();
         read_frags(0, fa[0], fb[0]);
         int kt = 0;
@@ -278,62 +304,84 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         wait_vm<0>();
     }
 
-    // ---- epilogue: lane holds column (lane & 15), rows 4 (lane >> 4) + v ---
+    // ---- epilogue through LDS ---------------------------------------------
+    // An MFMA lane holds column lane & 15 of rows 4 (lane >> 4) + v: stored
+    // straight from registers, each instruction would write 64-byte pieces of
+    // 4 rows.  Instead the tile goes to LDS EPI_ROWS rows at a time (the
+    // operand stages are free by now), and each wave then writes whole rows
+    // with 16 bytes per lane.
+    constexpr int EPI_ROWS = S::EPI_ROWS;
+    constexpr int IPP = EPI_ROWS / 16 / WM;        // 16-row tiles of a wave per pass
     const int ccol = lane & 15, crow = (lane >> 4) * 4;
-    if (WGRAD) {
-        float* C = (float*)(extra ? p.C_extra : (float*)p.C + (int64_t)g * p.c_group_stride);
+    float* stage = (float*)smem;
+    __syncthreads();                              // every wave is done with the operand stages
+    const float L = extra ? p.limit_extra : p.limit;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+    for (int pass = 0; pass < BM / EPI_ROWS; ++pass) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = n_tile * BN + (128 * wn + 16 * j) + ccol;
+        for (int ii = 0; ii < IPP; ++ii) {
+            const int i = pass * IPP + ii;
+            const int lr0 = 16 * (wm + WM * ii) + crow;   // row within the pass
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = m_tile * BM + 16 * (wm + WM * i) + crow + v;
-                    if (m < p.M && col < p.N) C[(int64_t)m * p.ldc + col] = acc[i][j][v];
-                }
-            }
-    } else if (EPI == ACT) {
-        // dh (this tile's columns i of the N = I hidden units) -> dgu
-        const float L = extra ? p.limit_extra : p.limit;
-        uint16_t* D = (uint16_t*)p.C;
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i >= n_i) continue;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = n_tile * BN + (128 * wn + 16 * j) + ccol;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int lr = 16 * (wm + WM * i) + crow + v;
-                    if (lr < valid && col < p.N) {
-                        const int64_t r = row0 + lr;
-                        const float gv = bf16_to_f32(p.gu[r * 2 * p.N + col]);
-                        const float uv = bf16_to_f32(p.gu[r * 2 * p.N + p.N + col]);
-                        float dg, du;
-                        swiglu_clip_grad(gv, uv, L, dg, du);
-                        const float dh = acc[i][j][v];
-                        D[r * 2 * p.N + col] = f32_to_bf16(dh * dg);
-                        D[r * 2 * p.N + p.N + col] = f32_to_bf16(dh * du);
+                for (int v = 0; v < 4; ++v)
+                    stage[(lr0 + v) * EPI_PITCH + 128 * wn + 16 * j + ccol] = acc[i][j][v];
+        }
+        __syncthreads();
+        if (WGRAD || EPI == F32) {
+            // EPI_ROWS rows x 64 float4; thread t: float4 t % 64 of rows t / 64 + NW q
+            float* C = WGRAD ? (float*)(extra ? p.C_extra : (float*)p.C + (int64_t)g * p.c_group_stride)
+                             : (float*)p.C;
+            const int c4 = (tid & 63) * 4;
+            const int col = n_tile * BN + c4;
+#pragma unroll 4
+            for (int q = 0; q < EPI_ROWS / NW; ++q) {
+                const int pr = (tid >> 6) + NW * q;
+                const int lr = EPI_ROWS * pass + pr;
+                const float4 v = *(const float4*)&stage[pr * EPI_PITCH + c4];
+                if (col < p.N) {
+                    if (WGRAD) {
+                        const int m = m_tile * BM + lr;
+                        if (m < p.M) *(float4*)&C[(int64_t)m * p.ldc + col] = v;
+                    } else if (lr < valid) {
+                        *(float4*)&C[(int64_t)(row0 + lr) * p.ldc + col] = v;
                     }
                 }
             }
-        }
-    } else {
-        float* C = (float*)p.C;
+        } else {
+            // dh -> dgu: 8 columns per thread (16-byte loads of gu, stores of dgu)
+            uint16_t* Dg = (uint16_t*)p.C;
+            const int c8 = (tid & 31) * 8;
+            const int col = n_tile * BN + c8;
+#pragma unroll 2
+            for (int q = 0; q < EPI_ROWS * 32 / (NW * 64); ++q) {
+                const int pr = (tid >> 5) + (NW * 2) * q;
+                const int lr = EPI_ROWS * pass + pr;
+                if (lr < valid && col < p.N) {
+                    const int64_t r = row0 + lr;
+                    const float* sv = &stage[pr * EPI_PITCH + c8];
+                    const uint4 gq = *(const uint4*)(p.gu + r * 2 * p.N + col);
+                    const uint4 uq = *(const uint4*)(p.gu + r * 2 * p.N + p.N + col);
+                    const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, uw[4] = {uq.x, uq.y, uq.z, uq.w};
+                    uint32_t dg_out[4], du_out[4];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i >= n_i) continue;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = n_tile * BN + (128 * wn + 16 * j) + ccol;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int lr = 16 * (wm + WM * i) + crow + v;
-                    if (lr < valid && col < p.N) C[(int64_t)(row0 + lr) * p.ldc + col] = acc[i][j][v];
+                    for (int e = 0; e < 4; ++e) {
+                        float dg0, du0, dg1, du1;
+                        swiglu_clip_grad(bf16_to_f32((uint16_t)(gw[e] & 0xffff)),
+                                         bf16_to_f32((uint16_t)(uw[e] & 0xffff)), L, dg0, du0);
+                        swiglu_clip_grad(bf16_to_f32((uint16_t)(gw[e] >> 16)), bf16_to_f32((uint16_t)(uw[e] >> 16)),
+                                         L, dg1, du1);
+                        const float dh0 = sv[2 * e], dh1 = sv[2 * e + 1];
+                        dg_out[e] = pack_bf16x2(dh0 * dg0, dh1 * dg1);
+                        du_out[e] = pack_bf16x2(dh0 * du0, dh1 * du1);
+                    }
+                    *(uint4*)(Dg + r * 2 * p.N + col) = make_uint4(dg_out[0], dg_out[1], dg_out[2], dg_out[3]);
+                    *(uint4*)(Dg + r * 2 * p.N + p.N + col) = make_uint4(du_out[0], du_out[1], du_out[2], du_out[3]);
                 }
             }
         }
+        __syncthreads();                          // the next pass reuses the staging area
     }
 }
 
@@ -341,8 +389,8 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 // from the tile plan.  Each XCD (blocks b with b % 8 == x) takes a
 // contiguous range, so the blocks that share an operand share an L2.
 template <bool WGRAD, int EPI>
-__global__ __launch_bounds__(NT, 1) void kernel(Params p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * ((WGRAD ? KM_BYTES : KC_BYTES) + KM_BYTES)];
+__global__ __launch_bounds__(Tile<WGRAD>::NW * 64, 1) void kernel(Params p) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Tile<WGRAD>::SMEM];
     int total;
     if (WGRAD) total = (p.groups + (p.extra_rows > 0 ? 1 : 0)) * p.m_tiles * p.n_tiles;
     else total = p.tile_start[p.groups + (p.extra_rows > 0 ? 1 : 0)] * p.n_tiles;
@@ -365,8 +413,6 @@ static hipError_t launch(const BwdArgs& a, hipStream_t s) {
     p.ldb = a.ldb;
     p.b_group_stride = a.b_group_stride;
     p.B_extra = (const uint16_t*)a.B_extra;
-    p.b_rows = a.b_rows;
-    p.b_div = a.b_div > 0 ? a.b_div : 1;
     p.zero_row = (const uint16_t*)a.zero_row;
     p.C = a.C;
     p.ldc = a.ldc;
@@ -383,12 +429,12 @@ static hipError_t launch(const BwdArgs& a, hipStream_t s) {
     p.groups = a.groups;
     p.extra_rows = a.extra_rows;
     p.n_tiles = (a.N + BN - 1) / BN;
-    p.m_tiles = (a.M + BM - 1) / BM;
+    p.m_tiles = (a.M + Tile<WGRAD>::BM - 1) / Tile<WGRAD>::BM;
     int64_t items = WGRAD ? (int64_t)(a.groups + (a.extra_rows > 0 ? 1 : 0)) * p.m_tiles * p.n_tiles
                           : (int64_t)a.max_tiles * p.n_tiles;
     if (items <= 0) return hipSuccess;
     const int64_t blocks = (items + NXCD - 1) / NXCD * NXCD;
-    kernel<WGRAD, EPI><<<(unsigned)blocks, NT, 0, s>>>(p);
+    kernel<WGRAD, EPI><<<(unsigned)blocks, Tile<WGRAD>::NW * 64, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -344,7 +344,7 @@ SavedWs saved_ws(const Dims& d) {
 }
 
 struct BwdWs {
-    size_t plan, zero, dy, dgu, dxr, da, total;
+    size_t plan, zero, dy, dgu, dxr, da, xp, total;
 };
 BwdWs bwd_ws(const Dims& d) {
     const int64_t rows = train_rows(d);
@@ -356,6 +356,7 @@ BwdWs bwd_ws(const Dims& d) {
     B.dgu = o;   o += align_up((size_t)rows * 2 * d.I * 2);
     B.dxr = o;   o += align_up((size_t)rows * d.H * 4);
     B.da = o;    o += align_up((size_t)d.P * 4);
+    B.xp = o;    o += align_up((size_t)rows * d.H * 2);   // x rows in row order
     B.total = o;
     return B;
 }
@@ -711,10 +712,8 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, int64_t T, const void* 
     moe::BwdArgs g1 = g2;
     g1.A = base + B.dgu;
     g1.lda = 2 * d.I;
-    g1.B = x;
+    g1.B = base + B.xp;
     g1.ldb = d.H;
-    g1.b_rows = r2p;
-    g1.b_div = d.k;
     g1.C = dw13;
     g1.ldc = d.H;
     g1.c_group_stride = (int64_t)2 * d.I * d.H;
@@ -722,6 +721,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, int64_t T, const void* 
     g1.M = 2 * d.I;
     g1.N = d.H;
     HIP_TRY(moe::launch_bwd_wgrad(g2, stream));
+    HIP_TRY(moe::launch_gather_rows(x, r2p, shared, base + B.xp, (int)T, d.H, d.k, stream));
     HIP_TRY(moe::launch_bwd_wgrad(g1, stream));
     HIP_TRY(moe::launch_bwd_router_wgrad(da, offsets, r2p, x, dw_router, d.E, d.H, d.k, stream));
     return MOE_OK;

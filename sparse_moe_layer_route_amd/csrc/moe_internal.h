@@ -107,8 +107,6 @@ struct BwdArgs {
     int64_t ldb = 0;
     int64_t b_group_stride = 0;
     const void* B_extra = nullptr;
-    const int32_t* b_rows = nullptr;
-    int b_div = 1;
     const void* zero_row = nullptr;
     void* C = nullptr;
     int64_t ldc = 0;
@@ -140,5 +138,9 @@ hipError_t launch_bwd_dx(const float* dxr, const int32_t* p2r, const float* da, 
 hipError_t launch_bwd_router_wgrad(const float* da, const int32_t* offsets, const int32_t* r2p, const void* x,
                                    float* dwg, int E, int H, int k, hipStream_t s);
 hipError_t launch_zero_u32(void* p, int64_t words, hipStream_t s);
+// x rows in the permuted row order: row r < P is x[r2p[r] / k], row P + t is
+// x[t] when shared (bf16, H % 8 == 0)
+hipError_t launch_gather_rows(const void* x, const int32_t* r2p, bool shared, void* out, int T, int H, int k,
+                              hipStream_t s);
 
 }  // namespace moe
