@@ -72,7 +72,9 @@ struct Shape {
     static constexpr int STAGES = BM == 256 ? 4 : 6;
 };
 
-enum { SWIGLU = 0, OUT_F16 = 1, OUT_F32 = 2 };
+// SWIGLU_SAVE: SWIGLU that also writes the pre-activations (gu_out)
+enum { SWIGLU = 0, OUT_F16 = 1, OUT_F32 = 2, SWIGLU_SAVE = 3 };
+constexpr bool is_swiglu(int mode) { return mode == SWIGLU || mode == SWIGLU_SAVE; }
 
 struct Params {
     const uint16_t* A;          // bf16 activations
@@ -233,7 +235,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         const int blk = B_PER_WAVE * wave + q;            // 0 .. NB-1
         const int r = block_row(blk);                     // tile column 0..255
         int wrow;
-        if (MODE == SWIGLU) {
+        if (is_swiglu(MODE)) {
             // each wave's GW columns: GW/2 gate columns, then the matching GW/2 up columns
             const int grp = r / S::GW, u = r % S::GW;
             const int hcol = min(n_tile * (BN / 2) + (S::GW / 2) * grp + u % (S::GW / 2), p.N - 1);
@@ -327,7 +329,65 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 
     // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + v ---
     const int ccol = lane & 15, crow = (lane >> 4) * 4;
-    if (MODE == SWIGLU) {
+    if (BM == 256 && MODE != SWIGLU_SAVE) {
+        // Through LDS, 128 rows at a time (the operand stages are free by
+        // now): each thread then writes 16 contiguous bytes of a row, where
+        // stores straight from the MFMA layout would move 2 or 4 bytes each.
+        constexpr int OUT_COLS = MODE == SWIGLU ? BN / 2 : BN;     // output columns of the tile
+        constexpr int PITCH = OUT_COLS + 4;                         // fp32, 16-byte skew per row
+        constexpr int CW = MODE == SWIGLU ? S::GW / 2 : S::GW;     // output columns per wave
+        float* stage = (float*)smem;
+        __syncthreads();
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * pass + ii;
+                const int pr0 = 16 * (wm + S::WM * ii) + crow;       // row within the pass
+#pragma unroll
+                for (int j = 0; j < (MODE == SWIGLU ? TN / 2 : TN); ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float o = MODE == SWIGLU ? swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit)
+                                                       : acc[i][j][v];
+                        stage[(pr0 + v) * PITCH + CW * wn + 16 * j + ccol] = o;
+                    }
+            }
+            __syncthreads();
+            constexpr int CHUNK = MODE == OUT_F32 ? 4 : 8;                 // values per 16-byte store
+            constexpr int PER_ROW = OUT_COLS / CHUNK;
+            const int c = (tid % PER_ROW) * CHUNK;
+            const int col = n_tile * OUT_COLS + c;
+#pragma unroll 4
+            for (int q = 0; q < 128 * PER_ROW / NT; ++q) {
+                const int pr = tid / PER_ROW + (NT / PER_ROW) * q;
+                const int lr = 128 * pass + pr;
+                if (lr < valid && col < p.N) {
+                    const float* sv = &stage[pr * PITCH + c];
+                    const int64_t r = row0 + lr;
+                    if (MODE == OUT_F32) {
+                        *(float4*)((float*)p.C + r * p.N + col) = *(const float4*)sv;
+                    } else if (MODE == OUT_F16) {
+                        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+                        f16x8 h8;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) h8[e] = f32_to_f16_sat(sv[e]);
+                        *(f16x8*)((_Float16*)p.C + r * p.N + col) = h8;
+                    } else {
+                        uint4 b;
+                        b.x = pack_bf16x2(sv[0], sv[1]);
+                        b.y = pack_bf16x2(sv[2], sv[3]);
+                        b.z = pack_bf16x2(sv[4], sv[5]);
+                        b.w = pack_bf16x2(sv[6], sv[7]);
+                        *(uint4*)((uint16_t*)p.C + r * p.N + col) = b;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    if (is_swiglu(MODE)) {
         uint16_t* H = (uint16_t*)p.C;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -340,7 +400,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                     const int lr = 16 * (wm + S::WM * i) + crow + v;
                     if (lr < valid && hcol < p.N) {
                         const int64_t r = row0 + lr;
-                        if (p.gu_out) {
+                        if (MODE == SWIGLU_SAVE) {
                             // kept for the backward; the activation uses the same rounded values
                             const uint16_t gq = f32_to_bf16(acc[i][j][v]);
                             const uint16_t uq = f32_to_bf16(acc[i][j + TN / 2][v]);
@@ -383,7 +443,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 template <int MODE, bool GROUPED, int BM, int BN>
 __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     using S = Shape<BM, BN>;
-    static_assert(MODE != SWIGLU || S::TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
+    static_assert(!is_swiglu(MODE) || S::TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S::STAGES * S::STAGE_BYTES];
     const Segments sg = segments<GROUPED, BM>(p);
     const int xcd = blockIdx.x % NXCD, slots = gridDim.x / NXCD;
@@ -411,7 +471,7 @@ static int grid_blocks(int64_t work) {
 
 template <int MODE, int BM, int BN>
 void launch(Params p, int64_t tiles, hipStream_t s) {
-    p.n_tiles = MODE == SWIGLU ? (2 * p.N + BN - 1) / BN : (p.N + BN - 1) / BN;
+    p.n_tiles = is_swiglu(MODE) ? (2 * p.N + BN - 1) / BN : (p.N + BN - 1) / BN;
     const int nb = grid_blocks(tiles * p.n_tiles);
     if (p.offsets) kernel<MODE, true, BM, BN><<<nb, NT, 0, s>>>(p);
     else kernel<MODE, false, BM, BN><<<nb, NT, 0, s>>>(p);
@@ -447,8 +507,13 @@ hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s) {
     p.gu_out = (uint16_t*)a.gu_out;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
-    if (a.bm == 64) gg::launch<gg::SWIGLU, 64, 256>(p, tiles, s);
-    else gg::launch<gg::SWIGLU, 256, 256>(p, tiles, s);
+    if (a.gu_out) {
+        if (a.bm == 64) gg::launch<gg::SWIGLU_SAVE, 64, 256>(p, tiles, s);
+        else gg::launch<gg::SWIGLU_SAVE, 256, 256>(p, tiles, s);
+    } else {
+        if (a.bm == 64) gg::launch<gg::SWIGLU, 64, 256>(p, tiles, s);
+        else gg::launch<gg::SWIGLU, 256, 256>(p, tiles, s);
+    }
     return hipGetLastError();
 }
 
