@@ -192,7 +192,7 @@ def main():
         note(f"{wl.name} as a block: RMSNorm in front, fp32 residual add in the combine")
         res["block"] = time_block(args, wl, moe, torch, mi)
 
-    if not args.no_train:
+    if not args.no_train and cfg.expert_dtype == "bf16":
         note(f"{wl.name} training step: moe_layer_forward_train + moe_layer_backward")
         res["train"] = time_train(args, wl, moe, torch, mi)
 
