@@ -42,9 +42,6 @@ namespace moe {
 namespace gg {
 
 constexpr int BK = 32;
-constexpr int NW = 8;                 // waves per block
-constexpr int NT = NW * 64;           // threads per block
-constexpr int TM = 4;                 // 16-row tiles per wave
 // One DMA block is 16 rows x 64 B.  The 4 blocks of a 64-row group start at
 // these byte offsets: 16-byte bank groups 0, 2, 16, 18 (mod 32), which makes
 // every 32-lane pass of a fragment read touch 32 distinct bank groups.
@@ -61,8 +58,11 @@ constexpr int NXCD = 8;
 //     last round on 256 CUs.
 template <int BM, int BN>
 struct Shape {
+    static constexpr int NW = 8;                       // waves per block
+    static constexpr int NT = NW * 64;                 // threads per block
     static constexpr int WM = BM / 64;                 // waves along M
     static constexpr int WN = NW / WM;                 // waves along N
+    static constexpr int TM = BM / 16 / WM;            // 16-row tiles per wave
     static constexpr int TN = BN / 16 / WN;            // 16-col tiles per wave
     static constexpr int GW = BN / WN;                 // columns per wave
     static constexpr int NA = BM / 16;                 // A DMA blocks per slice
@@ -70,6 +70,10 @@ struct Shape {
     static constexpr int A_OPERAND = (BM / 64) * GROUP;
     static constexpr int STAGE_BYTES = A_OPERAND + (BN / 64) * GROUP;
     static constexpr int STAGES = BM == 256 ? 4 : 6;
+    // epilogue staging through LDS (BM 256): rows per pass
+    static constexpr int EPI_ROWS = 128;
+    static constexpr int SMEM = STAGES * STAGE_BYTES > EPI_ROWS * (BN + 4) * 4 ? STAGES * STAGE_BYTES
+                                                                              : EPI_ROWS * (BN + 4) * 4;
 };
 
 // SWIGLU_SAVE: SWIGLU that also writes the pre-activations (gu_out)
@@ -144,7 +148,8 @@ __device__ __forceinline__ Segments segments(const Params& p) {
 template <int MODE, bool GROUPED, int BM, int BN>
 __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* smem) {
     using S = Shape<BM, BN>;
-    constexpr int STAGES = S::STAGES, STAGE_BYTES = S::STAGE_BYTES, TN = S::TN;
+    constexpr int STAGES = S::STAGES, STAGE_BYTES = S::STAGE_BYTES, TN = S::TN, TM = S::TM, NW = S::NW,
+                  NT = S::NT;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -278,10 +283,11 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: slices 0 .. STAGES-2 in flight (clamped re-reads past the end
-    // keep the per-step DMA count fixed, which the waits below rely on)
+    // prologue: slices 0 .. STAGES-1 in flight, one per stage (clamped re-reads
+    // past the end keep the per-step DMA count fixed, which the waits below
+    // rely on)
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(min(s, nk - 1), s);
+    for (int s = 0; s < STAGES; ++s) issue(min(s, nk - 1), s);
 
     // fragments of one slice, double-buffered in registers: the LDS reads of
     // slice kt+1 are issued before the MFMAs of slice kt, so they overlap
@@ -306,19 +312,22 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     };
     // DMAs per slice of this wave: B_PER_WAVE + A_PER_WAVE if it moves A blocks
     constexpr int D_HI = B_PER_WAVE + A_PER_WAVE, D_LO = B_PER_WAVE;
-    // one step: slice kt's fragments are in registers (cur); make slice kt+1
-    // visible, refill the stage slice kt-1 used, read slice kt+1 (nxt), multiply
+    // one step: slice kt's fragments are in registers (cur), so its stage is
+    // free: refill it with slice kt+STAGES, make slice kt+1 visible, read it
+    // (nxt), multiply slice kt.  Slices kt+1 .. kt+STAGES occupy the stages,
+    // so each DMA has STAGES-1 steps to land.
     auto step = [&](int kt, const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb) {
-        // slices kt+2 .. kt+STAGES-2 may stay in flight
-        if (a_mine) wait_vm<D_HI * (STAGES - 3)>(); else wait_vm<D_LO * (STAGES - 3)>();
+        // slices kt+2 .. kt+STAGES-1 may stay in flight; this wave's reads of
+        // slice kt have completed (its stage is refilled after the barrier)
+        if (a_mine) wait_vm<D_HI * (STAGES - 2)>(); else wait_vm<D_LO * (STAGES - 2)>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0), vmcnt/expcnt untouched
         __builtin_amdgcn_s_barrier();
-        // every wave finished reading slice kt-1 (its MFMAs waited for them)
-        issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
+        issue(min(kt + STAGES, nk - 1), kt % STAGES);
         read_frags((kt + 1 < nk ? kt + 1 : kt) % STAGES, na, nb);
         mfmas(ca, cb);
     };
 
-    if (a_mine) wait_vm<D_HI * (STAGES - 2)>(); else wait_vm<D_LO * (STAGES - 2)>();
+    if (a_mine) wait_vm<D_HI * (STAGES - 1)>(); else wait_vm<D_LO * (STAGES - 1)>();
     __builtin_amdgcn_s_barrier();
     read_frags(0, fa[0], fb[0]);
     for (int kt = 0; kt < nk; kt += 2) {
@@ -329,61 +338,81 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 
     // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + v ---
     const int ccol = lane & 15, crow = (lane >> 4) * 4;
-    if (BM == 256 && MODE != SWIGLU_SAVE) {
-        // Through LDS, 128 rows at a time (the operand stages are free by
+    if (BM == 256) {
+        // Through LDS, EPI_ROWS rows at a time (the operand stages are free by
         // now): each thread then writes 16 contiguous bytes of a row, where
         // stores straight from the MFMA layout would move 2 or 4 bytes each.
-        constexpr int OUT_COLS = MODE == SWIGLU ? BN / 2 : BN;     // output columns of the tile
+        // SWIGLU_SAVE stages three planes in turn: h, then the gate and up
+        // pre-activations it keeps (h is computed from their bf16 values).
+        constexpr bool SW = is_swiglu(MODE);
+        constexpr int OUT_COLS = SW ? BN / 2 : BN;                  // output columns of the tile
         constexpr int PITCH = OUT_COLS + 4;                         // fp32, 16-byte skew per row
-        constexpr int CW = MODE == SWIGLU ? S::GW / 2 : S::GW;     // output columns per wave
+        constexpr int CW = SW ? S::GW / 2 : S::GW;                 // output columns per wave
+        constexpr int EPI_ROWS = S::EPI_ROWS;
+        constexpr int IPP = EPI_ROWS / 16 / S::WM;                  // 16-row tiles of a wave per pass
+        constexpr int PLANES = MODE == SWIGLU_SAVE ? 3 : 1;
         float* stage = (float*)smem;
         __syncthreads();
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
+        for (int pass = 0; pass < BM / EPI_ROWS; ++pass) {
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                const int i = 2 * pass + ii;
-                const int pr0 = 16 * (wm + S::WM * ii) + crow;       // row within the pass
+            for (int plane = 0; plane < PLANES; ++plane) {
 #pragma unroll
-                for (int j = 0; j < (MODE == SWIGLU ? TN / 2 : TN); ++j)
+                for (int ii = 0; ii < IPP; ++ii) {
+                    const int i = IPP * pass + ii;
+                    const int pr0 = 16 * (wm + S::WM * ii) + crow;   // row within the pass
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float o = MODE == SWIGLU ? swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit)
-                                                       : acc[i][j][v];
-                        stage[(pr0 + v) * PITCH + CW * wn + 16 * j + ccol] = o;
-                    }
-            }
-            __syncthreads();
-            constexpr int CHUNK = MODE == OUT_F32 ? 4 : 8;                 // values per 16-byte store
-            constexpr int PER_ROW = OUT_COLS / CHUNK;
-            const int c = (tid % PER_ROW) * CHUNK;
-            const int col = n_tile * OUT_COLS + c;
+                    for (int j = 0; j < (SW ? TN / 2 : TN); ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            float o;
+                            if (MODE == SWIGLU) {
+                                o = swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit);
+                            } else if (MODE == SWIGLU_SAVE) {
+                                // kept for the backward; the activation uses the same rounded values
+                                const float gq = bf16_to_f32(f32_to_bf16(acc[i][j][v]));
+                                const float uq = bf16_to_f32(f32_to_bf16(acc[i][j + TN / 2][v]));
+                                o = plane == 0 ? swiglu_clip(gq, uq, limit) : (plane == 1 ? gq : uq);
+                            } else {
+                                o = acc[i][j][v];
+                            }
+                            stage[(pr0 + v) * PITCH + CW * wn + 16 * j + ccol] = o;
+                        }
+                }
+                __syncthreads();
+                constexpr int CHUNK = MODE == OUT_F32 ? 4 : 8;             // values per 16-byte store
+                constexpr int PER_ROW = OUT_COLS / CHUNK;
+                const int c = (tid % PER_ROW) * CHUNK;
+                const int col = n_tile * OUT_COLS + c;
 #pragma unroll 4
-            for (int q = 0; q < 128 * PER_ROW / NT; ++q) {
-                const int pr = tid / PER_ROW + (NT / PER_ROW) * q;
-                const int lr = 128 * pass + pr;
-                if (lr < valid && col < p.N) {
-                    const float* sv = &stage[pr * PITCH + c];
-                    const int64_t r = row0 + lr;
-                    if (MODE == OUT_F32) {
-                        *(float4*)((float*)p.C + r * p.N + col) = *(const float4*)sv;
-                    } else if (MODE == OUT_F16) {
-                        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-                        f16x8 h8;
+                for (int q = 0; q < EPI_ROWS * PER_ROW / NT; ++q) {
+                    const int pr = tid / PER_ROW + (NT / PER_ROW) * q;
+                    const int lr = EPI_ROWS * pass + pr;
+                    if (lr < valid && col < p.N) {
+                        const float* sv = &stage[pr * PITCH + c];
+                        const int64_t r = row0 + lr;
+                        if (MODE == OUT_F32) {
+                            *(float4*)((float*)p.C + r * p.N + col) = *(const float4*)sv;
+                        } else if (MODE == OUT_F16) {
+                            typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+                            f16x8 h8;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) h8[e] = f32_to_f16_sat(sv[e]);
-                        *(f16x8*)((_Float16*)p.C + r * p.N + col) = h8;
-                    } else {
-                        uint4 b;
-                        b.x = pack_bf16x2(sv[0], sv[1]);
-                        b.y = pack_bf16x2(sv[2], sv[3]);
-                        b.z = pack_bf16x2(sv[4], sv[5]);
-                        b.w = pack_bf16x2(sv[6], sv[7]);
-                        *(uint4*)((uint16_t*)p.C + r * p.N + col) = b;
+                            for (int e = 0; e < 8; ++e) h8[e] = f32_to_f16_sat(sv[e]);
+                            *(f16x8*)((_Float16*)p.C + r * p.N + col) = h8;
+                        } else {
+                            uint4 b;
+                            b.x = pack_bf16x2(sv[0], sv[1]);
+                            b.y = pack_bf16x2(sv[2], sv[3]);
+                            b.z = pack_bf16x2(sv[4], sv[5]);
+                            b.w = pack_bf16x2(sv[6], sv[7]);
+                            uint16_t* dst = plane == 0 ? (uint16_t*)p.C + r * p.N + col
+                                                       : p.gu_out + r * 2 * p.N + (plane == 2 ? p.N : 0) + col;
+                            *(uint4*)dst = b;
+                        }
                     }
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
         return;
     }
@@ -441,10 +470,10 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 // kernel traces.  Block (xcd, slot) runs the items at slots slot, slot +
 // slots, ... of its XCD's ranges (one item when the grid covers them).
 template <int MODE, bool GROUPED, int BM, int BN>
-__global__ __launch_bounds__(NT, 1) void kernel(Params p) {
+__global__ __launch_bounds__((Shape<BM, BN>::NT), 1) void kernel(Params p) {
     using S = Shape<BM, BN>;
     static_assert(!is_swiglu(MODE) || S::TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::STAGES * S::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
     const Segments sg = segments<GROUPED, BM>(p);
     const int xcd = blockIdx.x % NXCD, slots = gridDim.x / NXCD;
     for (int s = blockIdx.x / NXCD; s < sg.per1 + sg.per2; s += slots) {
@@ -473,8 +502,8 @@ template <int MODE, int BM, int BN>
 void launch(Params p, int64_t tiles, hipStream_t s) {
     p.n_tiles = is_swiglu(MODE) ? (2 * p.N + BN - 1) / BN : (p.N + BN - 1) / BN;
     const int nb = grid_blocks(tiles * p.n_tiles);
-    if (p.offsets) kernel<MODE, true, BM, BN><<<nb, NT, 0, s>>>(p);
-    else kernel<MODE, false, BM, BN><<<nb, NT, 0, s>>>(p);
+    if (p.offsets) kernel<MODE, true, BM, BN><<<nb, Shape<BM, BN>::NT, 0, s>>>(p);
+    else kernel<MODE, false, BM, BN><<<nb, Shape<BM, BN>::NT, 0, s>>>(p);
 }
 
 }  // namespace gg
