@@ -7,8 +7,9 @@
 // h = act(gate, up, L) in bf16 (clipped SwiGLU).  Mode F16 / F32 (second
 // projection, shared expert): plain output.
 //
-// Block tile: 256 rows x 256 weight rows, K in slices of 32, 8 waves (two
-// per SIMD) as 4 along M x 2 along N, each wave 64 rows x 128 columns of
+// Block tile (rows x weight rows): 256 x 256 for batches with many rows per
+// expert, 64 x 256 / 64 x 128 for few.  8 waves (two per SIMD); 256-row
+// tiles as 4 along M x 2 along N, each wave 64 rows x 128 columns of
 // 16x16x32 bf16 MFMA tiles.  Choices, each measured on MI355X:
 //   * Operands go global -> LDS by direct DMA (global_load_lds_dwordx4), so
 //     no registers stage them.  The DMA is issued from inline asm and its
@@ -16,24 +17,28 @@
 //     barrier of the step that reads it): the compiler cannot tell which LDS
 //     reads depend on which DMA and would otherwise wait for all of them at
 //     every step.  The instruction has no destination register.
-//   * Address pattern: each group of 4 lanes reads 64 contiguous bytes of
-//     one row (16 rows per instruction).  Spreading 16 lanes over 16 rows
-//     instead ran the address unit at a quarter of this rate (17 vs 61
-//     B/clk per CU on L2-resident data).
-//   * LDS: a DMA block lands lane-consecutive (16 rows x 64 B); the 4 blocks
-//     of a 64-row group sit at offsets chosen so that the MFMA fragment
-//     reads (lane l: row l & 15, 16 bytes of chunk l >> 4) are free of bank
-//     conflicts in the LDS's 32-lane passes.
-//   * 4 LDS stages; the fragments of slice k+1 are read into registers
-//     while the MFMAs of slice k run.
+//   * 256-row tiles: K slices of 64, each DMA instruction 8 rows x 128 B
+//     (whole lines), A in 2 LDS stages and W in 3 (160 KiB, no padding: an
+//     XOR swizzle of the 16-byte chunks keeps the fragment reads free of
+//     bank conflicts).  Each half slice's MFMAs run in four groups with this
+//     wave's DMAs and next fragment reads between them; issued as one burst
+//     after the barrier they held back the MFMAs (2.58 -> 2.43 ms for the
+//     Step-5 prefill's first projection).
+//   * 64-row tiles: K slices of 32, each DMA instruction 16 rows x 64 B
+//     (4 lanes per row: spreading 16 lanes over 16 rows ran the address unit
+//     at a quarter of the rate), 6 padded stages whose block offsets keep the
+//     fragment reads (lane l: row l & 15, 16 bytes of chunk l >> 4) free of
+//     bank conflicts.
+//   * The fragments of the next (half) slice are read into registers while
+//     the MFMAs of the current one run.
 //   * 16-row tiles are dealt to the waves along M round-robin (tile t to
-//     wave t % 4), so an expert's valid rows spread evenly over the SIMDs;
+//     wave t % WM), so an expert's valid rows spread evenly over the SIMDs;
 //     tiles past the expert's last row skip their MFMAs.
 //   * A rows are gathered straight from x by the DMA (row_to_pair / k); no
 //     permuted copy of x is written.
-//   * Work order: (expert, n-tile, m-tile) with m fastest, so the m-tiles of
-//     one expert's weight panel run together and share it in L2; each XCD
-//     (blocks b with b % 8 == x) takes a contiguous range of that list.
+//   * Work order: (expert, m-tile, n-tile) with n fastest, so the n-tiles
+//     that read one m-tile's gathered rows run together; each XCD (blocks b
+//     with b % 8 == x) takes a contiguous range of that list.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -41,7 +46,8 @@ namespace moe {
 
 namespace gg {
 
-constexpr int BK = 32;
+constexpr int BK = 32;    // K slice of the 64-row tiles
+constexpr int BK2 = 64;   // K slice of the 256-row tiles
 // One DMA block is 16 rows x 64 B.  The 4 blocks of a 64-row group start at
 // these byte offsets: 16-byte bank groups 0, 2, 16, 18 (mod 32), which makes
 // every 32-lane pass of a fragment read touch 32 distinct bank groups.
@@ -72,8 +78,10 @@ struct Shape {
     static constexpr int STAGES = BM == 256 ? 4 : 6;
     // epilogue staging through LDS (BM 256): rows per pass
     static constexpr int EPI_ROWS = 128;
-    static constexpr int SMEM = STAGES * STAGE_BYTES > EPI_ROWS * (BN + 4) * 4 ? STAGES * STAGE_BYTES
-                                                                              : EPI_ROWS * (BN + 4) * 4;
+    // operand LDS: 256-row tiles hold A in 2 and W in 3 stages of K 64
+    // (128 B per row); 64-row tiles STAGES stages of K 32
+    static constexpr int OPER = BM == 256 ? 2 * BM * 128 + 3 * BN * 128 : STAGES * STAGE_BYTES;
+    static constexpr int SMEM = OPER > EPI_ROWS * (BN + 4) * 4 ? OPER : EPI_ROWS * (BN + 4) * 4;
 };
 
 // SWIGLU_SAVE: SWIGLU that also writes the pre-activations (gu_out)
@@ -113,6 +121,11 @@ __device__ __forceinline__ void dma_frag(const void* g, unsigned lds_off) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g) : "memory");
 }
 
+// the same from a wave-uniform 64-bit base plus this lane's 32-bit byte offset
+__device__ __forceinline__ void dma_frag_s(const void* base, unsigned off, unsigned lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(off), "s"(base) : "memory");
+}
+
 // wait until at most n vector-memory operations of this wave are outstanding
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -120,7 +133,7 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// Work items: grouped, (group, n-tile, m-tile) with m fastest, from the
+// Work items: grouped, (group, m-tile, n-tile) with n fastest, from the
 // tile plan; dense, (n-tile, m-tile).  The routed items and the extra
 // group's are two segments; each is cut into 8 contiguous ranges, one per XCD
 // (block b runs on XCD b % 8), so every XCD gets an equal share of both and
@@ -168,12 +181,11 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         g = lo;
         const int mt = p.tile_start[g + 1] - p.tile_start[g];
         const int local = w - p.tile_start[g] * p.n_tiles;
-        n_tile = local / mt;
-        m_tile = local % mt;
+        m_tile = local / p.n_tiles;
+        n_tile = local % p.n_tiles;
         // the group's rows are split evenly over its mt tiles (each at most
         // BM rows, as mt = ceil(rows / BM)): the m-tiles of one weight panel
-        // then do the same work and stream the panel in step, so they share
-        // it in L2 instead of each reading it from HBM
+        // then do the same work at the same pace
         const int base = p.offsets[g];
         const int cnt = (g < p.groups ? p.offsets[g + 1] : base + p.extra_rows) - base;
         row0 = base + (int)(((int64_t)m_tile * cnt) / mt);
@@ -196,9 +208,201 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     // spread over the channels (measured: 5.0 -> 6.4 TB/s for this DMA
     // pattern).  One rotation per expert (per n-tile when dense) keeps the
     // blocks that share an A tile (grouped) or a weight panel (dense) in step.
-    const int nk = K / BK;                      // even: K % 64 == 0
+    // K slices: 64 (128 B of a row) for 256-row tiles, 32 for 64-row tiles
+    const int nk = K / (BM == 256 ? BK2 : BK);   // K % 64 == 0
     const int rot = (GROUPED ? (g + 1) * 37 : (n_tile + 1) * 37) % nk;
 
+    // valid 16-row tiles of this wave: tiles wm + WM i with 16 (wm + WM i) < valid
+    const int ntile_valid = (valid + 15) >> 4;
+    int n_i = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) n_i += (wm + S::WM * i < ntile_valid) ? 1 : 0;
+    n_i = __builtin_amdgcn_readfirstlane(n_i);
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if constexpr (BM == 256) {
+        // ---- 256-row tiles: K slices of 64, whole 128-byte lines per DMA ----
+        // One DMA instruction moves 8 rows x 128 B: lanes 8q .. 8q+7 read the
+        // 128-byte line of row q, so every request is a whole line (half the
+        // L2 requests of 64-byte pieces for the same bytes).  A block lands at
+        // LDS byte 16 l per lane l, i.e. rows of 128 B back to back; lane l
+        // reads the line's 16-byte chunk (l & 7) ^ swz(row), so LDS chunk p of
+        // a row holds global chunk p ^ swz(row), with swz(row) = 2 ((row & 15)
+        // >> 2).  A fragment read (lane l: row l & 15 of a 16-row tile, K
+        // chunk 4 sub + (l >> 4)) then touches 32 distinct 16-byte bank groups
+        // in each 32-lane pass.  LDS: A in 2 stages, W in 3 (W is the operand
+        // that streams from HBM, so it gets the longer lead), 160 KiB.
+        // Wave w moves A blocks 4w .. 4w+3 (rows 32w .. 32w+31) and W blocks
+        // 4w .. 4w+3 of every slice.
+        constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+        constexpr int NQA = BM / 8 / NW, NQB = BN / 8 / NW;      // DMA blocks per wave
+        const int dq = lane >> 3;                                 // row within the DMA block
+        // A blocks of a wave whose rows all lie past the valid ones are not
+        // moved (their tiles are not multiplied; a 16-row tile that is only
+        // partly valid reads clamped copies, or stale LDS for rows of a block
+        // not moved, which only reach output rows that are not written)
+        const bool a_mine = 32 * wave < valid;
+        // sources as 32-bit byte offsets from a wave-uniform base (gathered
+        // rows: all of A, which the launch checks is under 4 GiB; otherwise
+        // the tile's first row)
+        const bool gather = GROUPED && p.a_rows;
+        const uint16_t* a_base = gather ? p.A : p.A + (int64_t)row0 * K;
+        unsigned a_off[NQA];
+#pragma unroll
+        for (int q = 0; q < NQA; ++q) {
+            const int r = 8 * (NQA * wave + q) + dq;              // tile row 0..255
+            const int c = (lane & 7) ^ (2 * ((r & 15) >> 2));
+            int ar = min(r, valid - 1);
+            if (gather) {
+                ar += row0;
+                ar = extra ? ar - p.offsets[p.groups] : p.a_rows[ar] / p.a_div;
+                ar = min(max(ar, 0), p.a_nrows - 1);
+            }
+            a_off[q] = (unsigned)ar * (unsigned)(2 * K) + 16u * c;
+        }
+        // W rows of this wave's DMA q: wave-uniform w_add + min(w_base + 8 q +
+        // dq, w_last), computed at each DMA from two lane values (the four
+        // offsets would hold registers through the loop).  SwiGLU: the wave's
+        // 32 columns of a slice are gate rows (waves 4g, 4g+1 of column group
+        // g) or the matching up rows (4g+2, 4g+3).
+        int w_add, w_base, w_last;
+        if (is_swiglu(MODE)) {
+            w_add = (wave & 3) < 2 ? 0 : p.N;
+            w_base = n_tile * (BN / 2) + (S::GW / 2) * (8 * NQB * wave / S::GW) + 32 * (wave & 1);
+            w_last = p.N - 1;
+        } else {
+            w_add = 0;
+            w_base = n_tile * BN + 32 * wave;
+            w_last = p.N - 1;
+        }
+        static_assert(NQB == 4 && S::GW == 128, "the W row formula assumes 32 columns per wave and slice");
+        const unsigned b_chunk = 16u * ((lane & 7) ^ (2 * (dq >> 2)));   // chunk of even q; odd q: ^ 64
+        auto b_off = [&](int q) {
+            const int wrow = w_add + min(w_base + 8 * q + dq, w_last);
+            return (unsigned)wrow * (unsigned)(2 * K) + (b_chunk ^ (64u * (q & 1)));
+        };
+        const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
+        auto issue_a = [&](int kt, int stage) {
+            const int ks = kt + rot < nk ? kt + rot : kt + rot - nk;
+            const unsigned sb = lds_base + stage * A_BYTES + NQA * wave * 1024;
+            if (a_mine) {
+#pragma unroll
+                for (int q = 0; q < NQA; ++q)
+                    dma_frag_s(a_base + ks * BK2, a_off[q], __builtin_amdgcn_readfirstlane(sb + 1024 * q));
+            }
+        };
+        auto issue_b = [&](int kt, int stage) {
+            const int ks = kt + rot < nk ? kt + rot : kt + rot - nk;
+            const unsigned sb = lds_base + 2 * A_BYTES + stage * B_BYTES + NQB * wave * 1024;
+#pragma unroll
+            for (int q = 0; q < NQB; ++q)
+                dma_frag_s(Wg + ks * BK2, b_off(q), __builtin_amdgcn_readfirstlane(sb + 1024 * q));
+        };
+        // lane's byte offset in a 16-row tile for K chunk 4 sub + (lane >> 4)
+        const int fr = lane & 15, sw = 2 * (fr >> 2);
+        const unsigned off0 = 128 * fr + 16 * ((lane >> 4) ^ sw);
+        const unsigned off1 = off0 ^ 64u;         // chunk 4 + c: (c ^ sw) ^ 4
+        bf16x8 xa[TM], xb[TN], ya[TM], yb[TN];
+        auto read_frags = [&](int kt, unsigned off, bf16x8* a, bf16x8* b) {
+            const unsigned char* sa = smem + (kt & 1) * A_BYTES;
+            const unsigned char* sb = smem + 2 * A_BYTES + (kt % 3) * B_BYTES;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8*)(sb + 2048 * (wn * TN + j) + off);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off);
+        };
+        // Slice kt's A sits in stage kt % 2, its W in stage kt % 3.  Step kt
+        // multiplies the slice's two K halves; between them (its reads done,
+        // slice kt+1 landed) the barrier frees its stages, which take A of
+        // kt+2 and W of kt+3 (clamped re-reads past the end keep the DMA count
+        // per step fixed, which the waits rely on).  DMAs complete in order and
+        // the last ones issued before step kt's wait are the previous step's
+        // A of kt+1, then W of kt+2: at most NQB outstanding means A and W of
+        // slice kt+1 have landed.
+        issue_a(0, 0);
+        issue_b(0, 0);
+        issue_a(min(1, nk - 1), 1);
+        issue_b(min(1, nk - 1), 1);
+        issue_b(min(2, nk - 1), 2);
+        if (a_mine) wait_vm<2 * NQB + NQA>(); else wait_vm<2 * NQB>();
+        __builtin_amdgcn_s_barrier();
+        read_frags(0, off0, xa, xb);
+        // Each half step runs its MFMAs in TM groups (one 16-row tile each)
+        // and puts this wave's memory instructions between the groups: the
+        // LDS reads of the other half's fragments, and after the barrier two
+        // DMAs per group (A in the first half of the groups, W in the
+        // second).  Issued in one burst they queue at the wave's issue (the
+        // address and LDS units take one instruction at a time from all
+        // waves) and hold back its MFMAs.
+        static_assert(TM == NQA && TM == NQB && TM % 2 == 0 && TN % TM == 0, "two DMAs per 16-row tile group");
+        constexpr int JG = TN / TM;               // W fragments read per group
+        for (int kt = 0; kt < nk; ++kt) {
+            {
+                const unsigned char* sa = smem + (kt & 1) * A_BYTES;
+                const unsigned char* sb = smem + 2 * A_BYTES + (kt % 3) * B_BYTES;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    ya[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off1);
+#pragma unroll
+                    for (int jj = 0; jj < JG; ++jj)
+                        yb[JG * i + jj] = *(const bf16x8*)(sb + 2048 * (wn * TN + JG * i + jj) + off1);
+                    if (i < n_i) {
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            wait_vm<NQB>();                       // slice kt+1 has landed
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's reads of slice kt are done
+            __builtin_amdgcn_s_barrier();
+            {
+                const int ka = min(kt + 2, nk - 1), kb = min(kt + 3, nk - 1);
+                const int ksa = ka + rot < nk ? ka + rot : ka + rot - nk;
+                const int ksb = kb + rot < nk ? kb + rot : kb + rot - nk;
+                const unsigned da = lds_base + (kt & 1) * A_BYTES + NQA * wave * 1024;
+                const unsigned db = lds_base + 2 * A_BYTES + (kt % 3) * B_BYTES + NQB * wave * 1024;
+                const unsigned char* sa = smem + ((kt + 1) & 1) * A_BYTES;
+                const unsigned char* sb = smem + 2 * A_BYTES + ((kt + 1) % 3) * B_BYTES;
+                const bool more = kt + 1 < nk;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    // all A DMAs of the step before all W DMAs: the wait
+                    // above relies on W being the last NQB issued
+                    if (i < TM / 2) {
+                        if (a_mine) {
+                            dma_frag_s(a_base + ksa * BK2, a_off[2 * i], __builtin_amdgcn_readfirstlane(da + 2048 * i));
+                            dma_frag_s(a_base + ksa * BK2, a_off[2 * i + 1],
+                                       __builtin_amdgcn_readfirstlane(da + 2048 * i + 1024));
+                        }
+                    } else {
+                        const int q = 2 * (i - TM / 2);
+                        dma_frag_s(Wg + ksb * BK2, b_off(q), __builtin_amdgcn_readfirstlane(db + 1024 * q));
+                        dma_frag_s(Wg + ksb * BK2, b_off(q + 1), __builtin_amdgcn_readfirstlane(db + 1024 * (q + 1)));
+                    }
+                    if (more) {
+                        xa[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off0);
+#pragma unroll
+                        for (int jj = 0; jj < JG; ++jj)
+                            xb[JG * i + jj] = *(const bf16x8*)(sb + 2048 * (wn * TN + JG * i + jj) + off0);
+                    }
+                    if (i < n_i) {
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya[i], yb[j], acc[i][j], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        wait_vm<0>();
+    } else {
     // ---- DMA sources.  One DMA instruction moves a block of 16 rows x 64 B
     // (one K slice of 32): lane l reads 16 B of row quad l >> 2 at chunk
     // l & 3, so every 4 lanes read 64 contiguous bytes (the address unit
@@ -270,18 +474,6 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     const unsigned lane_off = BLK_OFF[fr >> 2] + 64 * (fr & 3) + 16 * (lane >> 4);
     auto tile_off = [&](int tau) { return (unsigned)((tau >> 2) * GROUP + 256 * (tau & 3)) + lane_off; };
 
-    // valid 16-row tiles of this wave: tiles wm + WM i with 16 (wm + WM i) < valid
-    const int ntile_valid = (valid + 15) >> 4;
-    int n_i = 0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) n_i += (wm + S::WM * i < ntile_valid) ? 1 : 0;
-    n_i = __builtin_amdgcn_readfirstlane(n_i);
-
-    f32x4 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // prologue: slices 0 .. STAGES-1 in flight, one per stage (clamped re-reads
     // past the end keep the per-step DMA count fixed, which the waits below
@@ -335,6 +527,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
     }
     wait_vm<0>();
+    }
 
     // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + v ---
     const int ccol = lane & 15, crow = (lane >> 4) * 4;
@@ -355,7 +548,9 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         __syncthreads();
 #pragma unroll
         for (int pass = 0; pass < BM / EPI_ROWS; ++pass) {
-#pragma unroll
+            // planes in a loop, not unrolled: each unrolled copy keeps its
+            // own row addresses in scalar registers, which then spill
+#pragma unroll 1
             for (int plane = 0; plane < PLANES; ++plane) {
 #pragma unroll
                 for (int ii = 0; ii < IPP; ++ii) {
@@ -536,6 +731,11 @@ hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s) {
     p.gu_out = (uint16_t*)a.gu_out;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
+    // 256-row tiles address gathered A rows and one group's weights by 32-bit
+    // byte offsets
+    if (a.bm == 256 && ((a.a_rows && (int64_t)a.a_nrows * a.K * 2 >= (int64_t(1) << 32)) ||
+                        (int64_t)2 * a.N * a.K * 2 >= (int64_t(1) << 32)))
+        return hipErrorInvalidValue;
     if (a.gu_out) {
         if (a.bm == 64) gg::launch<gg::SWIGLU_SAVE, 64, 256>(p, tiles, s);
         else gg::launch<gg::SWIGLU_SAVE, 256, 256>(p, tiles, s);
@@ -565,6 +765,7 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s)
     p.W_extra = (const uint16_t*)a.W_extra;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
+    if (a.bm == 256 && (int64_t)a.N * a.K * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     // 64-row tiles: 128-column tiles double the work items of these
     // (HBM-bound) launches, which evens out the last round on 256 CUs
     if (c_fp32) {
