@@ -220,11 +220,11 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         if (r >= k_end) return p.zero_row;
         return p.B + (int64_t)r * p.ldb;
     };
-    auto issue = [&](int kt, int stage) {
+    // this wave's DMA q of slice kt (A blocks first, then B) into `stage`
+    auto issue_q = [&](int kt, int stage, int q) {
         const unsigned sb = lds_base + stage * S::STAGE_BYTES;
         const int k0 = k_begin + kt * BK;
-#pragma unroll
-        for (int q = 0; q < A_PER_WAVE; ++q) {
+        if (q < A_PER_WAVE) {
             if (WGRAD) {
                 const int r = k0 + a_row[q];
                 const uint16_t* as = (r < k_end ? p.A + (int64_t)r * p.lda : p.zero_row) + a_col[q];
@@ -232,10 +232,14 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
             } else {
                 dma_frag(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
             }
+        } else {
+            const int qb = q - A_PER_WAVE;
+            dma_frag(b_row(k0 + b_row_k[qb]) + b_col[qb], __builtin_amdgcn_readfirstlane(sb + b_lds[qb]));
         }
+    };
+    auto issue = [&](int kt, int stage) {
 #pragma unroll
-        for (int q = 0; q < B_PER_WAVE; ++q)
-            dma_frag(b_row(k0 + b_row_k[q]) + b_col[q], __builtin_amdgcn_readfirstlane(sb + b_lds[q]));
+        for (int q = 0; q < D; ++q) issue_q(kt, stage, q);
     };
 
     // fragment offsets of the K-contiguous A (DGRAD)
@@ -264,37 +268,41 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         for (int s = 0; s < STAGES - 1; ++s) issue(min(s, nk - 1), s);
 
         bf16x8 fa[2][TM], fb[2][TN];
-        auto read_frags = [&](int stage, bf16x8* a, bf16x8* b) {
-            const unsigned char* st = smem + stage * S::STAGE_BYTES;
+        // group i of a slice's fragments: A tile wm + WM i and B tiles JG i ..
+        static_assert(D == TM && TN % TM == 0, "one DMA per 16-row tile group");
+        constexpr int JG = TN / TM;
+        auto read_group = [&](const unsigned char* st, int i, bf16x8* a, bf16x8* b) {
+            const int tau = wm + WM * i;          // 16-row tile of the block
+            if (WGRAD) a[i] = km_frag(st, 16 * tau, lane);
+            else a[i] = *(const bf16x8*)(st + tile_off(tau));
 #pragma unroll
-            for (int j = 0; j < TN; ++j) b[j] = km_frag(st + S::A_BYTES, (128 * wn + 16 * j), lane);
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int tau = wm + WM * i;      // 16-row tile of the block
-                if (WGRAD) a[i] = km_frag(st, 16 * tau, lane);
-                else a[i] = *(const bf16x8*)(st + tile_off(tau));
-            }
+            for (int jj = 0; jj < JG; ++jj)
+                b[JG * i + jj] = km_frag(st + S::A_BYTES, 128 * wn + 16 * (JG * i + jj), lane);
         };
-        auto mfmas = [&](const bf16x8* a, const bf16x8* b) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (i < n_i) {
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-                }
-            }
-        };
+        // The MFMAs run in TM groups (one 16-row tile each) with this wave's
+        // DMA and next fragment reads between them: issued in one burst after
+        // the barrier they queue at the wave's issue and hold back its MFMAs.
         auto step = [&](int kt, const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb) {
             wait_vm<D * (STAGES - 3)>();
             __builtin_amdgcn_s_barrier();
-            issue(min(kt + STAGES - 1, nk - 1), (kt + STAGES - 1) % STAGES);
-            read_frags((kt + 1 < nk ? kt + 1 : kt) % STAGES, na, nb);
-            mfmas(ca, cb);
+            const int kn = min(kt + STAGES - 1, nk - 1), sn = (kt + STAGES - 1) % STAGES;
+            const unsigned char* st = smem + ((kt + 1 < nk ? kt + 1 : kt) % STAGES) * S::STAGE_BYTES;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                issue_q(kn, sn, i);
+                read_group(st, i, na, nb);
+                if (i < n_i) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         };
         wait_vm<D * (STAGES - 2)>();
         __builtin_amdgcn_s_barrier();
-        read_frags(0, fa[0], fb[0]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) read_group(smem, i, fa[0], fb[0]);
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
             step(kt, fa[0], fb[0], fa[1], fb[1]);
