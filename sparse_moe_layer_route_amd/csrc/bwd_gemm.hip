@@ -351,7 +351,9 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                 if (col < p.N) {
                     if (WGRAD) {
                         const int m = m_tile * BM + lr;
-                        if (m < p.M) *(float4*)&C[(int64_t)m * p.ldc + col] = v;
+                        // written once and not read here: non-temporal stores
+                        const f32x4 vv = {v.x, v.y, v.z, v.w};
+                        if (m < p.M) __builtin_nontemporal_store(vv, (f32x4*)&C[(int64_t)m * p.ldc + col]);
                     } else if (lr < valid) {
                         *(float4*)&C[(int64_t)(row0 + lr) * p.ldc + col] = v;
                     }
