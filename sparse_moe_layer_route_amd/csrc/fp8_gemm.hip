@@ -183,14 +183,14 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     const float* sa_src = p.As + src_row(64 * (wave & 1) + lane);
 
     const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
-    auto issue = [&](int kt, int stage) {
+    // this wave's DMA q of slice kt into `stage`: q 0, 1 A blocks, 2 .. 5 W
+    // blocks, 6 the row scales (waves 0 and 1 only)
+    auto issue_q = [&](int kt, int stage, int q) {
         const int k0 = kt * BKB;
         const unsigned sb = lds_base + stage * STAGE_BYTES;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) dma16(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dma16(b_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + b_lds[q]));
-        if (wave < 2) dma4(sa_src + (int64_t)kt * p.a_ld, __builtin_amdgcn_readfirstlane(sb + SA_OFF + 256 * wave));
+        if (q < 2) dma16(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
+        else if (q < 6) dma16(b_src[q - 2] + k0, __builtin_amdgcn_readfirstlane(sb + b_lds[q - 2]));
+        else if (wave < 2) dma4(sa_src + (int64_t)kt * p.a_ld, __builtin_amdgcn_readfirstlane(sb + SA_OFF + 256 * wave));
     };
     // LDS offset of this lane's 32 bytes (two 16-byte reads, +0 and +16) in
     // 16-row tile tau = 4g + t: row r = lane & 15 from block r >> 2 of
@@ -232,31 +232,13 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(min(s, KB - 1), s);
-
+    // fragments and row scales of one slice
+    i32x8 bfr[TN], afr[TM];
+    f32x4 sa[TM];
     const int crow = (lane >> 4) * 4;
-    for (int kt = 0; kt < KB; ++kt) {
-        const int stage = kt % STAGES;
-        // the DMAs of slice kt + 1 (7 for waves 0 and 1, 6 for the others) may stay in flight
-        if (wave < 2) wait_vm<7 * (STAGES - 2)>(); else wait_vm<6 * (STAGES - 2)>();
-        __builtin_amdgcn_s_barrier();
-        issue(min(kt + STAGES - 1, KB - 1), (kt + STAGES - 1) % STAGES);
-
-        if ((kt & 63) == 0 && kt > 0) {
-            swa_v = kt + lane < KB ? swa_p[kt + lane] : 0.f;
-            swb_v = kt + lane < KB ? swb_p[kt + lane] : 0.f;
-            asm volatile("" ::"v"(swa_v), "v"(swb_v));
-        }
-        const float swa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swa_v), kt & 63));
-        const float swb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swb_v), kt & 63));
+    auto read_frags = [&](int stage) {
         const unsigned char* st = smem + stage * STAGE_BYTES;
         const float* sa_l = (const float*)(st + SA_OFF);
-        // the slice's fragments and row scales first, then every MFMA of the
-        // slice into temporaries, then the block scales: no MFMA result is
-        // consumed right after issue
-        i32x8 bfr[TN], afr[TM];
-        f32x4 sa[TM];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const unsigned char* f = st + A_BYTES + tile_off(4 * wn + j);
@@ -273,25 +255,67 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
                 sa[i] = *(const f32x4*)(sa_l + 16 * tile + crow);
             }
         }
-        f32x4 r[TM][TN];
+    };
+
+    // Slice s sits in stage s % STAGES.  Step kt multiplies slice kt from
+    // registers; its stage then takes slice kt + STAGES (its fragments were
+    // read during step kt-1), and the fragments of slice kt+1 are read into
+    // the same registers once this step's MFMAs have been issued, so the LDS
+    // latency overlaps the MFMAs.  The DMAs sit between the MFMA groups:
+    // issued in one burst after the barrier they queue at the wave's issue
+    // and hold back its MFMAs.  Clamped re-reads past the end keep the DMA
+    // count per step fixed, which the waits rely on.
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+#pragma unroll
+        for (int q = 0; q < 7; ++q) issue_q(min(s, KB - 1), s, q);
+    if (wave < 2) wait_vm<7 * (STAGES - 1)>(); else wait_vm<6 * (STAGES - 1)>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(0);
+
+    for (int kt = 0; kt < KB; ++kt) {
+        // slice kt+1 has landed (at most slice kt+2's DMAs outstanding), and
+        // this wave's reads of slice kt are done
+        if (wave < 2) wait_vm<7>(); else wait_vm<6>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0), vmcnt/expcnt untouched
+        __builtin_amdgcn_s_barrier();
+        const int kn = min(kt + STAGES, KB - 1), sn = kt % STAGES;
+
+        if ((kt & 63) == 0 && kt > 0) {
+            swa_v = kt + lane < KB ? swa_p[kt + lane] : 0.f;
+            swb_v = kt + lane < KB ? swb_p[kt + lane] : 0.f;
+            asm volatile("" ::"v"(swa_v), "v"(swb_v));
+        }
+        const float swa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swa_v), kt & 63));
+        const float swb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swb_v), kt & 63));
+        // The MFMAs of 16-row tile i go to temporaries; tile i-1's results
+        // are scaled and added while they run (so no MFMA result is consumed
+        // right after issue), and the DMAs sit between the groups.  The next
+        // slice's fragments are read after the last group is issued; the last
+        // tile's results are scaled after that, with its row scales kept.
+        f32x4 r[2][TN];
+        f32x4 sa_last = sa[TM - 1];
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        auto scale_add = [&](int i, const f32x4* ri, f32x4 sai) {
+            const f32x4 sga = sai * swa, sgb = sai * swb;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] += ri[j] * ((MODE == SWIGLU && j >= TN / 2) ? sgb : sga);
+        };
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+            issue_q(kn, sn, 2 * i);
+            if (2 * i + 1 < 7) issue_q(kn, sn, 2 * i + 1);
             if (i < n_i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     // E8M0 scale 127 = 1.0 on both operands; the fp32 block scales follow
-                    r[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr[i], bfr[j], z, 0, 0, 0, 127, 0, 127);
+                    r[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr[i], bfr[j], z, 0, 0, 0, 127, 0, 127);
             }
+            if (i > 0 && i - 1 < n_i) scale_add(i - 1, r[(i - 1) & 1], sa[i - 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i < n_i) {
-                const f32x4 sga = sa[i] * swa, sgb = sa[i] * swb;
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] += r[i][j] * ((MODE == SWIGLU && j >= TN / 2) ? sgb : sga);
-            }
-        }
+        if (kt + 1 < KB) read_frags((kt + 1) % STAGES);
+        if (TM - 1 < n_i) scale_add(TM - 1, r[(TM - 1) & 1], sa_last);
     }
     wait_vm<0>();
 
