@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--decode-workload", default="step5_decode")
     ap.add_argument("--fp8-workload", default="step5_fp8_prefill", help="'' to skip the FP8 report")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-half-workload", default="step5_decode_half",
+                    help="second decode report (hot experts take about half of the selections); '' to skip")
+    ap.add_argument("--no-ep-proxy", action="store_true",
+                    help="skip the report on one expert-parallel rank's share (44 experts, MFMA-bound)")
     ap.add_argument("--no-balanced", action="store_true", help="skip the static balanced routing report")
     ap.add_argument("--no-block", action="store_true", help="skip the RMSNorm + residual block report")
     ap.add_argument("--no-train", action="store_true", help="skip the forward + backward training report")
@@ -196,9 +200,27 @@ def main():
         note(f"{wl.name} training step: moe_layer_forward_train + moe_layer_backward")
         res["train"] = time_train(args, wl, moe, torch, mi)
 
+    if not args.no_ep_proxy and cfg.expert_dtype == "bf16":
+        we = mi.WORKLOADS["ep_rank_proxy"]
+        note(f"{we.name}: one expert-parallel rank's share ({we.cfg.num_experts} experts, {we.T} tokens)")
+        r = time_layer(args, we, moe, torch, mi)
+        fl = layer_flops(we, r["touched"])
+        up_fl = 2 * we.T * we.cfg.top_k * we.cfg.hidden_size * 2 * we.cfg.moe_intermediate_size
+        if shared_fused(we.cfg):
+            up_fl += 2 * we.T * we.cfg.hidden_size * 2 * we.cfg.share_expert_dim
+        res["ep_rank_proxy"] = {
+            "workload": we.name, "experts": we.cfg.num_experts, "tokens": we.T, "experts_touched": r["touched"],
+            "layer_forward_ms": r["layer_forward_ms"], "tflops": fl / (r["layer_forward_ms"] * 1e-3) / 1e12,
+            "mfma_frac": fl / (r["layer_forward_ms"] * 1e-3) / BF16_PEAK,
+            "up_ms": r["up_ms"], "up_tflops": up_fl / (r["up_ms"] * 1e-3) / 1e12,
+            "up_mfma_frac": up_fl / (r["up_ms"] * 1e-3) / BF16_PEAK}
+
     if not args.no_decode:
         note(f"decode workload {args.decode_workload}")
         res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
+        if args.decode_half_workload:
+            note(f"decode workload {args.decode_half_workload}")
+            res["decode_half"] = bench_decode(args, mi.WORKLOADS[args.decode_half_workload], moe, torch)
 
     if not args.no_cpu_baseline:
         note("CPU baseline (oracle on a token sample)")

@@ -80,6 +80,10 @@ WORKLOADS: Dict[str, Workload] = {
     # half of the selections (+1.0 gives them all of them)
     "step5_decode_half": Workload("step5_decode_half", 64, _mk(4096, 352, 8, 1536, 1536, 7.0, 7.0),
                                   hot_fraction=0.1, hot_bias=0.15),
+    # one rank's share of the Step-5 prefill under 8-way expert parallelism:
+    # 44 of the 352 experts, the 65,536 token-expert pairs of 8192 tokens
+    # (about 1490 rows per expert, so the expert GEMMs are MFMA-bound)
+    "ep_rank_proxy": Workload("ep_rank_proxy", 8192, _mk(4096, 44, 8, 1536, 1536, 7.0, 7.0)),
     # Step-5-Preview-shaped prefill with FP8 E4M3 routed experts
     "step5_fp8_prefill": Workload("step5_fp8_prefill", 8192,
                                   _mk(4096, 352, 8, 1536, 1536, 7.0, 7.0, expert_dtype="fp8")),
