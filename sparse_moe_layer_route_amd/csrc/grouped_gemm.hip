@@ -126,6 +126,18 @@ __device__ __forceinline__ void dma_frag_s(const void* base, unsigned off, unsig
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(off), "s"(base) : "memory");
 }
 
+// 16-byte chunk swizzle of row r (r & 15) of a 256-row tile's 128-byte LDS
+// rows: LDS chunk p holds global chunk p ^ swz(r).  Chosen by search so that
+// the fragment reads (lane l: row l & 15, chunk (l >> 4) or 4 + (l >> 4))
+// hit distinct 16-byte bank groups under every LDS service order that fits
+// the bank-conflict counter's readings on both this and the 64-row layout
+// (8 lanes per cycle over 256 bytes; lanes l, l+16, l+32, l+48 together over
+// 128 or 256 bytes; 32 lanes over 512 bytes).  The simpler 2 ((r & 15) >> 2)
+// is conflict-free only under the last and measured 2-way.
+__device__ __forceinline__ int swz(int r) {
+    return ((((r ^ (r >> 1) ^ (r >> 3)) & 1) << 2) | (((r >> 2) & 1) << 1));
+}
+
 // wait until at most n vector-memory operations of this wave are outstanding
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -232,10 +244,9 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         // L2 requests of 64-byte pieces for the same bytes).  A block lands at
         // LDS byte 16 l per lane l, i.e. rows of 128 B back to back; lane l
         // reads the line's 16-byte chunk (l & 7) ^ swz(row), so LDS chunk p of
-        // a row holds global chunk p ^ swz(row), with swz(row) = 2 ((row & 15)
-        // >> 2).  A fragment read (lane l: row l & 15 of a 16-row tile, K
-        // chunk 4 sub + (l >> 4)) then touches 32 distinct 16-byte bank groups
-        // in each 32-lane pass.  LDS: A in 2 stages, W in 3 (W is the operand
+        // a row holds global chunk p ^ swz(row).  A fragment read (lane l: row
+        // l & 15 of a 16-row tile, K chunk 4 sub + (l >> 4)) is then free of
+        // bank conflicts (see swz).  LDS: A in 2 stages, W in 3 (W is the operand
         // that streams from HBM, so it gets the longer lead), 160 KiB.
         // Wave w moves A blocks 4w .. 4w+3 (rows 32w .. 32w+31) and W blocks
         // 4w .. 4w+3 of every slice.
@@ -256,7 +267,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 #pragma unroll
         for (int q = 0; q < NQA; ++q) {
             const int r = 8 * (NQA * wave + q) + dq;              // tile row 0..255
-            const int c = (lane & 7) ^ (2 * ((r & 15) >> 2));
+            const int c = (lane & 7) ^ swz(r & 15);
             int ar = min(r, valid - 1);
             if (gather) {
                 ar += row0;
@@ -281,10 +292,11 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
             w_last = p.N - 1;
         }
         static_assert(NQB == 4 && S::GW == 128, "the W row formula assumes 32 columns per wave and slice");
-        const unsigned b_chunk = 16u * ((lane & 7) ^ (2 * (dq >> 2)));   // chunk of even q; odd q: ^ 64
+        // chunk of even / odd q (tile column 8 (4 wave + q) + dq: row 8 (q & 1) + dq of its 16)
+        const unsigned b_chunk0 = 16u * ((lane & 7) ^ swz(dq)), b_chunk1 = 16u * ((lane & 7) ^ swz(8 + dq));
         auto b_off = [&](int q) {
             const int wrow = w_add + min(w_base + 8 * q + dq, w_last);
-            return (unsigned)wrow * (unsigned)(2 * K) + (b_chunk ^ (64u * (q & 1)));
+            return (unsigned)wrow * (unsigned)(2 * K) + ((q & 1) ? b_chunk1 : b_chunk0);
         };
         const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
         auto issue_a = [&](int kt, int stage) {
@@ -304,7 +316,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                 dma_frag_s(Wg + ks * BK2, b_off(q), __builtin_amdgcn_readfirstlane(sb + 1024 * q));
         };
         // lane's byte offset in a 16-row tile for K chunk 4 sub + (lane >> 4)
-        const int fr = lane & 15, sw = 2 * (fr >> 2);
+        const int fr = lane & 15, sw = swz(fr);
         const unsigned off0 = 128 * fr + 16 * ((lane >> 4) ^ sw);
         const unsigned off1 = off0 ^ 64u;         // chunk 4 + c: (c ^ sw) ^ 4
         bf16x8 xa[TM], xb[TN], ya[TM], yb[TN];
