@@ -47,11 +47,14 @@ __device__ constexpr int BLK_OFF[4] = {0, 1024 + 32, 2048 + 256, 3072 + 288};
 constexpr int GROUP = 3072 + 288 + 1024;
 constexpr int KC_BYTES = 4 * GROUP;     // 256 rows x one K slice
 // K-major operand: 4 slabs of 64 columns x 4 blocks of 8 k-rows (one DMA
-// block each: 128 B per row, lane-consecutive).  The blocks of a slab sit
-// 1056 B apart, not 1024: a 32-lane pass of a transposing read touches 4
-// rows of two neighbouring blocks, and the 32-byte skew puts them on
-// distinct banks.
-constexpr int KB_PITCH = 1024 + 32;
+// block each: 128 B per row, lane-consecutive), k-row r of a slice holding
+// the row's 16-byte chunk c at position c ^ km_swz(r).  The swizzle was
+// found by search: the transposing reads are free of bank conflicts under
+// every LDS service order that fits the conflict counter's readings (16 or
+// 32 consecutive lanes, or lanes l and l + 32, over 128 to 512 bytes).  The
+// earlier 32-byte skew between blocks fitted only a 32-lane, 512-byte order
+// and measured 1.2-1.6 conflict cycles per LDS instruction.
+constexpr int KB_PITCH = 1024;
 constexpr int SLAB = 4 * KB_PITCH;
 constexpr int KM_BYTES = 4 * SLAB;
 // epilogue staging: rows of 256 fp32 with a 16-byte skew per row, so the 4
@@ -114,20 +117,36 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// LDS byte offset, inside a K-major operand, of the 8 bytes that lane s (of
-// its 16-lane group g) reads for the 16-column tile starting at column c0,
-// k rows 8g + 4 half + (s >> 2)
-__device__ __forceinline__ unsigned km_off(int c0, int g, int half, int s) {
-    return (unsigned)((c0 >> 6) * SLAB + g * KB_PITCH + (4 * half + (s >> 2)) * 128 + (c0 & 63) * 2 + (s & 3) * 8);
+// chunk swizzle of k-row r (0..31) of a K-major slice
+__device__ __forceinline__ int km_swz(int r) {
+    return (2 * ((r ^ (r >> 3) ^ (r >> 4)) & 1)) | (4 * (((r >> 1) ^ (r >> 4)) & 1));
+}
+
+// The 8 bytes that lane s (of its 16-lane group g) reads for the 16-column
+// tile at column c0 are in k-row r = 8g + 4 half + (s >> 2), chunk
+// (c0 & 63) / 8 + ((s & 3) >> 1), bytes 8 (s & 1) of it.  The chunk's high
+// bits come from c0 alone, so the offset is this lane's base for the half
+// XOR 16 (c0 & 63) / 8, plus the slab.
+struct KmLane {
+    unsigned half0, half1;
+};
+__device__ __forceinline__ KmLane km_lane(int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    KmLane kl;
+    const int r0 = 8 * g + (s >> 2), r1 = r0 + 4;
+    kl.half0 = (unsigned)(g * KB_PITCH + (r0 & 7) * 128 + 16 * (((s & 3) >> 1) ^ km_swz(r0)) + 8 * (s & 1));
+    kl.half1 = (unsigned)(g * KB_PITCH + (r1 & 7) * 128 + 16 * (((s & 3) >> 1) ^ km_swz(r1)) + 8 * (s & 1));
+    return kl;
 }
 
 // a 16x16x32 fragment from a K-major operand: two transposing reads
-__device__ __forceinline__ bf16x8 km_frag(const unsigned char* base, int c0, int lane) {
-    const int g = lane >> 4, s = lane & 15;
+__device__ __forceinline__ bf16x8 km_frag(const unsigned char* base, int c0, const KmLane& kl) {
+    const unsigned x = 16u * ((c0 & 63) >> 3);
+    const unsigned char* slab = base + (c0 >> 6) * SLAB;
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
-        (lds_u8*)(base + km_off(c0, g, 0, s))));
+        (lds_u8*)(slab + (kl.half0 ^ x))));
     const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
-        (lds_u8*)(base + km_off(c0, g, 1, s))));
+        (lds_u8*)(slab + (kl.half1 ^ x))));
     typedef short v8s __attribute__((ext_vector_type(8)));
     const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
@@ -195,7 +214,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         a_col[q] = 0;
         a_src[q] = p.A;
         if (WGRAD) {
-            a_col[q] = min(m_tile * BM + slab * 64, p.M - 64) + (lane & 7) * 8;
+            a_col[q] = min(m_tile * BM + slab * 64, p.M - 64) + ((lane & 7) ^ km_swz(a_row[q])) * 8;
             a_lds[q] = slab * SLAB + kb * KB_PITCH + 16 * lane;
         } else {
             const int ar = row0 + min(block_row(blk), valid - 1);
@@ -210,7 +229,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         const int blk = B_PER_WAVE * wave + q;
         const int kb = blk & 3, slab = blk >> 2;
         b_row_k[q] = 8 * kb + (lane >> 3);
-        b_col[q] = min(n_tile * BN + slab * 64, p.N - 64) + (lane & 7) * 8;
+        b_col[q] = min(n_tile * BN + slab * 64, p.N - 64) + ((lane & 7) ^ km_swz(b_row_k[q])) * 8;
         b_lds[q] = S::A_BYTES + slab * SLAB + kb * KB_PITCH + 16 * lane;
     }
     const unsigned lds_base = (unsigned)(size_t)(lds_u8*)smem;
@@ -268,16 +287,17 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         for (int s = 0; s < STAGES - 1; ++s) issue(min(s, nk - 1), s);
 
         bf16x8 fa[2][TM], fb[2][TN];
+        const KmLane kml = km_lane(lane);
         // group i of a slice's fragments: A tile wm + WM i and B tiles JG i ..
         static_assert(D == TM && TN % TM == 0, "one DMA per 16-row tile group");
         constexpr int JG = TN / TM;
         auto read_group = [&](const unsigned char* st, int i, bf16x8* a, bf16x8* b) {
             const int tau = wm + WM * i;          // 16-row tile of the block
-            if (WGRAD) a[i] = km_frag(st, 16 * tau, lane);
+            if (WGRAD) a[i] = km_frag(st, 16 * tau, kml);
             else a[i] = *(const bf16x8*)(st + tile_off(tau));
 #pragma unroll
             for (int jj = 0; jj < JG; ++jj)
-                b[JG * i + jj] = km_frag(st + S::A_BYTES, 128 * wn + 16 * (JG * i + jj), lane);
+                b[JG * i + jj] = km_frag(st + S::A_BYTES, 128 * wn + 16 * (JG * i + jj), kml);
         };
         // The MFMAs run in TM groups (one 16-row tile each) with this wave's
         // DMA and next fragment reads between them: issued in one burst after
