@@ -28,8 +28,10 @@
  * Threads: no global mutable state; calls are thread-safe.  Calls that share
  *   a workspace must be ordered on one stream.
  * Shapes: H % 64 == 0, I % 64 == 0, Is % 64 == 0 (or Is == 0), 1 <= k <= 32,
- *   k <= E <= 1024, T >= 0 (T == 0 is a no-op), T * k < 2^31.  FP8 experts
- *   also need H % 128 == 0 and I % 128 == 0.  Other shapes return
+ *   k <= E <= 1024, T >= 0 (T == 0 is a no-op), T * k < 2^31, and, as x and
+ *   one expert's fused first-projection weights are addressed with 32-bit
+ *   byte offsets, T * H < 2^31, 2 I * H < 2^31 and 2 Is * H < 2^31.  FP8
+ *   experts also need H % 128 == 0 and I % 128 == 0.  Other shapes return
  *   MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_MI355X_H

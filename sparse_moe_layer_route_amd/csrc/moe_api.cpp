@@ -39,6 +39,13 @@ moe_status_t check_config(const moe_config_t* c, int64_t T) {
     if (c->top_k > 32 || c->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
     if (T * (int64_t)c->top_k >= ((int64_t)1 << 31) || T >= ((int64_t)1 << 31) / 8)
         return MOE_ERR_UNSUPPORTED;
+    // the 256-row expert GEMMs address the gathered rows of x, and one
+    // expert's (or the shared expert's) first-projection weights, by 32-bit
+    // byte offsets
+    const int64_t H = c->hidden_size;
+    if (T * H >= ((int64_t)1 << 31) || 2 * (int64_t)c->moe_intermediate_size * H >= ((int64_t)1 << 31) ||
+        2 * (int64_t)c->share_expert_dim * H >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
     if (c->expert_dtype == MOE_FP8_E4M3_B128 && (c->hidden_size % 128 || c->moe_intermediate_size % 128))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;

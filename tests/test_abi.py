@@ -71,6 +71,17 @@ def test_config_validation(lib, field, value, status):
     assert ws_size(c, 64)[0] == status
 
 
+def test_32bit_offset_limits(lib):
+    # x of T x H bf16 and a 2I x H (or 2Is x H) weight panel must stay under 4 GiB
+    c = cfg_of(hidden_size=4096)
+    assert ws_size(c, (1 << 31) // 4096 - 1)[0] == 0
+    assert ws_size(c, (1 << 31) // 4096)[0] == 2
+    c = cfg_of(hidden_size=16384, moe_intermediate_size=65536)
+    assert ws_size(c, 8)[0] == 2
+    c = cfg_of(hidden_size=16384, moe_intermediate_size=64, share_expert_dim=65536)
+    assert ws_size(c, 8)[0] == 2
+
+
 def test_topk_above_32_unsupported(lib):
     c = cfg_of(num_experts=64, top_k=33)
     assert ws_size(c, 8)[0] == 2
