@@ -8,8 +8,8 @@
 // work per wave for that kernel, and router_logits_kernel below is used: no
 // LDS, each wave owns a 16-token x 16-expert tile and feeds
 // v_mfma_f32_16x16x32_bf16 straight from global memory (x rows and router
-// rows stay in L2), with the next K slice's loads issued before the current
-// slice's MFMAs; K is split over `nsplit` blocks (blockIdx.z) that write
+// rows stay in L2), with the loads of up to 16 K slices issued before their
+// MFMAs; K is split over `nsplit` blocks (blockIdx.z) that write
 // partial logits [nsplit][T][E], summed in split order by the top-k kernel,
 // so the dependent chain per wave is short.  K order inside a 32-wide slice:
 // lane group g = lane >> 4 takes 8-element chunk g, for both operands.
@@ -45,26 +45,29 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8 a[TM], b[TN], an[TM], bn[TN];
+    // all loads of up to CH slices are issued before their MFMAs, so a wave
+    // waits for memory once per CH slices (once in all when H/nsplit <= 512)
+    constexpr int CH = 16;
+    for (int k0 = 0; k0 < hk; k0 += 32 * CH) {
+        bf16x8 a[CH][TM], b[CH][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8*)(ap[i]);
+        for (int c = 0; c < CH; ++c) {
+            const int kk = min(k0 + 32 * c, hk - 32);   // past the end: a re-read, not multiplied
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8*)(bp[j]);
-    for (int k0 = 32; k0 <= hk; k0 += 32) {
-        const int kn = min(k0, hk - 32);          // the last step re-reads its own slice
+            for (int i = 0; i < TM; ++i) a[c][i] = *(const bf16x8*)(ap[i] + kk);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) an[i] = *(const bf16x8*)(ap[i] + kn);
+            for (int j = 0; j < TN; ++j) b[c][j] = *(const bf16x8*)(bp[j] + kk);
+        }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bn[j] = *(const bf16x8*)(bp[j] + kn);
+        for (int c = 0; c < CH; ++c) {
+            if (k0 + 32 * c < hk) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = an[i];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = bn[j];
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+            }
+        }
     }
     // lane holds expert column (lane & 15), token rows 4*(lane >> 4) + v
 #pragma unroll
