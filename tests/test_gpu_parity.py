@@ -78,6 +78,10 @@ SMALL = {
     "small_tiles_multi_tile": dict(T=600, num_experts=32, top_k=2),
     # shared width differs from the experts': the shared expert runs on its own
     "shared_width_differs": dict(moe_intermediate_size=192, share_expert_dim=128, T=100),
+    # small-batch router with H / 8 = 576 > 512: its K loop runs two chunks of
+    # 16 slices, the second ragged
+    "router_two_chunks": dict(hidden_size=4608, T=24, num_experts=16, top_k=4, moe_intermediate_size=64,
+                              share_expert_dim=64),
 }
 
 
