@@ -230,9 +230,13 @@ def main():
 
 
 def time_layer(args, wl, moe, torch, mi):
-    """Warm up, then time args.steps steps of the stepwise path (the routed
-    experts' first projection bracketed by HIP events on its stream), and the
-    same count of moe_layer_forward calls."""
+    """Warm up, then time args.steps steps, each one moe_layer_forward call
+    (the whole layer in one call: routing, permutation, both expert
+    projections with the shared expert, combine), bracketed by a
+    synchronisation on both sides.  Then, as a second timed region of as many
+    steps, the same layer through its separate entry points, with the routed
+    experts' first projection bracketed by HIP events on its stream: that
+    kernel's average duration for the roofline object."""
     dev = "cuda"
     cfg, T, k, H = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.hidden_size
     note(f"generating {wl.name} inputs")
@@ -241,6 +245,7 @@ def time_layer(args, wl, moe, torch, mi):
     stream = torch.cuda.current_stream()
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty((cfg.num_experts,), dtype=torch.int32, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     h = torch.empty(moe.moe_hidden_bytes(cfg, T), dtype=torch.uint8, device=dev)
     # the shared expert runs inside the expert launches when it can (as
@@ -251,47 +256,48 @@ def time_layer(args, wl, moe, torch, mi):
     s13, s2 = inp.get("w13_scale"), inp.get("w2_scale")
     ws13, ws2 = (inp["ws13"], inp["ws2"]) if fused else (None, None)
 
-    def step(ev=None):
+    def layer():
+        moe.moe_layer_forward(cfg, inp, out=out, ws=ws, stream=stream, expert_counts=counts)
+
+    def stepwise(ev):
         moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ids, w, ws=ws, stream=stream)
-        counts, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+        _, offsets, r2p, p2r = moe.moe_permute(cfg, ids, ws=ws, stream=stream)
+        ev[0].record(stream)
         moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], s13, h=h, ws=ws, stream=stream, ws13=ws13)
-        if ev is not None:
-            ev[1].record(stream)
+        ev[1].record(stream)
         moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], s2, y_rows=y_rows, ws=ws, stream=stream, ws2=ws2)
         if fused:
             moe.moe_combine(cfg, y_rows, p2r, w, shared_rows=y_rows[T * k:], out=out, stream=stream)
         else:
             moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], y_shared=y_sh, ws=ws, stream=stream)
             moe.moe_combine(cfg, y_rows, p2r, w, y_sh, out=out, stream=stream)
-        return counts
 
     note(f"{wl.name}: warmup {args.warmup} + timed {args.steps} steps")
+    warm_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for _ in range(args.warmup):
-        counts = step()
+        layer()
+        stepwise(warm_ev)
     torch.cuda.synchronize()
     touched = int((counts > 0).sum().item())
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    lw = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    lw[0].record(stream)
+    for _ in range(args.steps):
+        layer()
+    lw[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    up_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
-
-    # the single-call entry point does the same launches; time it too
-    lw = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    lw[0].record(stream)
-    for _ in range(args.steps):
-        moe.moe_layer_forward(cfg, inp, out=out, ws=ws, stream=stream)
-    lw[1].record(stream)
-    torch.cuda.synchronize()
     layer_fwd_ms = lw[0].elapsed_time(lw[1]) / args.steps
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for i in range(args.steps):
+        stepwise(events[i])
+    torch.cuda.synchronize()
+    up_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
     del inp, ws, h, y_rows, y_sh, out
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "up_ms": up_ms, "layer_forward_ms": layer_fwd_ms, "touched": touched}
