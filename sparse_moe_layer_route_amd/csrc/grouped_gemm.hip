@@ -428,15 +428,18 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     // offsets of BLK_OFF, each 32-lane pass of a ds_read_b128 hits 32
     // distinct bank groups.  Wave w moves B blocks (BN/128) w + q and A blocks
     // 2w, 2w+1 (BM 256) or A block w for w < 4 (BM 64) of every slice.
-    // 64-row tiles hold A differently: block b is the 16-row MFMA tile b
-    // (quad q = its row q, chunks XOR-swizzled by (q >> 2) & 3, which keeps
-    // the fragment reads free of bank conflicts), so a tile of few rows
-    // (decode: ~15 per expert) moves one A block per slice instead of four.
+    // Grouped 64-row tiles hold A differently: block b is the 16-row MFMA
+    // tile b (quad q = its row q, chunks XOR-swizzled by (q >> 2) & 3), so a
+    // tile of few rows (decode: ~15 per expert) moves one A block per slice
+    // instead of four.  (The counter reads some bank conflicts for it; dense
+    // 64-row launches, whose tiles are full, keep the layout above.)
     constexpr int A_PER_WAVE = S::NA >= NW ? S::NA / NW : 1;
     // A blocks hold only valid rows of their group (BM 256) or tile (BM 64):
     // a wave whose rows all lie past the valid ones moves none (those rows
     // are never multiplied)
-    const bool a_mine = S::NA >= NW ? 64 * ((A_PER_WAVE * wave) >> 2) < valid : (wave < S::NA && 16 * wave < valid);
+    constexpr bool A_TILED = BM == 64 && GROUPED;
+    const bool a_mine = S::NA >= NW ? 64 * ((A_PER_WAVE * wave) >> 2) < valid
+                                    : (wave < S::NA && (!A_TILED || 16 * wave < valid));
     const int quad = lane >> 2, chunk = lane & 3;
     auto block_row = [&](int blk) { return 64 * (blk >> 2) + 16 * (quad >> 2) + 4 * (blk & 3) + (quad & 3); };
     const uint16_t* a_src[A_PER_WAVE];
@@ -445,14 +448,14 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     for (int q = 0; q < A_PER_WAVE; ++q) {
         const int blk = S::NA >= NW ? A_PER_WAVE * wave + q : min(wave, S::NA - 1);
         // the gathered activation row (clamped inside the group, and to A)
-        int ar = row0 + min(BM == 64 ? 16 * blk + quad : block_row(blk), valid - 1);
+        int ar = row0 + min(A_TILED ? 16 * blk + quad : block_row(blk), valid - 1);
         if (GROUPED && p.a_rows) {
             // gathered rows (first projection): pair / k, or the token itself
             // for the extra group; otherwise A rows are the output rows
             ar = extra ? ar - p.offsets[p.groups] : p.a_rows[ar] / p.a_div;
             ar = min(max(ar, 0), p.a_nrows - 1);
         }
-        a_src[q] = p.A + (int64_t)ar * K + (BM == 64 ? chunk ^ ((quad >> 2) & 3) : chunk) * 8;
+        a_src[q] = p.A + (int64_t)ar * K + (A_TILED ? chunk ^ ((quad >> 2) & 3) : chunk) * 8;
         a_lds[q] = (blk >> 2) * GROUP + BLK_OFF[blk & 3];
     }
     constexpr int B_PER_WAVE = S::NB / NW;
@@ -492,9 +495,9 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     const int fr = lane & 15;
     const unsigned lane_off = BLK_OFF[fr >> 2] + 64 * (fr & 3) + 16 * (lane >> 4);
     auto tile_off = [&](int tau) { return (unsigned)((tau >> 2) * GROUP + 256 * (tau & 3)) + lane_off; };
-    // 64-row tiles' A: tile tau is block tau, row fr at 64 fr, chunk swizzled
+    // grouped 64-row tiles' A: tile tau is block tau, row fr at 64 fr, chunk swizzled
     const unsigned a64_off = 64 * fr + 16 * ((lane >> 4) ^ ((fr >> 2) & 3));
-    auto a_tile_off = [&](int tau) { return BM == 64 ? (unsigned)BLK_OFF[tau & 3] + a64_off : tile_off(tau); };
+    auto a_tile_off = [&](int tau) { return A_TILED ? (unsigned)BLK_OFF[tau & 3] + a64_off : tile_off(tau); };
 
 
     // prologue: slices 0 .. STAGES-1 in flight, one per stage (clamped re-reads
