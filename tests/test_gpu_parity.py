@@ -324,6 +324,34 @@ def test_replay_of_own_choice_is_bit_exact(name):
     assert torch.equal(out, out2)
 
 
+def test_layer_rows_per_expert_at_tile_boundaries():
+    """Few rows per expert (64-row tiles, each 16-row MFMA tile its own A
+    block): experts given exactly 1, 15, 16, 17, 31, 32, 33, 48, 63 and 64
+    rows, six experts none, through the routed entry point; every token
+    against the oracle with the same choice."""
+    counts_want = [1, 15, 16, 17, 31, 32, 33, 48, 63, 64, 0, 0, 0, 0, 0, 0]
+    wl = mi.workload("tiny", T=80, num_experts=16, top_k=4)
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    assert sum(counts_want) == T * k
+    # pair p (expert-sorted) goes to token p % T, slot p // T: an expert's
+    # pairs are consecutive and fewer than T, so a token's k experts differ
+    flat = np.repeat(np.arange(E), counts_want)
+    ids_np = np.empty((T, k), dtype=np.int32)
+    for p_, e in enumerate(flat):
+        ids_np[p_ % T, p_ // T] = e
+    assert all(len(set(r)) == k for r in ids_np.tolist())
+    say("[layer_rows_per_expert_at_tile_boundaries]")
+    inp = gpu_inputs(wl)
+    ids = torch.from_numpy(ids_np)
+    out, w, counts = run_routed(wl, inp, ids.to(DEV))
+    assert counts.cpu().tolist() == counts_want
+    ref = orc.layer(cfg, host(inp), ids_in=ids)
+    check_weights(w.cpu().numpy(), ref["w"])
+    err, rms = max_err_over_rms(out.float().cpu().numpy(), ref["out"])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_BF16
+
+
 @pytest.mark.parametrize("name", REPLAY_SMALL)
 def test_layer_replay_small(name):
     """A replayed choice that is not the router's (random distinct experts;
