@@ -67,23 +67,17 @@ def layer_bytes(wl, touched):
     return b
 
 
-def shared_fused(cfg):
-    return cfg.expert_dtype == "bf16" and 0 < cfg.share_expert_dim == cfg.moe_intermediate_size
-
-
 def up_kernel_bytes(wl, touched):
-    """Algorithmic bytes of the first-projection launch: W13 of every touched
-    expert once, x once, h written once -- plus, when the shared expert runs
-    in the same launch, its W13 once and its h rows written once."""
+    """Algorithmic bytes of the routed experts' first-projection launch: W13
+    of every touched expert once, x once, h written once.  (The whole-layer
+    call runs the shared expert in launches of its own, and so do the timed
+    separate entry points.)"""
     c = wl.cfg
-    T, H, k, I, Is = wl.T, c.hidden_size, c.top_k, c.moe_intermediate_size, c.share_expert_dim
+    T, H, k, I = wl.T, c.hidden_size, c.top_k, c.moe_intermediate_size
     if c.expert_dtype == "fp8":
         # codes + block scales of W13; x read once (bf16); h codes + scales written
         return touched * (2 * I * H + (2 * I // 128) * (H // 128) * 4) + T * H * 2 + T * k * (I + I // 128 * 4)
-    b = touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
-    if shared_fused(c):
-        b += 2 * Is * H * 2 + T * Is * 2
-    return b
+    return touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -163,7 +157,7 @@ def main():
         "hbm_frac": by / (ms_step * 1e-3) / HBM_PEAK,
         "layer_roofline_frac": max(fl / BF16_PEAK, by / HBM_PEAK) / (ms_step * 1e-3),
         "layer_forward_ms": layer_fwd_ms,
-        "roofline": {"kernel": "first projection + clipped SwiGLU of the routed experts and the shared expert "
+        "roofline": {"kernel": "first projection + clipped SwiGLU of the routed experts "
                                "(moe_expert_up, gg::kernel<0, true, 256, 256>)",
                      "bound": "hbm", "achieved": up_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": up_achieved / HBM_PEAK, "traffic": counter_traffic(wl), "avg_ms": up_ms,
@@ -206,8 +200,6 @@ def main():
         r = time_layer(args, we, moe, torch, mi)
         fl = layer_flops(we, r["touched"])
         up_fl = 2 * we.T * we.cfg.top_k * we.cfg.hidden_size * 2 * we.cfg.moe_intermediate_size
-        if shared_fused(we.cfg):
-            up_fl += 2 * we.T * we.cfg.hidden_size * 2 * we.cfg.share_expert_dim
         res["ep_rank_proxy"] = {
             "workload": we.name, "experts": we.cfg.num_experts, "tokens": we.T, "experts_touched": r["touched"],
             "layer_forward_ms": r["layer_forward_ms"], "tflops": fl / (r["layer_forward_ms"] * 1e-3) / 1e12,
@@ -248,9 +240,10 @@ def time_layer(args, wl, moe, torch, mi):
     counts = torch.empty((cfg.num_experts,), dtype=torch.int32, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     h = torch.empty(moe.moe_hidden_bytes(cfg, T), dtype=torch.uint8, device=dev)
-    # the shared expert runs inside the expert launches when it can (as
-    # moe_layer_forward does), else on its own
-    fused = moe.binding.shared_fusable(cfg)
+    # the separate entry points with the shared expert in launches of its own,
+    # as moe_layer_forward runs it at these sizes (on its side stream), so the
+    # routed experts' first projection is the same launch in both regions
+    fused = False
     y_rows = torch.empty((T * k + (T if fused else 0), H), dtype=torch.float16, device=dev)
     y_sh = None if fused else torch.empty((T, H), dtype=torch.float32, device=dev)
     s13, s2 = inp.get("w13_scale"), inp.get("w2_scale")

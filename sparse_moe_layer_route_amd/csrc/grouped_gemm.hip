@@ -112,6 +112,8 @@ struct Params {
     const uint16_t* W_extra;
     float limit_extra;
     uint16_t* gu_out;           // SWIGLU (optional): the pre-activations [rows][2N] bf16, gate then up
+    int rot_group;              // dense (>= 0): take the K rotation of group rot_group, so a dense
+                                // launch adds in the order of that group's grouped launch
 };
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -222,7 +224,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     // blocks that share an A tile (grouped) or a weight panel (dense) in step.
     // K slices: 64 (128 B of a row) for 256-row tiles, 32 for 64-row tiles
     const int nk = K / (BM == 256 ? BK2 : BK);   // K % 64 == 0
-    const int rot = (GROUPED ? (g + 1) * 37 : (n_tile + 1) * 37) % nk;
+    const int rot = (GROUPED ? (g + 1) * 37 : ((p.rot_group >= 0 ? p.rot_group : n_tile) + 1) * 37) % nk;
 
     // valid 16-row tiles of this wave: tiles wm + WM i with 16 (wm + WM i) < valid
     const int ntile_valid = (valid + 15) >> 4;
@@ -769,6 +771,7 @@ hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s) {
     p.W_extra = (const uint16_t*)a.W_extra;
     p.limit_extra = a.limit_extra;
     p.gu_out = (uint16_t*)a.gu_out;
+    p.rot_group = a.rot_group;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
     // 256-row tiles address gathered A rows and one group's weights by 32-bit
@@ -803,6 +806,7 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s)
     p.M = a.M;
     p.extra_rows = a.extra_rows;
     p.W_extra = (const uint16_t*)a.W_extra;
+    p.rot_group = a.rot_group;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
     if (a.bm == 256 && (int64_t)a.N * a.K * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;

@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -84,7 +85,7 @@ size_t shared_ws(const Dims& d) { return align_up((size_t)d.T * d.Is * 2); }
 
 // the whole layer: its own buffers followed by each step's scratch
 struct LayerWs {
-    size_t ids, w, counts, offsets, r2p, p2r, plan, x, y_rows, y_sh, step, total;
+    size_t ids, w, counts, offsets, r2p, p2r, plan, x, y_rows, y_sh, h_sh, step, total;
 };
 
 LayerWs layer_ws(const Dims& d) {
@@ -102,6 +103,7 @@ LayerWs layer_ws(const Dims& d) {
     L.x = o;       o += align_up((size_t)d.T * d.H * 2);    // the normalised input (moe_block_forward)
     L.y_rows = o;  o += align_up((size_t)rows * d.H * 2);
     L.y_sh = o;    o += (d.Is > 0 && !fuse) ? align_up((size_t)d.T * d.H * 4) : 0;
+    L.h_sh = o;    o += fuse ? align_up((size_t)d.T * d.Is * 2) : 0;   // the shared expert's h (side stream)
     L.step = o;
     const size_t grouped = fuse ? align_up(hidden_bytes(d)) : grouped_ws(d);
     o += std::max(std::max(route_ws(d), permute_ws(d)), std::max(grouped, shared_ws(d)));
@@ -117,6 +119,38 @@ inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK :
         if (_st != MOE_OK) return _st;             \
     } while (0)
 #define HIP_TRY(expr) MOE_TRY(hip_status(expr))
+
+// ---- the shared expert on a side stream ------------------------------------
+// The shared expert needs only x, so the whole-layer entry points run it on
+// a second stream of the same device, forked from the caller's stream before
+// routing (events: the side stream waits for the caller's work so far, the
+// caller's stream waits for the shared expert before the combine), so that
+// its GEMMs fill the chip while the router, the selection and the
+// permutation run.  One side stream and event pair per device, default
+// priority; the fork (record, wait, launches, record) is made under a lock,
+// so calls from several host threads order correctly (a join may then wait
+// for a later call's shared expert too, never for less than its own).
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream(SideStream** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    SideStream& ss = g_side[dev];
+    if (!ss.s) {
+        if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
 
 // ---- the steps, without argument checks ----------------------------------
 
@@ -287,11 +321,60 @@ moe_status_t check_layer(const moe_config_t* cfg, int64_t T, const void* x, cons
     return MOE_OK;
 }
 
+// The side stream pays from prefill sizes on (Step-5, 8192 tokens: layer
+// 3.89 -> 3.86 ms); at decode the two streams' kernels and the cross-stream
+// waits cost more than the overlap gains (64 tokens: 296 -> 307 us), and the
+// shared expert stays one more group of the routed launches.
+bool side_shared(const Dims& d) { return fuse_shared(d) && d.T >= 1024; }
+
+// the shared expert (fused layout: Is == I, bf16) on the side stream:
+// h_sh = act(ws13 . x) into L.h_sh, then its fp16 rows ws2 . h_sh after the
+// routed rows of y_rows, where the combine reads them.  The dense launches
+// use the routed launches' tile height and the K order of group E, the
+// shared expert's group in those launches, so the result is bit for bit the
+// one the separate entry points give.
+moe_status_t fork_shared(const moe_config_t* cfg, const Dims& d, const LayerWs& L, char* base, const void* x,
+                         const void* ws13, const void* ws2, hipStream_t stream, SideStream** side) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = nullptr;
+    HIP_TRY(side_stream(&ss));
+    HIP_TRY(hipEventRecord(ss->fork, stream));
+    HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
+    void* h_sh = base + L.h_sh;
+    moe::GroupedArgs a;
+    a.A = x;
+    a.a_nrows = (int)d.T;
+    a.W = ws13;
+    a.C = h_sh;
+    a.M = (int)d.T;
+    a.N = d.Is;
+    a.K = d.H;
+    a.limit = cfg->swiglu_limit_shared;
+    a.bm = tile_m(d);
+    a.rot_group = d.E;
+    HIP_TRY(moe::launch_grouped_up(a, ss->s));
+    moe::GroupedArgs b;
+    b.A = h_sh;
+    b.a_nrows = (int)d.T;
+    b.W = ws2;
+    b.C = base + L.y_rows + (size_t)d.P * d.H * 2;
+    b.M = (int)d.T;
+    b.N = d.H;
+    b.K = d.Is;
+    b.bm = a.bm;
+    b.rot_group = d.E;
+    HIP_TRY(moe::launch_grouped_down(b, false, ss->s));
+    HIP_TRY(hipEventRecord(ss->join, ss->s));
+    *side = ss;
+    return MOE_OK;
+}
+
 // the layer after routing: permute, routed + shared experts, combine
 moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs& L, char* base, const void* x,
                            const int32_t* ids, const float* w, const void* w13, const float* w13_scale,
                            const void* w2, const float* w2_scale, const void* ws13, const void* ws2, void* out,
-                           int32_t* expert_counts_out, hipStream_t stream, const float* resid = nullptr) {
+                           int32_t* expert_counts_out, hipStream_t stream, const float* resid = nullptr,
+                           SideStream* side = nullptr) {
     const int T = (int)d.T;
     int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)(base + L.counts);
     int32_t* offsets = (int32_t*)(base + L.offsets);
@@ -306,10 +389,15 @@ moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs
         // (at `step`) is still in use while the plan is made.
         int32_t* tile_start = (int32_t*)(base + L.plan);
         void* h = step;
-        HIP_TRY(moe::launch_permute_plan(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, tile_m(d), T,
-                                         tile_start, stream));
-        HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, ws13), stream));
-        HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, stream));
+        // with a side stream the shared expert runs there (fork_shared),
+        // else as group E of the routed launches
+        HIP_TRY(moe::launch_permute_plan(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, tile_m(d),
+                                         side ? 0 : T, tile_start, stream));
+        HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, side ? nullptr : ws13),
+                                       stream));
+        HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, side ? nullptr : ws2),
+                                         false, stream));
+        if (side) HIP_TRY(hipStreamWaitEvent(stream, side->join, 0));
         HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * d.H * 2, resid, out,
                                     out_bf16, T, d.H, d.k, stream));
         return MOE_OK;
@@ -497,9 +585,11 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
     char* base = (char*)ws;
     int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+    SideStream* side = nullptr;
+    if (side_shared(d)) MOE_TRY(fork_shared(cfg, d, L, base, x, ws13, ws2, stream, &side));
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
-                         expert_counts_out, stream);
+                         expert_counts_out, stream, nullptr, side);
 }
 
 moe_status_t moe_route_replay(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
@@ -532,9 +622,11 @@ moe_status_t moe_layer_forward_routed(const moe_config_t* cfg, int64_t T, const 
     LayerWs L = layer_ws(d);
     char* base = (char*)ws;
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+    SideStream* side = nullptr;
+    if (side_shared(d)) MOE_TRY(fork_shared(cfg, d, L, base, x, ws13, ws2, stream, &side));
     MOE_TRY(do_replay(cfg, d, x, w_router, topk_ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, topk_ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
-                         expert_counts_out, stream);
+                         expert_counts_out, stream, nullptr, side);
 }
 
 moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* resid_in, const float* norm_weight,
@@ -555,9 +647,11 @@ moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* 
     HIP_TRY(moe::launch_rmsnorm(resid_in, norm_weight, eps, x, (int)T, d.H, stream));
     int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+    SideStream* side = nullptr;
+    if (side_shared(d)) MOE_TRY(fork_shared(cfg, d, L, base, x, ws13, ws2, stream, &side));
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, resid_out,
-                         expert_counts_out, stream, resid_in);
+                         expert_counts_out, stream, resid_in, side);
 }
 
 moe_status_t moe_saved_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes) {

@@ -65,6 +65,7 @@ struct GroupedArgs {
     const void* W_extra = nullptr;
     float limit_extra = 0.f;
     void* gu_out = nullptr;          // first projection: also keep the pre-activations (bf16 [rows][2N])
+    int rot_group = -1;              // dense launch: add over K in the order group rot_group's grouped launch uses
 };
 int grouped_tile_m(int64_t rows, int groups);
 hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s);

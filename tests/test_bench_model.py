@@ -34,11 +34,9 @@ def test_first_projection_bytes():
     touched = 284
     T, k = 8192, 8
     want = (touched * 24 * MIB          # W13 of every touched expert, once
-            + 24 * MIB                  # the shared expert's W13 (same launch)
             + T * 4096 * 2              # x, once
-            + T * k * 1536 * 2          # h of the routed rows, written once
-            + T * 1536 * 2)             # h of the shared rows, written once
-    assert bench.up_kernel_bytes(wl, touched) == want == 7_465_861_120
+            + T * k * 1536 * 2)         # h of the routed rows, written once
+    assert bench.up_kernel_bytes(wl, touched) == want == 7_415_529_472
 
 
 def test_layer_bytes_and_flops():

@@ -210,7 +210,9 @@ def test_nan_inf_inputs_keep_ids_in_range():
     assert np.array_equal(ids[:3], ref_ids[:3])
 
 
-@pytest.mark.parametrize("name", ["step5_decode", "tiny"])
+# step35_prefill: the shared expert on the library's side stream (fork and
+# join captured with the rest)
+@pytest.mark.parametrize("name", ["step5_decode", "tiny", "step35_prefill"])
 def test_graph_replay_matches_eager(name):
     """moe_layer_forward captured into a HIP graph: every replay (with eager
     work and synchronisations between them) equals the eager result."""
