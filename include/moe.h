@@ -22,6 +22,14 @@
  *   The fused first projection holds the gate rows 0..I-1, then the up rows
  *   I..2I-1.
  * Streams: all work is enqueued on `stream`; no call waits for the device.
+ *   Exception, with the same ordering: from 1024 tokens on, moe_layer_forward,
+ *   moe_layer_forward_routed and moe_block_forward run the shared expert on a
+ *   second stream of the device that the library owns, forked from `stream`
+ *   by an event before routing and joined back by another before the
+ *   combine, so the call's work still starts after and ends before the
+ *   neighbouring work on `stream` (a HIP graph captures both).  Calls on one
+ *   device share that stream; capturing on one host thread while another
+ *   thread calls these entry points on the same device is not supported.
  * Errors: arguments are checked before anything is launched; on an argument
  *   error nothing is written.  MOE_ERR_HIP reports a launch failure;
  *   faults inside kernels surface on the stream.
