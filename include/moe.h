@@ -33,8 +33,9 @@
  * Errors: arguments are checked before anything is launched; on an argument
  *   error nothing is written.  MOE_ERR_HIP reports a launch failure;
  *   faults inside kernels surface on the stream.
- * Threads: no global mutable state; calls are thread-safe.  Calls that share
- *   a workspace must be ordered on one stream.
+ * Threads: the only global state is that side stream and its two events
+ *   (per device, created on first use under a lock); calls are thread-safe.
+ *   Calls that share a workspace must be ordered on one stream.
  * Shapes: H % 64 == 0, I % 64 == 0, Is % 64 == 0 (or Is == 0), 1 <= k <= 32,
  *   k <= E <= 1024, T >= 0 (T == 0 is a no-op), T * k < 2^31, and, as x and
  *   one expert's fused first-projection weights are addressed with 32-bit
