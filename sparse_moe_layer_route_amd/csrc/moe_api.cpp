@@ -103,7 +103,7 @@ LayerWs layer_ws(const Dims& d) {
     L.x = o;       o += align_up((size_t)d.T * d.H * 2);    // the normalised input (moe_block_forward)
     L.y_rows = o;  o += align_up((size_t)rows * d.H * 2);
     L.y_sh = o;    o += (d.Is > 0 && !fuse) ? align_up((size_t)d.T * d.H * 4) : 0;
-    L.h_sh = o;    o += fuse ? align_up((size_t)d.T * d.Is * 2) : 0;   // the shared expert's h (side stream)
+    L.h_sh = o;    o += d.Is > 0 ? align_up((size_t)d.T * d.Is * 2) : 0;   // the shared expert's h (side stream)
     L.step = o;
     const size_t grouped = fuse ? align_up(hidden_bytes(d)) : grouped_ws(d);
     o += std::max(std::max(route_ws(d), permute_ws(d)), std::max(grouped, shared_ws(d)));
@@ -325,14 +325,15 @@ moe_status_t check_layer(const moe_config_t* cfg, int64_t T, const void* x, cons
 // 3.89 -> 3.86 ms); at decode the two streams' kernels and the cross-stream
 // waits cost more than the overlap gains (64 tokens: 296 -> 307 us), and the
 // shared expert stays one more group of the routed launches.
-bool side_shared(const Dims& d) { return fuse_shared(d) && d.T >= 1024; }
+bool side_shared(const Dims& d) { return d.Is > 0 && d.T >= 1024; }
 
-// the shared expert (fused layout: Is == I, bf16) on the side stream:
-// h_sh = act(ws13 . x) into L.h_sh, then its fp16 rows ws2 . h_sh after the
-// routed rows of y_rows, where the combine reads them.  The dense launches
-// use the routed launches' tile height and the K order of group E, the
-// shared expert's group in those launches, so the result is bit for bit the
-// one the separate entry points give.
+// the shared expert on the side stream: h_sh = act(ws13 . x) into L.h_sh,
+// then ws2 . h_sh.  Fused layout (Is == I, bf16 experts): fp16 rows after
+// the routed rows of y_rows, where the combine reads them, from dense
+// launches with the routed launches' tile height and the K order of group
+// E, the shared expert's group in those launches; otherwise fp32 rows in
+// L.y_sh from the launches moe_shared_ffn makes.  Either way the result is
+// bit for bit the one the separate entry points give.
 moe_status_t fork_shared(const moe_config_t* cfg, const Dims& d, const LayerWs& L, char* base, const void* x,
                          const void* ws13, const void* ws2, hipStream_t stream, SideStream** side) {
     std::lock_guard<std::mutex> lock(g_side_mu);
@@ -350,20 +351,21 @@ moe_status_t fork_shared(const moe_config_t* cfg, const Dims& d, const LayerWs& 
     a.N = d.Is;
     a.K = d.H;
     a.limit = cfg->swiglu_limit_shared;
-    a.bm = tile_m(d);
-    a.rot_group = d.E;
+    const bool fused = fuse_shared(d);
+    a.bm = fused ? tile_m(d) : (d.T <= 64 ? 64 : 256);
+    a.rot_group = fused ? d.E : -1;
     HIP_TRY(moe::launch_grouped_up(a, ss->s));
     moe::GroupedArgs b;
     b.A = h_sh;
     b.a_nrows = (int)d.T;
     b.W = ws2;
-    b.C = base + L.y_rows + (size_t)d.P * d.H * 2;
+    b.C = fused ? (void*)(base + L.y_rows + (size_t)d.P * d.H * 2) : (void*)(base + L.y_sh);
     b.M = (int)d.T;
     b.N = d.H;
     b.K = d.Is;
     b.bm = a.bm;
-    b.rot_group = d.E;
-    HIP_TRY(moe::launch_grouped_down(b, false, ss->s));
+    b.rot_group = a.rot_group;
+    HIP_TRY(moe::launch_grouped_down(b, !fused, ss->s));
     HIP_TRY(hipEventRecord(ss->join, ss->s));
     *side = ss;
     return MOE_OK;
@@ -405,7 +407,8 @@ moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs
     HIP_TRY(moe::launch_permute(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
     float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
     MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w13_scale, w2, w2_scale, y_rows, step, stream));
-    if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
+    if (side) HIP_TRY(hipStreamWaitEvent(stream, side->join, 0));
+    else if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
     HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, nullptr, resid, out, out_bf16, T, d.H, d.k, stream));
     return MOE_OK;
 }
