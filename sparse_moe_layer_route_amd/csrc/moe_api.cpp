@@ -137,16 +137,25 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream g_side[64];
 
-hipError_t side_stream(SideStream** out) {
+// the side stream of the device `stream` belongs to (created there on first use)
+hipError_t side_stream(hipStream_t stream, SideStream** out) {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     SideStream& ss = g_side[dev];
     if (!ss.s) {
-        if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess) {
+            ss = SideStream{};
+            return e;
+        }
     }
     *out = &ss;
     return hipSuccess;
@@ -338,7 +347,7 @@ moe_status_t fork_shared(const moe_config_t* cfg, const Dims& d, const LayerWs& 
                          const void* ws13, const void* ws2, hipStream_t stream, SideStream** side) {
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* ss = nullptr;
-    HIP_TRY(side_stream(&ss));
+    HIP_TRY(side_stream(stream, &ss));
     HIP_TRY(hipEventRecord(ss->fork, stream));
     HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
     void* h_sh = base + L.h_sh;
