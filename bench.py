@@ -2,16 +2,20 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
 One step = the whole hot path (route -> permute -> routed experts' up and
-down projections -> shared expert -> combine) over one batch of synthetic
-tokens whose inputs are already resident in HBM.  The default workload is the
-Step-5-Preview-shaped prefill: 8192 tokens, hidden 4096, 352 routed experts,
-top-8, expert and shared intermediate 1536, clipped SwiGLU at 7.0, bf16.
+down projections with the shared expert -> combine) over one batch of
+synthetic tokens whose inputs are already resident in HBM: one
+moe_layer_forward call.  The workload of record is the Step-5-Preview-shaped
+prefill: 8192 tokens, hidden 4096, 352 routed experts, top-8, expert and
+shared intermediate 1536, clipped SwiGLU at 7.0, bf16.
 
-Prints one JSON line with tokens/s, the whole-layer TFLOP/s and bytes/s, the
-roofline of the dominant kernel (routed experts' first projection + SwiGLU,
-timed with HIP events on the stream it runs on), the oracle timed on the
-host cores on a bounded token sample, and the 64-token decode shape's
-bandwidth.
+Prints one JSON line with tokens/s, the whole layer's TFLOP/s and bytes/s,
+the roofline of the dominant kernel (the first projection + clipped SwiGLU
+of the routed experts, with the shared expert as one more group, as the
+layer runs it; timed with HIP events on the stream it runs on), the
+attainable peaks measured in the same run (a device copy, a vendor bf16
+GEMM), the Step-3.5-Flash prefill, the FP8-expert prefill, the 64-token
+decode shapes (the memory-side cache flushed between timed calls, medians),
+and the oracle timed on the host cores on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ import time
 METRIC = "MoE-layer fwd tokens/s + % bf16 MFMA peak (prefill) / % HBM BW (decode)"
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 BF16_PEAK = 2.5166e15      # dense bf16 MFMA FLOP/s
+FP8_PEAK = 5.0332e15       # dense fp8 MFMA FLOP/s
 
 
 def parse():
@@ -32,16 +37,19 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="step5_prefill")
+    ap.add_argument("--step35-workload", default="step35_prefill", help="'' to skip the Step-3.5 prefill report")
     ap.add_argument("--decode-workload", default="step5_decode")
     ap.add_argument("--fp8-workload", default="step5_fp8_prefill", help="'' to skip the FP8 report")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-half-workload", default="step5_decode_half",
-                    help="second decode report (hot experts take about half of the selections); '' to skip")
+                    help="decode with the hot bias calibrated so the hot experts take about half of the "
+                         "selections; '' to skip")
     ap.add_argument("--no-ep-proxy", action="store_true",
                     help="skip the report on one expert-parallel rank's share (44 experts, MFMA-bound)")
     ap.add_argument("--no-balanced", action="store_true", help="skip the static balanced routing report")
     ap.add_argument("--no-block", action="store_true", help="skip the RMSNorm + residual block report")
     ap.add_argument("--no-train", action="store_true", help="skip the forward + backward training report")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring the attainable peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -57,27 +65,46 @@ def layer_flops(wl, touched):
 
 def layer_bytes(wl, touched):
     """Algorithmic HBM bytes of one layer forward: the weights of the experts
-    the routing touches, the shared expert and router weights, the bias, the
-    input once and the fp32 output once."""
+    the routing touches (and their FP8 block scales), the shared expert and
+    router weights, the bias, the input once and the output once."""
     c = wl.cfg
     T, H, E, I, Is = wl.T, c.hidden_size, c.num_experts, c.moe_intermediate_size, c.share_expert_dim
     bpw = 1 if c.expert_dtype == "fp8" else 2
     b = touched * 3 * H * I * bpw + 3 * H * Is * 2 + 2 * E * H + 4 * E + 2 * T * H
+    if c.expert_dtype == "fp8":
+        b += touched * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)) * 4
     b += (2 if c.out_dtype == "bf16" else 4) * T * H
     return b
 
 
+def shared_in_launch(cfg):
+    """The shared expert runs as one more group of the routed launches (bf16
+    experts, shared width equal to the experts')."""
+    return cfg.expert_dtype == "bf16" and cfg.share_expert_dim > 0 and cfg.share_expert_dim == \
+        cfg.moe_intermediate_size
+
+
 def up_kernel_bytes(wl, touched):
-    """Algorithmic bytes of the routed experts' first-projection launch: W13
-    of every touched expert once, x once, h written once.  (The whole-layer
-    call runs the shared expert in launches of its own, and so do the timed
-    separate entry points.)"""
+    """Algorithmic bytes of the first-projection launch the layer makes: the
+    first-projection weights of every touched expert once (and the shared
+    expert's when it is a group of the launch), the activations once.  Its
+    output h is an intermediate the method does not need and is not
+    counted."""
     c = wl.cfg
-    T, H, k, I = wl.T, c.hidden_size, c.top_k, c.moe_intermediate_size
+    T, H, I, Is = wl.T, c.hidden_size, c.moe_intermediate_size, c.share_expert_dim
     if c.expert_dtype == "fp8":
-        # codes + block scales of W13; x read once (bf16); h codes + scales written
-        return touched * (2 * I * H + (2 * I // 128) * (H // 128) * 4) + T * H * 2 + T * k * (I + I // 128 * 4)
-    return touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+        # codes + block scales of W13; x read once as E4M3 codes with one fp32 scale per 128 columns
+        return touched * (2 * I * H + (2 * I // 128) * (H // 128) * 4) + T * H + T * (H // 128) * 4
+    b = touched * 2 * I * H * 2 + T * H * 2
+    if shared_in_launch(c):
+        b += 2 * Is * H * 2
+    return b
+
+
+def up_kernel_flops(wl):
+    c = wl.cfg
+    rows = wl.T * c.top_k + (wl.T if shared_in_launch(c) else 0)
+    return 2 * rows * 2 * c.moe_intermediate_size * c.hidden_size
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -87,7 +114,7 @@ KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_mo
 
 
 def counter_traffic(wl):
-    """HBM bytes per launch of the routed first projection from the committed
+    """HBM bytes per launch of the first projection from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a plain copy's
     counts), or None when the summary is for another workload or the kernel
     source has changed since the counters were taken."""
@@ -107,6 +134,12 @@ def counter_traffic(wl):
 
 def note(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
 def main():
@@ -132,16 +165,13 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return
     moe.load()
+    peaks = None if args.no_peaks else measure_peaks(torch)
     wl = mi.WORKLOADS[args.workload]
     cfg, T, k, E, H, I = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size, \
         wl.cfg.moe_intermediate_size
     r = time_layer(args, wl, moe, torch, mi)
-    ms_step, up_ms, layer_fwd_ms, touched = r["ms_step"], r["up_ms"], r["layer_forward_ms"], r["touched"]
+    ms_step, touched = r["ms_step"], r["touched"]
     tok_s = T / (ms_step * 1e-3)
-    fl = layer_flops(wl, touched)
-    by = layer_bytes(wl, touched)
-    up_bytes = up_kernel_bytes(wl, touched)
-    up_achieved = up_bytes / (up_ms * 1e-3)
     res = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -151,29 +181,28 @@ def main():
                    "swiglu_limit": cfg.swiglu_limit, "swiglu_limit_shared": cfg.swiglu_limit_shared,
                    "router_scaling_factor": cfg.router_scaling_factor, "experts_touched": touched,
                    "parallelism": "single GPU"},
-        "tflops": fl / (ms_step * 1e-3) / 1e12,
-        "mfma_frac": fl / (ms_step * 1e-3) / BF16_PEAK,
-        "layer_gbs": by / (ms_step * 1e-3) / 1e9,
-        "hbm_frac": by / (ms_step * 1e-3) / HBM_PEAK,
-        "layer_roofline_frac": max(fl / BF16_PEAK, by / HBM_PEAK) / (ms_step * 1e-3),
-        "layer_forward_ms": layer_fwd_ms,
-        "roofline": {"kernel": "first projection + clipped SwiGLU of the routed experts "
-                               "(moe_expert_up, gg::kernel<0, true, 256, 256>)",
-                     "bound": "hbm", "achieved": up_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": up_achieved / HBM_PEAK, "traffic": counter_traffic(wl), "avg_ms": up_ms,
-                     "algorithmic_bytes": up_bytes},
     }
+    res.update(layer_report(wl, r, peaks))
+    res["roofline"] = up_roofline(wl, r, peaks, counter_traffic(wl))
+    if peaks:
+        res["attainable_peaks"] = peaks
+
+    if args.step35_workload:
+        w35 = mi.WORKLOADS[args.step35_workload]
+        note(f"{w35.name}")
+        r35 = time_layer(args, w35, moe, torch, mi)
+        res["step35_prefill"] = dict(layer_report(w35, r35, peaks), workload=w35.name, experts_touched=r35["touched"],
+                                     first_projection=up_roofline(w35, r35, peaks, None))
 
     if args.fp8_workload:
         wf = mi.WORKLOADS[args.fp8_workload]
+        note(f"{wf.name}")
         rf = time_layer(args, wf, moe, torch, mi)
-        ub = up_kernel_bytes(wf, rf["touched"])
-        res["fp8"] = {"workload": wf.name, "experts_touched": rf["touched"], "ms_per_step": rf["ms_step"],
-                      "tokens_per_s": wf.T / (rf["ms_step"] * 1e-3),
-                      "tflops": layer_flops(wf, rf["touched"]) / (rf["ms_step"] * 1e-3) / 1e12,
-                      "layer_forward_ms": rf["layer_forward_ms"],
-                      "up_ms": rf["up_ms"], "up_gbs": ub / (rf["up_ms"] * 1e-3) / 1e9,
-                      "up_hbm_frac": ub / (rf["up_ms"] * 1e-3) / HBM_PEAK}
+        rep = layer_report(wf, rf, peaks)
+        fl = layer_flops(wf, rf["touched"])
+        rep["fp8_mfma_frac"] = fl / (rf["ms_step"] * 1e-3) / FP8_PEAK
+        res["fp8"] = dict(rep, workload=wf.name, experts_touched=rf["touched"],
+                          first_projection=up_roofline(wf, rf, peaks, None))
 
     if not args.no_balanced:
         note(f"{wl.name} with the static balanced routing")
@@ -199,20 +228,22 @@ def main():
         note(f"{we.name}: one expert-parallel rank's share ({we.cfg.num_experts} experts, {we.T} tokens)")
         r = time_layer(args, we, moe, torch, mi)
         fl = layer_flops(we, r["touched"])
-        up_fl = 2 * we.T * we.cfg.top_k * we.cfg.hidden_size * 2 * we.cfg.moe_intermediate_size
         res["ep_rank_proxy"] = {
             "workload": we.name, "experts": we.cfg.num_experts, "tokens": we.T, "experts_touched": r["touched"],
-            "layer_forward_ms": r["layer_forward_ms"], "tflops": fl / (r["layer_forward_ms"] * 1e-3) / 1e12,
-            "mfma_frac": fl / (r["layer_forward_ms"] * 1e-3) / BF16_PEAK,
-            "up_ms": r["up_ms"], "up_tflops": up_fl / (r["up_ms"] * 1e-3) / 1e12,
-            "up_mfma_frac": up_fl / (r["up_ms"] * 1e-3) / BF16_PEAK}
+            "ms_per_step": r["ms_step"], "tflops": fl / (r["ms_step"] * 1e-3) / 1e12,
+            "mfma_frac": fl / (r["ms_step"] * 1e-3) / BF16_PEAK,
+            "first_projection": up_roofline(we, r, peaks, None)}
 
     if not args.no_decode:
         note(f"decode workload {args.decode_workload}")
-        res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch)
+        res["decode"] = bench_decode(args, mi.WORKLOADS[args.decode_workload], moe, torch, peaks)
         if args.decode_half_workload:
-            note(f"decode workload {args.decode_half_workload}")
-            res["decode_half"] = bench_decode(args, mi.WORKLOADS[args.decode_half_workload], moe, torch)
+            base = mi.WORKLOADS[args.decode_half_workload]
+            bias, share = calibrate_hot_bias(base, moe, torch, mi)
+            note(f"decode with the hot bias calibrated to {bias:.4f} (hot share {share:.3f})")
+            rep = bench_decode(args, mi.workload(args.decode_half_workload, hot_bias=bias), moe, torch, peaks)
+            rep.update(hot_bias=bias, hot_share=share)
+            res["decode_half"] = rep
 
     if not args.no_cpu_baseline:
         note("CPU baseline (oracle on a token sample)")
@@ -221,14 +252,84 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def layer_report(wl, r, peaks):
+    """Whole-layer rates of a timed layer."""
+    fl, by = layer_flops(wl, r["touched"]), layer_bytes(wl, r["touched"])
+    s = r["ms_step"] * 1e-3
+    fp8 = wl.cfg.expert_dtype == "fp8"
+    rep = {"ms_per_step": r["ms_step"], "tokens_per_s": wl.T / s, "tflops": fl / s / 1e12,
+           "mfma_frac": fl / s / BF16_PEAK, "layer_gbs": by / s / 1e9, "hbm_frac": by / s / HBM_PEAK,
+           "layer_roofline_frac": max(fl / (FP8_PEAK if fp8 else BF16_PEAK), by / HBM_PEAK) / s,
+           "layer_forward_ms": r["layer_forward_ms"], "algorithmic_bytes": by, "flops": fl}
+    if peaks:
+        rep["hbm_frac_attainable"] = by / s / (peaks["hbm_gbs"] * 1e9)
+        if not fp8:
+            rep["mfma_frac_attainable"] = fl / s / (peaks["bf16_tflops"] * 1e12)
+    return rep
+
+
+def up_roofline(wl, r, peaks, traffic):
+    """The first projection's launch as the layer makes it: algorithmic bytes
+    per launch / its average duration (HIP events on its stream)."""
+    c = wl.cfg
+    fp8 = c.expert_dtype == "fp8"
+    b = up_kernel_bytes(wl, r["touched"])
+    fl = up_kernel_flops(wl)
+    s = r["up_ms"] * 1e-3
+    kern = ("f8::kernel<0> (FP8 routed experts' first projection + clipped SwiGLU + h quantisation)" if fp8 else
+            "gg::kernel<0, true, 256, 256> (routed experts' first projection + clipped SwiGLU"
+            + (", shared expert as one more group)" if shared_in_launch(c) else ")"))
+    out = {"kernel": kern, "bound": "hbm", "achieved": b / s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+           "frac": b / s / HBM_PEAK, "traffic": traffic, "avg_ms": r["up_ms"], "algorithmic_bytes": b,
+           "tflops": fl / s / 1e12, "mfma_frac": fl / s / (FP8_PEAK if fp8 else BF16_PEAK)}
+    if peaks:
+        out["frac_attainable"] = b / s / (peaks["hbm_gbs"] * 1e9)
+    return out
+
+
+def measure_peaks(torch):
+    """Attainable peaks on this chip: a device-to-device copy of 2 GiB (bytes
+    read + written per second, the median of 10) and the vendor library's
+    bf16 GEMM of 8192 x 8192 x 8192 (hipBLASLt through torch.matmul)."""
+    note("measuring attainable peaks (device copy, vendor bf16 GEMM)")
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts = []
+    for i in range(13):
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+    hbm = 2 * n / median(ts)
+    del src, dst
+    a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+    ts = []
+    for i in range(13):
+        ev[0].record()
+        torch.matmul(a, b)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+    gemm = 2 * 8192 ** 3 / median(ts)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_gbs": hbm / 1e9, "hbm_how": "device-to-device copy of 2 GiB, read + written bytes, median of 10",
+            "bf16_tflops": gemm / 1e12, "bf16_how": "torch.matmul (hipBLASLt) 8192^3 bf16, median of 10"}
+
+
 def time_layer(args, wl, moe, torch, mi):
-    """Warm up, then time args.steps steps, each one moe_layer_forward call
-    (the whole layer in one call: routing, permutation, both expert
-    projections with the shared expert, combine), bracketed by a
-    synchronisation on both sides.  Then, as a second timed region of as many
-    steps, the same layer through its separate entry points, with the routed
-    experts' first projection bracketed by HIP events on its stream: that
-    kernel's average duration for the roofline object."""
+    """Warm up, then time args.steps steps, each one moe_layer_forward call,
+    bracketed by a synchronisation on both sides.  Then, as a second timed
+    region of as many steps, the same layer through its separate entry points
+    (the same launches in the same order), with the first projection
+    bracketed by HIP events on its stream: that launch's average duration
+    for the roofline object."""
     dev = "cuda"
     cfg, T, k, H = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.hidden_size
     note(f"generating {wl.name} inputs")
@@ -240,12 +341,9 @@ def time_layer(args, wl, moe, torch, mi):
     counts = torch.empty((cfg.num_experts,), dtype=torch.int32, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     h = torch.empty(moe.moe_hidden_bytes(cfg, T), dtype=torch.uint8, device=dev)
-    # the separate entry points with the shared expert in launches of its own,
-    # as moe_layer_forward runs it at these sizes (on its side stream), so the
-    # routed experts' first projection is the same launch in both regions
-    fused = False
-    y_rows = torch.empty((T * k + (T if fused else 0), H), dtype=torch.float16, device=dev)
-    y_sh = None if fused else torch.empty((T, H), dtype=torch.float32, device=dev)
+    fused = shared_in_launch(cfg)
+    y_rows = moe.binding.expert_rows(cfg, T * k + (T if fused else 0), dev)
+    y_sh = None if fused or not cfg.share_expert_dim else torch.empty((T, H), dtype=torch.float32, device=dev)
     s13, s2 = inp.get("w13_scale"), inp.get("w2_scale")
     ws13, ws2 = (inp["ws13"], inp["ws2"]) if fused else (None, None)
 
@@ -261,9 +359,11 @@ def time_layer(args, wl, moe, torch, mi):
         moe.moe_expert_down(cfg, T, h, offsets, inp["w2"], s2, y_rows=y_rows, ws=ws, stream=stream, ws2=ws2)
         if fused:
             moe.moe_combine(cfg, y_rows, p2r, w, shared_rows=y_rows[T * k:], out=out, stream=stream)
-        else:
+        elif y_sh is not None:
             moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], y_shared=y_sh, ws=ws, stream=stream)
             moe.moe_combine(cfg, y_rows, p2r, w, y_sh, out=out, stream=stream)
+        else:
+            moe.moe_combine(cfg, y_rows, p2r, w, out=out, stream=stream)
 
     note(f"{wl.name}: warmup {args.warmup} + timed {args.steps} steps")
     warm_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -412,7 +512,44 @@ def time_train(args, wl, moe, torch, mi):
             "backward_hbm_frac": (grad_bytes + w_bytes) / (bwd * 1e-3) / HBM_PEAK}
 
 
-def bench_decode(args, wl, moe, torch):
+def hot_share(wl, moe, torch, inp):
+    """Share of the (token, slot) selections that go to the hot experts."""
+    ids, _ = moe.moe_route(wl.cfg, inp["x"], inp["w_router"], inp["router_bias"])
+    hot = torch.zeros(wl.cfg.num_experts, dtype=torch.bool, device="cuda")
+    hot[inp["hot_experts"]] = True
+    return float(hot[ids.long()].float().mean().item())
+
+
+def calibrate_hot_bias(wl, moe, torch, mi, target=0.5, tol=0.02):
+    """Bisection on the hot experts' bias until they take target +- tol of
+    the decode batch's selections (the routing itself runs on the GPU)."""
+    inp = mi.make_inputs(wl, "cuda", seed=0)
+    base = inp["router_bias"].clone()
+    base[inp["hot_experts"]] -= wl.hot_bias
+    lo, hi = 0.0, 1.0
+    bias, share = hi, 1.0
+    for _ in range(30):
+        bias = 0.5 * (lo + hi)
+        inp["router_bias"] = base.clone()
+        inp["router_bias"][inp["hot_experts"]] += bias
+        share = hot_share(wl, moe, torch, inp)
+        if abs(share - target) <= tol:
+            break
+        if share < target:
+            lo = bias
+        else:
+            hi = bias
+    del inp
+    torch.cuda.empty_cache()
+    return bias, share
+
+
+def bench_decode(args, wl, moe, torch, peaks):
+    """The decode layer call, one at a time: before each timed call an
+    untimed write of 1 GiB flushes the 256 MiB memory-side cache, so the
+    call streams its expert weights from HBM; the median of the per-call
+    HIP-event times.  The same for the call captured once in a HIP graph and
+    replayed."""
     import moe_inputs as mi
     inp = mi.make_inputs(wl, "cuda", seed=0)
     T, k, E, H = wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size
@@ -420,21 +557,27 @@ def bench_decode(args, wl, moe, torch):
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
     counts = torch.empty((E,), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     for _ in range(max(args.warmup, 3)):
         moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, expert_counts=counts, stream=stream)
     torch.cuda.synchronize()
     touched = int((counts > 0).sum().item())
     n = max(args.steps, 20)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(stream)
-    for _ in range(n):
-        moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, stream=stream)
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    us = ev[0].elapsed_time(ev[1]) * 1e3 / n
+
+    def timed(fn):
+        ts = []
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(n):
+            flush.fill_(1)
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        return median(ts)
+
+    us = timed(lambda: moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, stream=stream))
     by = layer_bytes(wl, touched)
-    # the same layer call captured once into a HIP graph and replayed, as a
-    # decode loop would run it (launch gaps removed; the work is identical)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -446,18 +589,16 @@ def bench_decode(args, wl, moe, torch):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(n):
-        g.replay()
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    us_graph = ev[0].elapsed_time(ev[1]) * 1e3 / n
-    del g, inp, ws
+    us_graph = timed(g.replay)
+    del g, inp, ws, flush
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "tokens": T, "experts_touched": touched, "us_per_step": us,
-            "tokens_per_s": T / (us * 1e-6), "gbs": by / (us * 1e-6) / 1e9, "hbm_frac": by / (us * 1e-6) / HBM_PEAK,
-            "us_per_step_graph": us_graph, "hbm_frac_graph": by / (us_graph * 1e-6) / HBM_PEAK,
-            "algorithmic_bytes": by}
+    rep = {"workload": wl.name, "tokens": T, "experts_touched": touched, "us_per_step": us,
+           "tokens_per_s": T / (us * 1e-6), "gbs": by / (us * 1e-6) / 1e9, "hbm_frac": by / (us * 1e-6) / HBM_PEAK,
+           "us_per_step_graph": us_graph, "hbm_frac_graph": by / (us_graph * 1e-6) / HBM_PEAK,
+           "algorithmic_bytes": by, "timing": "median of %d calls, 1 GiB written before each (untimed)" % n}
+    if peaks:
+        rep["hbm_frac_attainable"] = by / (us * 1e-6) / (peaks["hbm_gbs"] * 1e9)
+    return rep
 
 
 def cpu_baseline(args, wl, mi):

@@ -21,20 +21,13 @@
  *   checkpoint tensors (layers.{i}.moe.{proj}.weight [num_experts, ...]).
  *   The fused first projection holds the gate rows 0..I-1, then the up rows
  *   I..2I-1.
- * Streams: all work is enqueued on `stream`; no call waits for the device.
- *   Exception, with the same ordering: from 1024 tokens on, moe_layer_forward,
- *   moe_layer_forward_routed and moe_block_forward run the shared expert on a
- *   second stream of the device that the library owns, forked from `stream`
- *   by an event before routing and joined back by another before the
- *   combine, so the call's work still starts after and ends before the
- *   neighbouring work on `stream` (a HIP graph captures both).  Calls on one
- *   device share that stream; capturing on one host thread while another
- *   thread calls these entry points on the same device is not supported.
+ * Streams: all work is enqueued on `stream`, and only there; no call waits
+ *   for the device, so a HIP graph can capture any call.
  * Errors: arguments are checked before anything is launched; on an argument
- *   error nothing is written.  MOE_ERR_HIP reports a launch failure;
- *   faults inside kernels surface on the stream.
- * Threads: the only global state is that side stream and its two events
- *   (per device, created on first use under a lock); calls are thread-safe.
+ *   error nothing is written.  MOE_ERR_HIP reports a launch failure (the
+ *   launches before it stay queued on `stream`); faults inside kernels
+ *   surface on the stream.
+ * Threads: the library keeps no global mutable state; calls are thread-safe.
  *   Calls that share a workspace must be ordered on one stream.
  * Shapes: H % 64 == 0, I % 64 == 0, Is % 64 == 0 (or Is == 0), 1 <= k <= 32,
  *   k <= E <= 1024, T >= 0 (T == 0 is a no-op), T * k < 2^31, and, as x and
@@ -126,9 +119,15 @@ moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk
  * columns to E4M3FN (round to nearest even) with scale amax/448, or 1 for an
  * all-zero group, and both projections accumulate the exact code products
  * of each 128-wide block in fp32 before applying the two scales.
- * y_rows [T*k, H] fp16 (round to nearest even, saturating at +-65504),
- * unweighted, in row order: fp16 keeps 11 significant bits for the same
- * bytes as bf16, so the rows add at most 2^-11 relative rounding. */
+ * y_rows: T*k expert output rows, unweighted, in row order, each in the
+ * scaled-fp16 row format: H fp16 values (round to nearest even), then one
+ * int8 exponent e per 128 columns, then zero bytes up to a multiple of 16; the
+ * value is fp16 * 2^e.  The library picks e so that the group's largest
+ * magnitude scales into [2^14, 2^15) (rounding may carry it to 2^15), so no
+ * finite result overflows and every
+ * value keeps fp16's 11 significant bits relative to its group's largest
+ * (for the same bytes as bf16 rows plus 1/256).  moe_expert_rows_bytes()
+ * gives the size of n rows. */
 moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* x,
                                 const int32_t* expert_offsets, const int32_t* row_to_pair,
                                 const void* w13, const float* w13_scale,
@@ -161,6 +160,10 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t T, const void* h,
 /* Bytes of the h buffer moe_expert_up writes for T tokens (with room for
  * the shared expert's rows when it can run in the same launches). */
 moe_status_t moe_hidden_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes);
+/* Bytes of `rows` expert output rows in the scaled-fp16 row format of
+ * moe_grouped_swiglu (2 H + 16 ceil(H / 2048) bytes per row).  Pure host
+ * function. */
+moe_status_t moe_expert_rows_bytes(const moe_config_t* cfg, int64_t rows, size_t* bytes);
 
 /* Shared expert (MAX page, MoE section: always-on MLP of width
  * share_expert_dim, clipped with swiglu_limit_shared):
@@ -173,11 +176,12 @@ moe_status_t moe_shared_ffn(const moe_config_t* cfg, int64_t T, const void* x,
 
 /* Weighted combine (MAX page, MoE section: routed output plus the shared
  * expert's): out[t] = sum_j topk_w[t,j] * y_rows[pair_to_row[t*k+j]] + s[t]
- * accumulated in fp32 in slot order; y_rows [T*k,H] fp16 as written by the
- * routed experts.  The shared term s is y_shared (fp32 [T,H], from
- * moe_shared_ffn) or shared_rows (fp16 [T,H], the shared expert's rows
- * written by moe_expert_down, i.e. y_rows + T*k*H), or absent when both
- * are NULL; passing both is MOE_ERR_INVALID_ARGUMENT.  residual (fp32
+ * accumulated in fp32 in slot order; y_rows: T*k rows in the scaled-fp16
+ * row format, as written by the routed experts.  The shared term s is
+ * y_shared (fp32 [T,H], from moe_shared_ffn) or shared_rows (T rows in the
+ * same scaled format: the shared expert's rows written by moe_expert_down,
+ * i.e. y_rows + T*k rows), or absent when both are NULL; passing both is
+ * MOE_ERR_INVALID_ARGUMENT.  residual (fp32
  * [T,H], optional): the block's fp32 residual stream (AutoModel page,
  * benchmark table), added last, out[t] = residual[t] + (the sum above); out
  * may then be the residual buffer itself when out_dtype is fp32 (in-place
@@ -198,7 +202,10 @@ moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const float* resid,
                          float eps, void* x, hipStream_t stream);
 
 /* The whole layer: route, permute, routed experts, shared expert, combine.
- * Inputs as above (ws13/ws2 may be NULL when share_expert_dim == 0).
+ * Inputs as above (ws13/ws2 may be NULL when share_expert_dim == 0).  With
+ * bf16 experts and share_expert_dim == moe_intermediate_size the shared
+ * expert runs as one more group of the routed experts' launches, else in
+ * launches of its own after them.
  * out [T,H] in out_dtype.  Optional outputs (NULL to skip): topk_ids_out
  * [T,k], topk_w_out [T,k], expert_counts_out [E]. */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x,
@@ -284,7 +291,7 @@ moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, int64_t T, siz
  * owned device memory of moe_saved_bytes, to be passed unchanged to
  * moe_layer_backward) the expert choice, the weights, the chosen raw scores,
  * the permutation, the first projection's pre-activations (bf16), h (bf16)
- * and the expert output rows (fp16).  The activation is applied to the
+ * and the expert output rows (scaled fp16).  The activation is applied to the
  * bf16-rounded pre-activations it keeps, so the backward differentiates the
  * function that ran.  topk_ids_in [T,k] int32 (optional): a replayed choice
  * (see moe_route_replay; router_bias may then be NULL).  ws: moe_workspace_size. */

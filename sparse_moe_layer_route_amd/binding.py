@@ -22,7 +22,7 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ER
 MOE_BF16, MOE_FP32, MOE_FP8_E4M3_B128 = range(3)
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_expert_up",
-            "moe_expert_down", "moe_hidden_bytes", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
+            "moe_expert_down", "moe_hidden_bytes", "moe_expert_rows_bytes", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
             "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_rmsnorm", "moe_block_forward",
             "moe_saved_bytes", "moe_backward_workspace_size", "moe_layer_forward_train", "moe_layer_backward",
             "moe_status_string")
@@ -66,6 +66,7 @@ def load(path: Optional[str] = None):
         "moe_expert_up": [C, I64, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_down": [C, I64, P, P, P, P, P, P, P, SZ, P],
         "moe_hidden_bytes": [C, I64, ctypes.POINTER(SZ)],
+        "moe_expert_rows_bytes": [C, I64, ctypes.POINTER(SZ)],
         "moe_shared_ffn": [C, I64, P, P, P, P, P, SZ, P],
         "moe_combine": [C, I64, P, P, P, P, P, P, P, P],
         "moe_rmsnorm": [C, I64, P, P, ctypes.c_float, P, P],
@@ -207,11 +208,30 @@ def moe_permute(cfg, topk_ids, ws=None, stream=None):
     return counts, offsets, r2p, p2r
 
 
+def moe_expert_rows_bytes(cfg, rows: int) -> int:
+    """Bytes of ``rows`` expert output rows (scaled fp16 row format)."""
+    n = ctypes.c_size_t(0)
+    c = make_config(cfg)
+    _check(load().moe_expert_rows_bytes(ctypes.byref(c), rows, ctypes.byref(n)), "moe_expert_rows_bytes")
+    return n.value
+
+
+def expert_rows(cfg, rows: int, device) -> torch.Tensor:
+    """A uint8 [rows, row bytes] tensor for expert output rows."""
+    return torch.empty((rows, moe_expert_rows_bytes(cfg, 1)), dtype=torch.uint8, device=device)
+
+
+def _rows_ptr(cfg, t, rows, name):
+    return _ptr(t, torch.uint8, (rows, moe_expert_rows_bytes(cfg, 1)), name)
+
+
 def moe_grouped_swiglu(cfg, x, expert_offsets, row_to_pair, w13, w2, w13_scale=None, w2_scale=None,
                        y_rows=None, ws=None, stream=None):
+    """Both projections of the routed experts; y_rows: T*k expert output rows
+    (uint8 [T*k, row bytes], scaled fp16 row format)."""
     T, H, E, k, I = x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size
     wdt = _weights_dtype(cfg)
-    y_rows = y_rows if y_rows is not None else torch.empty((T * k, H), dtype=torch.float16, device=x.device)
+    y_rows = y_rows if y_rows is not None else expert_rows(cfg, T * k, x.device)
     ws = ws if ws is not None else workspace(cfg, T, x.device)
     fp8 = cfg.expert_dtype == "fp8"
     c = make_config(cfg)
@@ -223,7 +243,7 @@ def moe_grouped_swiglu(cfg, x, expert_offsets, row_to_pair, w13, w2, w13_scale=N
         _ptr(w13_scale, torch.float32, (E, 2 * I // 128, H // 128) if fp8 else None, "w13_scale"),
         _ptr(w2, wdt, (E, H, I), "w2"),
         _ptr(w2_scale, torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
-        _ptr(y_rows, torch.float16, (T * k, H), "y_rows"),
+        _rows_ptr(cfg, y_rows, T * k, "y_rows"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_grouped_swiglu")
     return y_rows
@@ -270,14 +290,15 @@ def moe_expert_up(cfg, x, expert_offsets, row_to_pair, w13, w13_scale=None, h=No
 
 
 def moe_expert_down(cfg, T, h, expert_offsets, w2, w2_scale=None, y_rows=None, ws=None, stream=None, ws2=None):
-    """Second projection: y_rows [T*k, H] fp16 (with ws2: [T*k + T, H], the
-    shared expert's rows last)."""
+    """Second projection: T*k expert output rows (with ws2: T*k + T, the
+    shared expert's rows last), uint8 [rows, row bytes] in the scaled fp16
+    row format."""
     H, E, k, I = cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size
     fp8 = cfg.expert_dtype == "fp8"
     if h.numel() * h.element_size() < moe_hidden_bytes(cfg, T):
         raise ValueError("h is smaller than moe_hidden_bytes()")
     rows = T * k + (T if ws2 is not None else 0)
-    y_rows = y_rows if y_rows is not None else torch.empty((rows, H), dtype=torch.float16, device=h.device)
+    y_rows = y_rows if y_rows is not None else expert_rows(cfg, rows, h.device)
     ws = ws if ws is not None else workspace(cfg, T, h.device)
     c = make_config(cfg)
     Is = cfg.share_expert_dim
@@ -287,7 +308,7 @@ def moe_expert_down(cfg, T, h, expert_offsets, w2, w2_scale=None, y_rows=None, w
         _ptr(w2, _weights_dtype(cfg), (E, H, I), "w2"),
         _ptr(w2_scale, torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
         _ptr(ws2, torch.bfloat16, (H, Is), "ws2"),
-        _ptr(y_rows, torch.float16, (rows, H), "y_rows"),
+        _rows_ptr(cfg, y_rows, rows, "y_rows"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_expert_down")
     return y_rows
@@ -313,19 +334,21 @@ def _out_dtype(cfg):
 
 def moe_combine(cfg, y_rows, pair_to_row, topk_w, y_shared=None, out=None, stream=None, shared_rows=None,
                 residual=None):
-    """y_rows: at least T*k rows of [H] fp16 (the routed rows come first);
-    the shared term is y_shared (fp32 [T, H]) or shared_rows (fp16 [T, H]);
-    residual (fp32 [T, H]) is added last and may also be ``out``."""
+    """y_rows: at least T*k expert output rows (uint8 [rows, row bytes], the
+    routed rows first); the shared term is y_shared (fp32 [T, H]) or
+    shared_rows (T rows of the same format); residual (fp32 [T, H]) is added
+    last and may also be ``out``."""
     T, H, k = topk_w.shape[0], cfg.hidden_size, cfg.top_k
-    if y_rows.dim() != 2 or y_rows.shape[0] < T * k or y_rows.shape[1] != H:
-        raise ValueError(f"y_rows must be [>= {T * k}, {H}] (got {tuple(y_rows.shape)})")
+    rb = moe_expert_rows_bytes(cfg, 1)
+    if y_rows.dim() != 2 or y_rows.shape[0] < T * k or y_rows.shape[1] != rb or y_rows.dtype != torch.uint8:
+        raise ValueError(f"y_rows must be uint8 [>= {T * k}, {rb}] (got {tuple(y_rows.shape)} {y_rows.dtype})")
     out = out if out is not None else torch.empty((T, H), dtype=_out_dtype(cfg), device=y_rows.device)
     c = make_config(cfg)
-    st = load().moe_combine(ctypes.byref(c), T, _ptr(y_rows, torch.float16, None, "y_rows"),
+    st = load().moe_combine(ctypes.byref(c), T, _ptr(y_rows, torch.uint8, None, "y_rows"),
                             _ptr(pair_to_row, torch.int32, (T * k,), "pair_to_row"),
                             _ptr(topk_w, torch.float32, (T, k), "topk_w"),
                             _ptr(y_shared, torch.float32, (T, H), "y_shared"),
-                            _ptr(shared_rows, torch.float16, (T, H), "shared_rows"),
+                            _ptr(shared_rows, torch.uint8, (T, rb), "shared_rows"),
                             _ptr(residual, torch.float32, (T, H), "residual"),
                             _ptr(out, _out_dtype(cfg), (T, H), "out"), _stream(stream))
     _check(st, "moe_combine")

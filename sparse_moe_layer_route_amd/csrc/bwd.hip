@@ -17,7 +17,7 @@ namespace moe {
 // One block (256 threads) per token: the k dot products dout . y_j (block
 // sums in slot order), the bf16 dy rows, and da.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ dout,
-                                                       const _Float16* __restrict__ y_rows,
+                                                       const char* __restrict__ y_rows,
                                                        const int32_t* __restrict__ p2r, const float* __restrict__ w,
                                                        const float* __restrict__ s_raw, float scale, int norm,
                                                        int shared, uint16_t* __restrict__ dy, float* __restrict__ da,
@@ -31,14 +31,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     for (int j = 0; j < k; ++j) {
         const int64_t r = p2r[(int64_t)t * k + j];
         const float wj = w[(int64_t)t * k + j];
-        const _Float16* y = y_rows + r * H;
+        const char* y = y_rows + r * yrow_bytes(H);
         uint16_t* o = dy + r * H;
         float acc = 0.f;
         for (int h = tid * 4; h < H; h += 256 * 4) {
             const float4 dv = *(const float4*)(d + h);
             typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-            const f16x4 yv = *(const f16x4*)(y + h);
-            acc += dv.x * (float)yv[0] + dv.y * (float)yv[1] + dv.z * (float)yv[2] + dv.w * (float)yv[3];
+            const f16x4 yv = *(const f16x4*)(y + 2 * h);
+            const float sc = exp2_int((signed char)y[2 * H + (h >> 7)]);
+            acc += (dv.x * (float)yv[0] + dv.y * (float)yv[1] + dv.z * (float)yv[2] + dv.w * (float)yv[3]) * sc;
             uint2 q;
             q.x = pack_bf16x2(wj * dv.x, wj * dv.y);
             q.y = pack_bf16x2(wj * dv.z, wj * dv.w);
@@ -151,7 +152,7 @@ hipError_t launch_bwd_prep(const float* dout, const void* y_rows, const int32_t*
                            const float* s_raw, float scale, int norm, bool shared, void* dy, float* da, int T,
                            int H, int k, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    bwd_prep_kernel<<<T, 256, 0, s>>>(dout, (const _Float16*)y_rows, p2r, w, s_raw, scale, norm, shared ? 1 : 0,
+    bwd_prep_kernel<<<T, 256, 0, s>>>(dout, (const char*)y_rows, p2r, w, s_raw, scale, norm, shared ? 1 : 0,
                                       (uint16_t*)dy, da, T, H, k);
     return hipGetLastError();
 }

@@ -65,10 +65,11 @@ struct Params {
     const float* Ws;            // weight scales [groups][Nw/128][K/128]
     int64_t w_group_stride;     // bytes between groups' weights
     int64_t ws_group_stride;    // floats between groups' scales
-    void* C;                    // SWIGLU: h codes [rows][N]; OUT_F16: fp16 [rows][N]
+    void* C;                    // SWIGLU: h codes [rows][N]; OUT_F16: scaled fp16 rows of c_row_bytes
     float* Cs;                  // SWIGLU: h scales [N/128][c_ld]
     int c_ld;
     int N, K;
+    int64_t c_row_bytes;
     float limit;
     const int32_t* offsets;
     const int32_t* tile_start;
@@ -362,17 +363,47 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             }
         }
     } else {
-        _Float16* Y = (_Float16*)p.C;
+        // scaled fp16 rows: a 128-column exponent group is two waves along N;
+        // each row's largest magnitude over the wave's 64 columns goes
+        // through LDS to its partner wave
+        float* red = (float*)smem;                              // [128 rows][4 waves along N]
+        __syncthreads();                                       // every wave is done with the ring
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int lr = 16 * (wm + 2 * i) + crow + v;
+                float m = 0.f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n_tile * BN + 64 * wn + 16 * j + ccol;
+                    if (i < n_i && lr < valid && col < p.N) m = fmaxf(m, fabsf(acc[i][j][v]));
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));   // the row's 16 lanes
+                if (ccol == 0) red[lr * 4 + wn] = m;
+            }
+        __syncthreads();
+        const int gw = wn & ~1;                                 // first wave of this wave's group
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if (i >= n_i) continue;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = n_tile * BN + 64 * wn + 16 * j + ccol;
+            for (int v = 0; v < 4; ++v) {
+                const int lr = 16 * (wm + 2 * i) + crow + v;
+                if (lr >= valid) continue;
+                const int ex = yrow_exp(fmaxf(red[lr * 4 + gw], red[lr * 4 + gw + 1]));
+                const float sc = exp2_int(-ex);
+                char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int lr = 16 * (wm + 2 * i) + crow + v;
-                    if (lr < valid && col < p.N) Y[(int64_t)(row0 + lr) * p.N + col] = f32_to_f16_sat(acc[i][j][v]);
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n_tile * BN + 64 * wn + 16 * j + ccol;
+                    if (col < p.N) *(_Float16*)(row + 2 * col) = (_Float16)(acc[i][j][v] * sc);
+                }
+                const int gcol = n_tile * BN + 64 * gw;
+                if (wn == gw && ccol == 0 && gcol < p.N) {
+                    row[2 * p.N + (gcol >> 7)] = (char)ex;
+                    if (gcol == 0) yrow_zero_pad(row, p.N);
                 }
             }
         }
@@ -469,6 +500,7 @@ hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows,
     p.C = y;
     p.N = N;
     p.K = K;
+    p.c_row_bytes = yrow_bytes(N);
     p.offsets = offsets;
     p.tile_start = tile_start;
     p.groups = groups;

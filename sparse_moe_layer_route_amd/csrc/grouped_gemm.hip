@@ -36,9 +36,14 @@
 //     tiles past the expert's last row skip their MFMAs.
 //   * A rows are gathered straight from x by the DMA (row_to_pair / k); no
 //     permuted copy of x is written.
-//   * Work order: (expert, m-tile, n-tile) with n fastest, so the n-tiles
-//     that read one m-tile's gathered rows run together; each XCD (blocks b
-//     with b % 8 == x) takes a contiguous range of that list.
+//   * Work order: (expert, n-tile, m-tile) with m fastest, so the m-tiles
+//     that stream one weight panel are dispatched together and share it in
+//     L2 (against n fastest: 2.34 -> 2.10 ms for the Step-5 prefill's first
+//     projection, whose experts of up to 705 rows take up to 3 m-tiles);
+//     each XCD (blocks b with b % 8 == x) takes a contiguous range of that
+//     list.  256-row launches read each item's (expert, first row, rows,
+//     n-tile) from a table a one-block launch writes first (one load instead
+//     of a binary search over the tile plan: 2.10 -> 2.02 ms).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -112,6 +117,8 @@ struct Params {
     const uint16_t* W_extra;
     float limit_extra;
     uint16_t* gu_out;           // SWIGLU (optional): the pre-activations [rows][2N] bf16, gate then up
+    const int4* items;          // grouped (optional): per work item {group, first row, rows, n-tile}
+    int64_t c_row_bytes;        // OUT_F16: bytes per output row (scaled fp16 rows)
     int rot_group;              // dense (>= 0): take the K rotation of group rot_group, so a dense
                                 // launch adds in the order of that group's grouped launch
 };
@@ -184,26 +191,34 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     const int wm = wave / S::WN, wn = wave % S::WN;
 
     // ---- decode the work item ------------------------------------------
-    int g = 0, m_tile, n_tile, row0, row_end;
+    int g = 0, m_tile = 0, n_tile, row0, row_end;
     if (GROUPED) {
-        // group owning work item w: largest g with tile_start[g]*n_tiles <= w
-        int lo = 0, hi = p.groups + (p.extra_rows > 0 ? 1 : 0) - 1;
-        while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
-            if (p.tile_start[mid] * p.n_tiles <= w) lo = mid; else hi = mid - 1;
+        if (p.items) {
+            const int4 d = p.items[w];
+            g = __builtin_amdgcn_readfirstlane(d.x);
+            row0 = __builtin_amdgcn_readfirstlane(d.y);
+            row_end = row0 + __builtin_amdgcn_readfirstlane(d.z);
+            n_tile = __builtin_amdgcn_readfirstlane(d.w);
+        } else {
+            // group owning work item w: largest g with tile_start[g]*n_tiles <= w
+            int lo = 0, hi = p.groups + (p.extra_rows > 0 ? 1 : 0) - 1;
+            while (lo < hi) {
+                int mid = (lo + hi + 1) >> 1;
+                if (p.tile_start[mid] * p.n_tiles <= w) lo = mid; else hi = mid - 1;
+            }
+            g = lo;
+            const int mt = p.tile_start[g + 1] - p.tile_start[g];
+            const int local = w - p.tile_start[g] * p.n_tiles;
+            n_tile = local / mt;
+            m_tile = local % mt;
+            // the group's rows are split evenly over its mt tiles (each at most
+            // BM rows, as mt = ceil(rows / BM)): the m-tiles of one weight panel
+            // then do the same work at the same pace
+            const int base = p.offsets[g];
+            const int cnt = (g < p.groups ? p.offsets[g + 1] : base + p.extra_rows) - base;
+            row0 = base + (int)(((int64_t)m_tile * cnt) / mt);
+            row_end = base + (int)(((int64_t)(m_tile + 1) * cnt) / mt);
         }
-        g = lo;
-        const int mt = p.tile_start[g + 1] - p.tile_start[g];
-        const int local = w - p.tile_start[g] * p.n_tiles;
-        m_tile = local / p.n_tiles;
-        n_tile = local % p.n_tiles;
-        // the group's rows are split evenly over its mt tiles (each at most
-        // BM rows, as mt = ceil(rows / BM)): the m-tiles of one weight panel
-        // then do the same work at the same pace
-        const int base = p.offsets[g];
-        const int cnt = (g < p.groups ? p.offsets[g + 1] : base + p.extra_rows) - base;
-        row0 = base + (int)(((int64_t)m_tile * cnt) / mt);
-        row_end = base + (int)(((int64_t)(m_tile + 1) * cnt) / mt);
     } else {
         const int mt = (p.M + BM - 1) / BM;
         n_tile = w / mt;
@@ -634,17 +649,32 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                 for (int q = 0; q < EPI_ROWS * PER_ROW / NT; ++q) {
                     const int pr = tid / PER_ROW + (NT / PER_ROW) * q;
                     const int lr = EPI_ROWS * pass + pr;
-                    if (lr < valid && col < p.N) {
-                        const float* sv = &stage[pr * PITCH + c];
-                        const int64_t r = row0 + lr;
-                        if (MODE == OUT_F32) {
-                            *(float4*)((float*)p.C + r * p.N + col) = *(const float4*)sv;
-                        } else {
+                    const bool ok = lr < valid && col < p.N;
+                    const float* sv = &stage[pr * PITCH + c];
+                    const int64_t r = row0 + lr;
+                    if (MODE == OUT_F32) {
+                        if (ok) *(float4*)((float*)p.C + r * p.N + col) = *(const float4*)sv;
+                    } else {
+                        // scaled fp16 row: the 16 lanes of one 128-column group
+                        // agree on its exponent
+                        float m = 0.f;
+                        if (ok) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(sv[e]));
+                        }
+#pragma unroll
+                        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+                        const int ex = yrow_exp(m);
+                        const float sc = exp2_int(-ex);
+                        if (ok) {
                             typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
                             f16x8 h8;
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) h8[e] = f32_to_f16_sat(sv[e]);
-                            *(f16x8*)((_Float16*)p.C + r * p.N + col) = h8;
+                            for (int e = 0; e < 8; ++e) h8[e] = (_Float16)(sv[e] * sc);
+                            char* row = (char*)p.C + r * p.c_row_bytes;
+                            *(f16x8*)(row + 2 * col) = h8;
+                            if ((col & 127) == 0) row[2 * p.N + (col >> 7)] = (char)ex;
+                            if (col == 0) yrow_zero_pad(row, p.N);
                         }
                     }
                 }
@@ -680,7 +710,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                 }
             }
         }
-    } else {
+    } else if (MODE == OUT_F32) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if (i >= n_i) continue;
@@ -690,12 +720,53 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int lr = 16 * (wm + S::WM * i) + crow + v;
-                    if (lr < valid && col < p.N) {
-                        if (MODE == OUT_F32)
-                            ((float*)p.C)[(int64_t)(row0 + lr) * p.N + col] = acc[i][j][v];
-                        else
-                            ((_Float16*)p.C)[(int64_t)(row0 + lr) * p.N + col] = f32_to_f16_sat(acc[i][j][v]);
-                    }
+                    if (lr < valid && col < p.N) ((float*)p.C)[(int64_t)(row0 + lr) * p.N + col] = acc[i][j][v];
+                }
+            }
+        }
+    } else if constexpr (BM == 64 && BN == 128 && S::WM == 1) {
+        // scaled fp16 rows (64-row tiles, 128 columns = one exponent group
+        // per tile): each row's largest magnitude over the wave's columns,
+        // then over the waves through LDS, sets the group's exponent
+        float* red = (float*)smem;                 // [NW waves][64 rows]
+        __syncthreads();                           // every wave is done with the operand ring
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float m = 0.f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n_tile * BN + S::GW * wn + 16 * j + ccol;
+                    const int lr = 16 * i + crow + v;
+                    if (i < n_i && lr < valid && col < p.N) m = fmaxf(m, fabsf(acc[i][j][v]));
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+                if (ccol == 0) red[wave * 64 + 16 * i + crow + v] = m;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i >= n_i) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int lr = 16 * i + crow + v;
+                if (lr >= valid) continue;
+                float m = 0.f;
+#pragma unroll
+                for (int w8 = 0; w8 < NW; ++w8) m = fmaxf(m, red[w8 * 64 + lr]);
+                const int ex = yrow_exp(m);
+                const float sc = exp2_int(-ex);
+                char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n_tile * BN + S::GW * wn + 16 * j + ccol;
+                    if (col < p.N) *(_Float16*)(row + 2 * col) = (_Float16)(acc[i][j][v] * sc);
+                }
+                if (wave == 0 && ccol == 0) {
+                    row[2 * p.N + n_tile] = (char)ex;
+                    if (n_tile == 0) yrow_zero_pad(row, p.N);
                 }
             }
         }
@@ -710,6 +781,7 @@ template <int MODE, bool GROUPED, int BM, int BN>
 __global__ __launch_bounds__((Shape<BM, BN>::NT), 1) void kernel(Params p) {
     using S = Shape<BM, BN>;
     static_assert(!is_swiglu(MODE) || S::TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
+    static_assert(MODE != OUT_F16 || BM == 256 || (BM == 64 && BN == 128), "scaled fp16 rows: 256-row or 64 x 128 tiles");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
     const Segments sg = segments<GROUPED, BM>(p);
     const int xcd = blockIdx.x % NXCD, slots = gridDim.x / NXCD;
@@ -735,15 +807,52 @@ static int grid_blocks(int64_t work) {
     return (int)(per * NXCD);
 }
 
+// The work items of a grouped launch, {group, first row, rows, n-tile}, in
+// the kernel's order: group-major, then n-tile, then m-tile.  A group's rows
+// are split evenly over its m-tiles (each at most bm rows, as the tile plan
+// counts ceil(rows / bm) of them), so the m-tiles that share a weight panel
+// do the same work at the same pace.  One block of 1024 threads; each thread
+// takes m-tiles (its group found by a binary search of the tile plan in LDS)
+// and writes their n_tiles items.
+__global__ __launch_bounds__(1024) void item_table_kernel(const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ tile_start, int groups,
+                                                         int extra_rows, int n_tiles, int4* __restrict__ items) {
+    __shared__ int32_t ts[1026];
+    const int ng = groups + (extra_rows > 0 ? 1 : 0);
+    for (int g = threadIdx.x; g <= ng; g += blockDim.x) ts[g] = tile_start[g];
+    __syncthreads();
+    const int total = ts[ng];
+    for (int i = threadIdx.x; i < total; i += blockDim.x) {
+        int lo = 0, hi = ng - 1;                // the group g with ts[g] <= i < ts[g + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (ts[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        const int g = lo, t0 = ts[g], mt = ts[g + 1] - t0, m = i - t0;
+        const int base = offsets[min(g, groups)];
+        const int cnt = (g < groups ? offsets[g + 1] : base + extra_rows) - base;
+        const int a = (int)(((int64_t)m * cnt) / mt), b = (int)(((int64_t)(m + 1) * cnt) / mt);
+        int4* out = items + (int64_t)t0 * n_tiles + m;
+        for (int n = 0; n < n_tiles; ++n) out[n * mt] = make_int4(g, base + a, b - a, n);
+    }
+}
+
 template <int MODE, int BM, int BN>
 void launch(Params p, int64_t tiles, hipStream_t s) {
     p.n_tiles = is_swiglu(MODE) ? (2 * p.N + BN - 1) / BN : (p.N + BN - 1) / BN;
+    if (p.items) {
+        item_table_kernel<<<1, 1024, 0, s>>>(p.offsets, p.tile_start, p.groups, p.extra_rows, p.n_tiles,
+                                             (int4*)p.items);
+    }
     const int nb = grid_blocks(tiles * p.n_tiles);
     if (p.offsets) kernel<MODE, true, BM, BN><<<nb, Shape<BM, BN>::NT, 0, s>>>(p);
     else kernel<MODE, false, BM, BN><<<nb, Shape<BM, BN>::NT, 0, s>>>(p);
 }
 
 }  // namespace gg
+
+size_t grouped_item_bytes(int64_t max_tiles, int n_tiles) { return (size_t)max_tiles * n_tiles * 16; }
+int64_t expert_row_bytes(int H) { return yrow_bytes(H); }
 
 int grouped_tile_m(int64_t rows, int groups) {
     // 64-row tiles when the groups average under 48 rows (decode-like
@@ -772,6 +881,7 @@ hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s) {
     p.limit_extra = a.limit_extra;
     p.gu_out = (uint16_t*)a.gu_out;
     p.rot_group = a.rot_group;
+    p.items = (a.bm == 256 && a.offsets) ? (const int4*)a.items : nullptr;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
     // 256-row tiles address gathered A rows and one group's weights by 32-bit
@@ -807,6 +917,8 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s)
     p.extra_rows = a.extra_rows;
     p.W_extra = (const uint16_t*)a.W_extra;
     p.rot_group = a.rot_group;
+    p.items = (a.bm == 256 && a.offsets) ? (const int4*)a.items : nullptr;
+    p.c_row_bytes = yrow_bytes(a.N);
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
     if (a.bm == 256 && (int64_t)a.N * a.K * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;

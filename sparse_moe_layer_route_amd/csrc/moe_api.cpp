@@ -6,7 +6,6 @@
 #include <math.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "moe_internal.h"
 
@@ -63,10 +62,21 @@ Dims dims(const moe_config_t* c, int64_t T) {
                 c->share_expert_dim, c->expert_dtype == MOE_FP8_E4M3_B128};
 }
 
+int tile_m(const Dims& d);
+
 // scratch each step needs at the start of the workspace it is handed
 size_t route_ws(const Dims& d) { return align_up((size_t)moe::router_splits(d.T, d.H) * d.T * d.E * 4); }
 size_t permute_ws(const Dims& d) { return align_up(moe::permute_scratch_bytes(d.P, d.E)); }
-size_t plan_ws(const Dims& d) { return align_up((size_t)(d.E + 2) * 4); }
+// the tile plan, then (256-row tiles) the work-item table of the grouped
+// launches, sized for the larger of the two projections' column-tile counts
+// and for the shared expert as one more group
+size_t plan_head(const Dims& d) { return align_up((size_t)(d.E + 2) * 4); }
+int64_t max_tiles(const Dims& d, bool extra);
+size_t item_ws(const Dims& d) {
+    const int n_up = (2 * d.I + 255) / 256, n_down = (d.H + 255) / 256;
+    return align_up(moe::grouped_item_bytes(max_tiles(d, true), std::max(n_up, n_down)));
+}
+size_t plan_ws(const Dims& d) { return plan_head(d) + item_ws(d); }
 // FP8: x quantised per token, codes [T, H] then scales [H/128][T]
 size_t xq_bytes(const Dims& d) { return align_up((size_t)d.T * d.H); }
 size_t xq_ws(const Dims& d) { return d.fp8 ? xq_bytes(d) + align_up((size_t)(d.H / 128) * d.T * 4) : 0; }
@@ -85,8 +95,10 @@ size_t shared_ws(const Dims& d) { return align_up((size_t)d.T * d.Is * 2); }
 
 // the whole layer: its own buffers followed by each step's scratch
 struct LayerWs {
-    size_t ids, w, counts, offsets, r2p, p2r, plan, x, y_rows, y_sh, h_sh, step, total;
+    size_t ids, w, counts, offsets, r2p, p2r, plan, x, y_rows, y_sh, step, total;
 };
+// bytes of one expert output row (H fp16 values + one exponent per 128 columns)
+size_t row_bytes(const Dims& d) { return (size_t)moe::expert_row_bytes(d.H); }
 
 LayerWs layer_ws(const Dims& d) {
     const bool fuse = fuse_shared(d);
@@ -101,9 +113,8 @@ LayerWs layer_ws(const Dims& d) {
     L.p2r = o;     o += align_up((size_t)d.P * 4);
     L.plan = o;    o += plan_ws(d);
     L.x = o;       o += align_up((size_t)d.T * d.H * 2);    // the normalised input (moe_block_forward)
-    L.y_rows = o;  o += align_up((size_t)rows * d.H * 2);
+    L.y_rows = o;  o += align_up((size_t)rows * row_bytes(d));
     L.y_sh = o;    o += (d.Is > 0 && !fuse) ? align_up((size_t)d.T * d.H * 4) : 0;
-    L.h_sh = o;    o += d.Is > 0 ? align_up((size_t)d.T * d.Is * 2) : 0;   // the shared expert's h (side stream)
     L.step = o;
     const size_t grouped = fuse ? align_up(hidden_bytes(d)) : grouped_ws(d);
     o += std::max(std::max(route_ws(d), permute_ws(d)), std::max(grouped, shared_ws(d)));
@@ -119,47 +130,6 @@ inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK :
         if (_st != MOE_OK) return _st;             \
     } while (0)
 #define HIP_TRY(expr) MOE_TRY(hip_status(expr))
-
-// ---- the shared expert on a side stream ------------------------------------
-// The shared expert needs only x, so the whole-layer entry points run it on
-// a second stream of the same device, forked from the caller's stream before
-// routing (events: the side stream waits for the caller's work so far, the
-// caller's stream waits for the shared expert before the combine), so that
-// its GEMMs fill the chip while the router, the selection and the
-// permutation run.  One side stream and event pair per device, default
-// priority; the fork (record, wait, launches, record) is made under a lock,
-// so calls from several host threads order correctly (a join may then wait
-// for a later call's shared expert too, never for less than its own).
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-SideStream g_side[64];
-
-// the side stream of the device `stream` belongs to (created there on first use)
-hipError_t side_stream(hipStream_t stream, SideStream** out) {
-    int dev = 0;
-    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    SideStream& ss = g_side[dev];
-    if (!ss.s) {
-        int cur = 0;
-        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
-        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-        e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
-        if (cur != dev) (void)hipSetDevice(cur);
-        if (e != hipSuccess) {
-            ss = SideStream{};
-            return e;
-        }
-    }
-    *out = &ss;
-    return hipSuccess;
-}
 
 // ---- the steps, without argument checks ----------------------------------
 
@@ -186,10 +156,12 @@ int tile_m(const Dims& d) { return d.fp8 ? moe::fp8_tile_m() : moe::grouped_tile
 
 // upper bound on the tiles of a grouped launch: every group may end in a
 // partial tile (the extra group holds T rows)
-int max_tiles(const Dims& d, bool extra = false) {
+int64_t max_tiles(const Dims& d, bool extra) {
     const int bm = tile_m(d);
-    return (int)((d.P + bm - 1) / bm) + d.E + (extra ? (int)((d.T + bm - 1) / bm) + 1 : 0);
+    return (d.P + bm - 1) / bm + d.E + (extra ? (d.T + bm - 1) / bm + 1 : 0);
 }
+// the work-item table sits right after the tile plan
+void* item_table(const Dims& d, const int32_t* tile_start) { return (char*)tile_start + plan_head(d); }
 
 // the bf16 grouped launches of the routed experts (optionally with the
 // shared expert as an extra group of T rows after the P routed rows)
@@ -212,7 +184,8 @@ moe::GroupedArgs up_args(const moe_config_t* c, const Dims& d, const void* x, co
     a.tile_start = tile_start;
     a.groups = d.E;
     a.bm = tile_m(d);
-    a.max_tiles = max_tiles(d, ws13 != nullptr);
+    a.max_tiles = (int)max_tiles(d, ws13 != nullptr);
+    a.items = item_table(d, tile_start);
     if (ws13) {
         a.extra_rows = (int)d.T;
         a.W_extra = ws13;
@@ -236,7 +209,8 @@ moe::GroupedArgs down_args(const Dims& d, const void* h, const int32_t* offsets,
     a.tile_start = tile_start;
     a.groups = d.E;
     a.bm = tile_m(d);
-    a.max_tiles = max_tiles(d, ws2 != nullptr);
+    a.max_tiles = (int)max_tiles(d, ws2 != nullptr);
+    a.items = item_table(d, tile_start);
     if (ws2) {
         a.extra_rows = (int)d.T;
         a.W_extra = ws2;
@@ -256,7 +230,7 @@ moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const in
         float* hs = (float*)((char*)h + hcode_bytes(d));
         HIP_TRY(moe::launch_quant_rows(x, (int)d.T, d.H, xq, xs, (int)d.T, s));
         HIP_TRY(moe::launch_fp8_up(xq, xs, (int)d.T, r2p, d.k, (int)d.T, w13, w13s, h, hs, (int)d.P, d.I, d.H,
-                                   c->swiglu_limit, offsets, tile_start, d.E, max_tiles(d), s));
+                                   c->swiglu_limit, offsets, tile_start, d.E, (int)max_tiles(d, false), s));
         return MOE_OK;
     }
     HIP_TRY(moe::launch_grouped_up(up_args(c, d, x, offsets, r2p, w13, h, tile_start, ws13), s));
@@ -273,7 +247,7 @@ moe_status_t do_down(const moe_config_t* c, const Dims& d, const void* h, const 
     if (d.fp8) {
         const float* hs = (const float*)((const char*)h + hcode_bytes(d));
         HIP_TRY(moe::launch_fp8_down(h, hs, (int)d.P, (int)d.P, w2, w2s, y_rows, d.H, d.I, offsets, tile_start,
-                                     d.E, max_tiles(d), s));
+                                     d.E, (int)max_tiles(d, false), s));
         return MOE_OK;
     }
     HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, s));
@@ -330,62 +304,14 @@ moe_status_t check_layer(const moe_config_t* cfg, int64_t T, const void* x, cons
     return MOE_OK;
 }
 
-// The side stream pays from prefill sizes on (Step-5, 8192 tokens: layer
-// 3.89 -> 3.86 ms); at decode the two streams' kernels and the cross-stream
-// waits cost more than the overlap gains (64 tokens: 296 -> 307 us), and the
-// shared expert stays one more group of the routed launches.
-bool side_shared(const Dims& d) { return d.Is > 0 && d.T >= 1024; }
-
-// the shared expert on the side stream: h_sh = act(ws13 . x) into L.h_sh,
-// then ws2 . h_sh.  Fused layout (Is == I, bf16 experts): fp16 rows after
-// the routed rows of y_rows, where the combine reads them, from dense
-// launches with the routed launches' tile height and the K order of group
-// E, the shared expert's group in those launches; otherwise fp32 rows in
-// L.y_sh from the launches moe_shared_ffn makes.  Either way the result is
-// bit for bit the one the separate entry points give.
-moe_status_t fork_shared(const moe_config_t* cfg, const Dims& d, const LayerWs& L, char* base, const void* x,
-                         const void* ws13, const void* ws2, hipStream_t stream, SideStream** side) {
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* ss = nullptr;
-    HIP_TRY(side_stream(stream, &ss));
-    HIP_TRY(hipEventRecord(ss->fork, stream));
-    HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
-    void* h_sh = base + L.h_sh;
-    moe::GroupedArgs a;
-    a.A = x;
-    a.a_nrows = (int)d.T;
-    a.W = ws13;
-    a.C = h_sh;
-    a.M = (int)d.T;
-    a.N = d.Is;
-    a.K = d.H;
-    a.limit = cfg->swiglu_limit_shared;
-    const bool fused = fuse_shared(d);
-    a.bm = fused ? tile_m(d) : (d.T <= 64 ? 64 : 256);
-    a.rot_group = fused ? d.E : -1;
-    HIP_TRY(moe::launch_grouped_up(a, ss->s));
-    moe::GroupedArgs b;
-    b.A = h_sh;
-    b.a_nrows = (int)d.T;
-    b.W = ws2;
-    b.C = fused ? (void*)(base + L.y_rows + (size_t)d.P * d.H * 2) : (void*)(base + L.y_sh);
-    b.M = (int)d.T;
-    b.N = d.H;
-    b.K = d.Is;
-    b.bm = a.bm;
-    b.rot_group = a.rot_group;
-    HIP_TRY(moe::launch_grouped_down(b, !fused, ss->s));
-    HIP_TRY(hipEventRecord(ss->join, ss->s));
-    *side = ss;
-    return MOE_OK;
-}
-
-// the layer after routing: permute, routed + shared experts, combine
+// the layer after routing: permute, routed + shared experts, combine.  The
+// shared expert runs as group E of the routed experts' launches when it has
+// their width and dtype (bf16, Is == I: both models), else in dense launches
+// of its own after them; everything is on the caller's stream.
 moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs& L, char* base, const void* x,
                            const int32_t* ids, const float* w, const void* w13, const float* w13_scale,
                            const void* w2, const float* w2_scale, const void* ws13, const void* ws2, void* out,
-                           int32_t* expert_counts_out, hipStream_t stream, const float* resid = nullptr,
-                           SideStream* side = nullptr) {
+                           int32_t* expert_counts_out, hipStream_t stream, const float* resid = nullptr) {
     const int T = (int)d.T;
     int32_t* counts = expert_counts_out ? expert_counts_out : (int32_t*)(base + L.counts);
     int32_t* offsets = (int32_t*)(base + L.offsets);
@@ -400,24 +326,18 @@ moe_status_t layer_experts(const moe_config_t* cfg, const Dims& d, const LayerWs
         // (at `step`) is still in use while the plan is made.
         int32_t* tile_start = (int32_t*)(base + L.plan);
         void* h = step;
-        // with a side stream the shared expert runs there (fork_shared),
-        // else as group E of the routed launches
-        HIP_TRY(moe::launch_permute_plan(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, tile_m(d),
-                                         side ? 0 : T, tile_start, stream));
-        HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, side ? nullptr : ws13),
-                                       stream));
-        HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, side ? nullptr : ws2),
-                                         false, stream));
-        if (side) HIP_TRY(hipStreamWaitEvent(stream, side->join, 0));
-        HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * d.H * 2, resid, out,
+        HIP_TRY(moe::launch_permute_plan(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, tile_m(d), T,
+                                         tile_start, stream));
+        HIP_TRY(moe::launch_grouped_up(up_args(cfg, d, x, offsets, r2p, w13, h, tile_start, ws13), stream));
+        HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, stream));
+        HIP_TRY(moe::launch_combine(y_rows, p2r, w, nullptr, y_rows + (size_t)d.P * row_bytes(d), resid, out,
                                     out_bf16, T, d.H, d.k, stream));
         return MOE_OK;
     }
     HIP_TRY(moe::launch_permute(ids, T, d.k, d.E, counts, offsets, r2p, p2r, step, stream));
     float* y_sh = d.Is > 0 ? (float*)(base + L.y_sh) : nullptr;
     MOE_TRY(do_grouped(cfg, d, x, offsets, r2p, w13, w13_scale, w2, w2_scale, y_rows, step, stream));
-    if (side) HIP_TRY(hipStreamWaitEvent(stream, side->join, 0));
-    else if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
+    if (d.Is > 0) MOE_TRY(do_shared(cfg, d, x, ws13, ws2, y_sh, step, stream));
     HIP_TRY(moe::launch_combine(y_rows, p2r, w, y_sh, nullptr, resid, out, out_bf16, T, d.H, d.k, stream));
     return MOE_OK;
 }
@@ -445,7 +365,7 @@ SavedWs saved_ws(const Dims& d) {
     S.p2r = o;     o += align_up((size_t)d.P * 4);
     S.gu = o;      o += align_up((size_t)rows * 2 * d.I * 2);
     S.h = o;       o += align_up((size_t)rows * d.I * 2);
-    S.y = o;       o += align_up((size_t)rows * d.H * 2);
+    S.y = o;       o += align_up((size_t)rows * row_bytes(d));
     S.total = o;
     return S;
 }
@@ -545,6 +465,13 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t T, const void* h, 
     return do_down(cfg, d, h, expert_offsets, w2, w2_scale, y_rows, (char*)ws, stream, ws2);
 }
 
+moe_status_t moe_expert_rows_bytes(const moe_config_t* cfg, int64_t rows, size_t* bytes) {
+    if (!bytes || rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_config(cfg, 0));
+    *bytes = (size_t)rows * (size_t)moe::expert_row_bytes(cfg->hidden_size);
+    return MOE_OK;
+}
+
 moe_status_t moe_hidden_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes) {
     if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
     MOE_TRY(check_config(cfg, T));
@@ -597,11 +524,9 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
     char* base = (char*)ws;
     int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
-    SideStream* side = nullptr;
-    if (side_shared(d)) MOE_TRY(fork_shared(cfg, d, L, base, x, ws13, ws2, stream, &side));
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
-                         expert_counts_out, stream, nullptr, side);
+                         expert_counts_out, stream);
 }
 
 moe_status_t moe_route_replay(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
@@ -634,11 +559,9 @@ moe_status_t moe_layer_forward_routed(const moe_config_t* cfg, int64_t T, const 
     LayerWs L = layer_ws(d);
     char* base = (char*)ws;
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
-    SideStream* side = nullptr;
-    if (side_shared(d)) MOE_TRY(fork_shared(cfg, d, L, base, x, ws13, ws2, stream, &side));
     MOE_TRY(do_replay(cfg, d, x, w_router, topk_ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, topk_ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
-                         expert_counts_out, stream, nullptr, side);
+                         expert_counts_out, stream);
 }
 
 moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* resid_in, const float* norm_weight,
@@ -659,11 +582,9 @@ moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* 
     HIP_TRY(moe::launch_rmsnorm(resid_in, norm_weight, eps, x, (int)T, d.H, stream));
     int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
-    SideStream* side = nullptr;
-    if (side_shared(d)) MOE_TRY(fork_shared(cfg, d, L, base, x, ws13, ws2, stream, &side));
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, resid_out,
-                         expert_counts_out, stream, resid_in, side);
+                         expert_counts_out, stream, resid_in);
 }
 
 moe_status_t moe_saved_bytes(const moe_config_t* cfg, int64_t T, size_t* bytes) {
@@ -723,7 +644,7 @@ moe_status_t moe_layer_forward_train(const moe_config_t* cfg, int64_t T, const v
     HIP_TRY(moe::launch_grouped_up(up, stream));
     HIP_TRY(moe::launch_grouped_down(down_args(d, sv + S.h, offsets, w2, sv + S.y, tile_start,
                                                shared ? ws2 : nullptr), false, stream));
-    HIP_TRY(moe::launch_combine(sv + S.y, p2r, w, nullptr, shared ? sv + S.y + (size_t)d.P * d.H * 2 : nullptr,
+    HIP_TRY(moe::launch_combine(sv + S.y, p2r, w, nullptr, shared ? sv + S.y + (size_t)d.P * row_bytes(d) : nullptr,
                                 nullptr, out, cfg->out_dtype == MOE_BF16, (int)T, d.H, d.k, stream));
     return MOE_OK;
 }

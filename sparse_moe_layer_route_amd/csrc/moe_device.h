@@ -34,6 +34,28 @@ __device__ __forceinline__ _Float16 f32_to_f16_sat(float f) {
     return (_Float16)c;
 }
 
+// ---- expert output rows: fp16 values with a power-of-two scale per 128 columns ----
+// A row of H values is H fp16 numbers, then one int8 exponent e per 128
+// columns (then zeros to a multiple of 16 bytes); value = fp16 * 2^e.  e
+// scales the group's largest magnitude into [2^14, 2^15) (rounding to fp16
+// may carry it to 2^15), so no finite value overflows and every
+// value keeps fp16's 11 significant bits relative to its group's largest
+// (scaling by a power of two commutes with the rounding, so where plain
+// fp16 neither overflows nor underflows the stored value is the same).
+__host__ __device__ __forceinline__ int64_t yrow_bytes(int H) { return 2 * (int64_t)H + ((H + 127) / 128 + 15) / 16 * 16; }
+// exponent for a group whose largest magnitude is amax (>= 0, NaN-free)
+__device__ __forceinline__ int yrow_exp(float amax) {
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;   // floor(log2 amax); -127 for 0 and subnormals
+    return min(max(ex - 14, -126), 113);
+}
+// zero the padding after a row's exponents (called by the thread that writes
+// the row's first exponent), so rows are fully defined bytes
+__device__ __forceinline__ void yrow_zero_pad(char* row, int H) {
+    for (int64_t b = 2 * (int64_t)H + (H + 127) / 128; b < yrow_bytes(H); ++b) row[b] = 0;
+}
+// 2^e for e in [-126, 127]
+__device__ __forceinline__ float exp2_int(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }

@@ -43,7 +43,7 @@ hipError_t launch_tile_plan(const int32_t* offsets, int E, int bm, int extra_row
 // Weight-streaming bf16 GEMMs (direct-to-LDS DMA ring).
 // Up: h[rows, N] bf16 = act(A[rows] . W13^T) with A rows gathered through
 // a_rows / a_div (clamped to a_nrows) or dense; W13 [2N, K] per group.
-// Down: C[rows, N] = A[rows, K] . W^T, C fp16 (saturating) or fp32.
+// Down: C[rows, N] = A[rows, K] . W^T, C scaled fp16 rows (expert_row_bytes(N) each) or fp32.
 // Grouped when offsets != nullptr (groups, tile_start from the plan with the
 // same bm, max_tiles bounds the plan); otherwise dense with M rows.  An extra
 // group (extra_rows > 0, grouped only) follows the groups: rows
@@ -66,7 +66,15 @@ struct GroupedArgs {
     float limit_extra = 0.f;
     void* gu_out = nullptr;          // first projection: also keep the pre-activations (bf16 [rows][2N])
     int rot_group = -1;              // dense launch: add over K in the order group rot_group's grouped launch uses
+    void* items = nullptr;           // grouped 256-row launches (optional): scratch for the work-item
+                                     // table, grouped_item_bytes(max_tiles, N, K-side) bytes
 };
+// bytes of the work-item table of a grouped 256-row launch with max_tiles
+// tiles over n_tiles column tiles
+size_t grouped_item_bytes(int64_t max_tiles, int n_tiles);
+// bytes of one expert output row of H columns: H fp16 values, then one int8
+// exponent per 128 columns (padded to 16 bytes); value = fp16 * 2^exponent
+int64_t expert_row_bytes(int H);
 int grouped_tile_m(int64_t rows, int groups);
 hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s);
@@ -76,7 +84,7 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s)
 // quant: xq[rows, H] E4M3 codes, xs[H/128][ld] fp32 scales (amax / 448).
 // up: hq[rows, N] codes + hs[N/128][hs_ld] scales of act(A . W13^T), A rows
 // gathered through a_rows / a_div; W13 [groups][2N, K] codes, w13s
-// [groups][2N/128][K/128].  down: y[rows, N] fp16 (saturating) = hq . W2^T.
+// [groups][2N/128][K/128].  down: y = hq . W2^T as scaled fp16 rows (expert_row_bytes(N) each).
 // K % 128 == 0, N % 128 == 0.
 int fp8_tile_m();
 hipError_t launch_quant_rows(const void* x, int rows, int H, void* xq, float* xs, int ld, hipStream_t s);
@@ -89,7 +97,7 @@ hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows,
                            int max_tiles, hipStream_t s);
 
 // ---- combine --------------------------------------------------------------
-// shared expert output: y_shared fp32 [T, H], or shared_rows fp16 [T, H], or neither
+// shared expert output: y_shared fp32 [T, H], or shared_rows (scaled fp16 rows), or neither
 // zero-centred RMSNorm of fp32 rows -> bf16 rows (H % 4 == 0)
 hipError_t launch_rmsnorm(const float* resid, const float* norm_weight, float eps, void* x, int T, int H,
                           hipStream_t s);

@@ -72,3 +72,36 @@ def max_err_over_rms(gpu_out, orc_out):
     orc_out = np.asarray(orc_out, dtype=np.float64)
     rms = np.sqrt((orc_out ** 2).mean())
     return float(np.abs(gpu_out - orc_out).max() / rms), rms
+
+
+def decode_rows(y_rows, H):
+    """Expert output rows in the scaled fp16 row format (uint8 [rows, row
+    bytes]: H fp16 values, then one int8 exponent per 128 columns) as
+    float64 [rows, H]: value = fp16 * 2^exponent."""
+    import torch
+    y = y_rows.cpu()
+    vals = y[:, :2 * H].contiguous().view(torch.float16).double().numpy()
+    G = (H + 127) // 128
+    ex = y[:, 2 * H:2 * H + G].contiguous().view(torch.int8).numpy().astype(np.int64)
+    return vals * np.exp2(np.repeat(ex, 128, axis=1)[:, :H].astype(np.float64))
+
+
+def tile_plan_sample(offsets, r2p, k, bm, rng, per_tile=1):
+    """Tokens whose rows reach every (expert, m-tile) work item of a grouped
+    launch with bm-row tiles (a group's rows split evenly over ceil(rows/bm)
+    tiles): the first and last row of every tile, ``per_tile`` random rows
+    of each, and every row of the largest expert.  Returns sorted unique
+    token indices."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    r2p = np.asarray(r2p, dtype=np.int64)
+    rows = []
+    cnt = np.diff(offsets)
+    for e in np.nonzero(cnt)[0]:
+        n, base = int(cnt[e]), int(offsets[e])
+        mt = (n + bm - 1) // bm
+        for m in range(mt):
+            a, b = base + m * n // mt, base + (m + 1) * n // mt
+            rows += [a, b - 1] + rng.integers(a, b, per_tile).tolist()
+    big = int(np.argmax(cnt))
+    rows += list(range(int(offsets[big]), int(offsets[big + 1])))
+    return np.unique(r2p[np.asarray(rows, dtype=np.int64)] // k)

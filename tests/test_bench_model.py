@@ -1,7 +1,9 @@
 """CPU: the benchmark's roofline accounting, pinned to numbers the pages print.
 
-bench.py prices the dominant kernel (the routed experts' first projection)
-and the whole layer by algorithmic bytes and flops.  The per-expert weight
+bench.py prices the dominant kernel (the routed experts' first projection,
+with the shared expert as one more group of the launch) and the whole layer
+by algorithmic bytes and flops: weights once, activations in once, outputs
+out once; intermediates (h, the expert rows) are not counted.  The per-expert weight
 sizes those formulas imply must be the expert tensors of 24 MiB (fused gate
 and up projection) and 12 MiB (down projection) in bf16 that the miles page
 lists for Step-5-Preview (section 5.3 Optimizer), at the Model Architecture
@@ -32,11 +34,13 @@ def test_expert_tensor_sizes_match_the_page():
 def test_first_projection_bytes():
     wl = mi.WORKLOADS["step5_prefill"]
     touched = 284
-    T, k = 8192, 8
+    T = 8192
     want = (touched * 24 * MIB          # W13 of every touched expert, once
-            + T * 4096 * 2              # x, once
-            + T * k * 1536 * 2)         # h of the routed rows, written once
-    assert bench.up_kernel_bytes(wl, touched) == want == 7_415_529_472
+            + 24 * MIB                  # the shared expert's, a group of the same launch
+            + T * 4096 * 2)             # x, once (h is an intermediate: not counted)
+    assert bench.up_kernel_bytes(wl, touched) == want == 7_239_368_704
+    # its flops: the routed pairs' and the shared expert's rows, gate and up
+    assert bench.up_kernel_flops(wl) == 2 * (T * 8 + T) * 2 * 1536 * 4096
 
 
 def test_layer_bytes_and_flops():
@@ -53,10 +57,19 @@ def test_layer_bytes_and_flops():
 
 def test_fp8_first_projection_bytes():
     wl = mi.WORKLOADS["step5_fp8_prefill"]
-    touched, T, H, I, k = 284, 8192, 4096, 1536, 8
-    # one byte per code, one fp32 scale per 128 x 128 block; h as codes plus
-    # one fp32 scale per 128 columns of a row
+    touched, T, H, I = 284, 8192, 4096, 1536
+    # one byte per code, one fp32 scale per 128 x 128 block; x read once as
+    # codes with one fp32 scale per 128 columns of a row (the shared expert
+    # runs in bf16 launches of its own)
     w13 = 2 * I * H + (2 * I // 128) * (H // 128) * 4
-    want = touched * w13 + T * H * 2 + T * k * (I + I // 128 * 4)
+    want = touched * w13 + T * H + T * (H // 128) * 4
     assert w13 == 12 * MIB + 3072
     assert bench.up_kernel_bytes(wl, touched) == want
+
+
+def test_fp8_layer_bytes_count_block_scales():
+    wl = mi.WORKLOADS["step5_fp8_prefill"]
+    touched, T, E, H, I = 284, 8192, 352, 4096, 1536
+    scales = touched * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)) * 4
+    want = touched * 18 * MIB + scales + 36 * MIB + E * H * 2 + E * 4 + T * H * 2 + T * H * 4
+    assert bench.layer_bytes(wl, touched) == want

@@ -5,8 +5,10 @@ Small workloads (tiny, ragged and edge-case shapes spanning several tiles and
 ragged tails) are compared on every token; the full-size Step-3.5-Flash and
 Step-5-Preview workloads are run through moe_layer_forward exactly as the
 benchmark runs them, with routing and per-expert counts checked on every token
-and outputs on a seeded sample of tokens (rows are independent, so a sampled
-row is checked exactly).
+and outputs on a sample of tokens built from the GPU's own permutation so that
+it reaches every (expert, m-tile) work item of the grouped launches: the first
+and last row of every tile, a random row of each, and every row of the
+largest expert (rows are independent, so a sampled row is checked exactly).
 """
 import sys
 
@@ -17,7 +19,8 @@ import torch
 import moe_inputs as mi
 import sparse_moe_layer_route_amd as moe
 from oracle import oracle as orc
-from parity import (TOL_BF16, TOL_FP8, check_counts, check_routing, exempt_tokens, max_err_over_rms)
+from parity import (TOL_BF16, TOL_FP8, check_counts, check_routing, decode_rows, exempt_tokens,
+                    max_err_over_rms, tile_plan_sample)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,7 +132,7 @@ def test_steps_small(name):
     ref = orc.layer(cfg, h, want_parts=True)
     _, _, _, corr = orc.route(cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
     ex = check_routing(ids_h, w.cpu().numpy(), ref["ids"], ref["w"], corr, k)
-    yr = y_rows.float().cpu().numpy()
+    yr = decode_rows(y_rows, H)
     pairs = or2p
     t_of, j_of = pairs // k, pairs % k
     keep = ~ex[t_of]
@@ -155,8 +158,8 @@ def test_steps_small(name):
 @pytest.mark.parametrize("name", ["tiny", "small_tiles_multi_tile", "wide_tiles"])
 def test_steps_shared_rows(name):
     """The split path with the shared expert inside the expert launches
-    (moe_expert_up / moe_expert_down with its weights, combine of its fp16
-    rows) equals moe_layer_forward bit for bit, and the oracle within
+    (moe_expert_up / moe_expert_down with its weights, combine of its scaled
+    fp16 rows) equals moe_layer_forward bit for bit, and the oracle within
     tolerance; where the widths differ, the entry points refuse."""
     wl = mi.workload("tiny", **SMALL[name])
     cfg, T, k = wl.cfg, wl.T, wl.cfg.top_k
@@ -210,8 +213,6 @@ def test_nan_inf_inputs_keep_ids_in_range():
     assert np.array_equal(ids[:3], ref_ids[:3])
 
 
-# step35_prefill: the shared expert on the library's side stream (fork and
-# join captured with the rest)
 @pytest.mark.parametrize("name", ["step5_decode", "tiny", "step35_prefill"])
 def test_graph_replay_matches_eager(name):
     """moe_layer_forward captured into a HIP graph: every replay (with eager
@@ -420,8 +421,7 @@ def test_layer_balanced_full_size(name):
     torch.cuda.empty_cache()
     _, o_w = orc.route(cfg, h["x"], h["w_router"], None, ids_in=o_ids)
     check_weights(w.cpu().numpy(), o_w)
-    rng = np.random.default_rng(5)
-    sample = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, min(N_SAMPLE, T), replace=False)]))
+    sample = item_sample(cfg, T, ids, np.zeros(T, bool), seed=5)
     ref = orc.layer(cfg, h, tokens=sample, ids_in=o_ids)
     err, rms = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
     say(f"  sampled {sample.size} tokens: max_err/rms = {err:.3e} (rms {rms:.3e})")
@@ -487,10 +487,18 @@ BLOCK_GAP, BLOCK_W_RTOL = 1e-3, 5e-3
 
 
 def check_block(wl, inp, out, ids, w, counts, tokens=None):
-    """Routing against the oracle's own normalised rows, then the layer part
-    (resid_out - resid) against the oracle's layer output."""
+    """Routing against the oracle's routing of the GPU's own normalised rows
+    at the usual 1e-6 tie gap and weight tolerance (the selection itself,
+    with the inputs held equal), and against the oracle's own normalised
+    rows at the widened gap; then the layer part (resid_out - resid) against
+    the oracle's layer output."""
     cfg, k, E = wl.cfg, wl.cfg.top_k, wl.cfg.num_experts
+    x_gpu = moe.moe_rmsnorm(cfg, inp["resid"], inp["norm_weight"], inp["eps"])
+    torch.cuda.synchronize()
     h = host(inp)
+    g_ids, g_w, _, g_corr = orc.route(cfg, x_gpu.cpu(), h["w_router"], h["router_bias"], want_scores=True)
+    ex_own = check_routing(ids.cpu().numpy(), w.cpu().numpy(), g_ids, g_w, g_corr, k)
+    check_counts(counts.cpu().numpy(), g_ids, ids.cpu().numpy(), ex_own, E)
     x_o = orc.rmsnorm(h["resid"], h["norm_weight"], h["eps"])
     o_ids, o_w, _, corr = orc.route(cfg, x_o, h["w_router"], h["router_bias"], want_scores=True)
     ids_h = ids.cpu().numpy()
@@ -554,8 +562,7 @@ def test_block_full_size(name):
     inp = dict(gpu_inputs(wl), **mi.block_inputs(wl, DEV))
     del inp["x"]
     out, ids, w, counts = run_block(wl, inp)
-    rng = np.random.default_rng(2)
-    sample = np.unique(np.concatenate([[0, 1, wl.T - 1], rng.choice(wl.T, min(N_SAMPLE, wl.T), replace=False)]))
+    sample = item_sample(wl.cfg, wl.T, ids, np.zeros(wl.T, bool), seed=2)
     check_block(wl, inp, out, ids, w, counts, tokens=sample)
 
 
@@ -563,7 +570,33 @@ def test_block_full_size(name):
 # full-size workloads through moe_layer_forward
 
 FULL = ["step35_prefill", "step5_prefill", "step5_decode", "step5_decode_half"]
-N_SAMPLE = 24
+
+
+def tile_rows(cfg, T):
+    """Row height of the grouped launches' tiles (the library's rule: FP8
+    experts 128; bf16 64 when experts average under 48 rows, else 256)."""
+    if cfg.expert_dtype == "fp8":
+        return 128
+    return 64 if T * cfg.top_k < 48 * cfg.num_experts else 256
+
+
+def item_sample(cfg, T, ids, exempt, seed):
+    """Tokens reaching every (expert, m-tile) work item of the grouped
+    launches (from the GPU's own permutation of its ids), and every m-tile of
+    the shared expert's group, less the near-tie tokens."""
+    k = cfg.top_k
+    _, offsets, r2p, _ = moe.moe_permute(cfg, ids)
+    torch.cuda.synchronize()
+    bm = tile_rows(cfg, T)
+    rng = np.random.default_rng(seed)
+    toks = [tile_plan_sample(offsets.cpu().numpy(), r2p.cpu().numpy(), k, bm, rng)]
+    if cfg.share_expert_dim:
+        mt = (T + bm - 1) // bm
+        for m in range(mt):
+            a, b = m * T // mt, (m + 1) * T // mt
+            toks.append(np.array([a, b - 1, int(rng.integers(a, b))]))
+    sample = np.unique(np.concatenate(toks))
+    return sample[~exempt[sample]]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -585,10 +618,9 @@ def test_layer_full_size(name):
     check_counts(counts.cpu().numpy(), o_ids, ids_h, ex, E)
     say(f"  routing ok on all {T} tokens; exempt {int(ex.sum())}; experts touched "
         f"{int((counts.cpu().numpy() > 0).sum())}")
-    rng = np.random.default_rng(0)
-    cand = np.nonzero(~ex)[0]
-    sample = np.unique(np.concatenate([cand[:2], cand[-2:], rng.choice(cand, min(N_SAMPLE, cand.size),
-                                                                        replace=False)]))
+    sample = item_sample(cfg, T, ids, ex, seed=0)
+    say(f"  comparing {sample.size} tokens that reach every work item")
+    assert T < 500 or sample.size > 500
     ref = orc.layer(cfg, h, tokens=sample)
     assert np.array_equal(ref["ids"], o_ids[sample])
     err, rms = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
@@ -671,7 +703,7 @@ def test_fp8_expert_steps():
     keep = ~ex[t_of]
     orc_slot = {(t, e): j for t in range(T) for j, e in enumerate(ref["ids"][t].tolist())}
     ref_rows = np.stack([ref["y_routed"][t, orc_slot[(t, ids_h[t, j])]] for t, j in zip(t_of, j_of)])
-    err, _ = max_err_over_rms(y_split.float().cpu().numpy()[keep], ref_rows[keep])
+    err, _ = max_err_over_rms(decode_rows(y_split, cfg.hidden_size)[keep], ref_rows[keep])
     say(f"  routed rows max_err/rms = {err:.3e}")
     assert err <= TOL_FP8
 
@@ -699,11 +731,124 @@ def test_layer_fp8_full_size():
     ids_h = ids.cpu().numpy()
     ex = check_routing(ids_h, w.cpu().numpy(), o_ids, o_w, corr, k)
     check_counts(counts.cpu().numpy(), o_ids, ids_h, ex, E)
-    rng = np.random.default_rng(1)
-    cand = np.nonzero(~ex)[0]
-    sample = np.unique(np.concatenate([cand[:2], cand[-2:], rng.choice(cand, min(N_SAMPLE, cand.size),
-                                                                        replace=False)]))
+    sample = item_sample(cfg, T, ids, ex, seed=1)
+    say(f"  comparing {sample.size} tokens that reach every work item")
+    assert sample.size > 500
     ref = orc.layer(cfg, h, tokens=sample)
     err, rms = max_err_over_rms(out.cpu().numpy()[sample], ref["out"])
     say(f"  sampled {sample.size} tokens: max_err/rms = {err:.3e} (rms {rms:.3e})")
     assert err <= TOL_FP8
+
+
+# ----------------------------------------------------------------------------------------
+# the expert rows' range: no clip (limit 0) with outputs far beyond fp16's
+# range, and tiny outputs far below its normal range
+
+def large_y_workload(fp8=False):
+    # x scaled so that, with no clip, h ~ 0.1 x_scale^2 and the expert
+    # outputs reach about 0.02 sqrt(I) h ~ 2e5, beyond fp16's largest (65504)
+    kw = dict(swiglu_limit=0.0, swiglu_limit_shared=0.0, x_scale=3000.0, T=96)
+    if fp8:
+        kw.update(hidden_size=256, moe_intermediate_size=128, expert_dtype="fp8")
+    return mi.workload("tiny", **kw)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_layer_no_clip_outputs_beyond_fp16(fp8):
+    """Limit 0 (no clip) with expert outputs above 65504: the whole layer
+    against the oracle within the usual tolerance, and the expert rows'
+    format kept (each 128-column group's largest fp16 magnitude in
+    [2^14, 2^15))."""
+    wl = large_y_workload(fp8)
+    cfg, T, k, H = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.hidden_size
+    say(f"[no_clip_beyond_fp16] fp8={fp8} T={T}")
+    inp = gpu_inputs(wl)
+    out, ids, w, counts = run_layer(wl, inp)
+    h = host(inp)
+    ref = orc.layer(cfg, h, want_parts=True)
+    big = float(np.abs(ref["y_routed"]).max())
+    say(f"  oracle max |expert output| = {big:.3e}")
+    assert big > 65504.0, "the case must reach beyond fp16's range"
+    _, _, _, corr = orc.route(cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ex = check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], corr, k)
+    err, rms = max_err_over_rms(out.float().cpu().numpy()[~ex], ref["out"][~ex])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert np.isfinite(out.cpu().numpy()).all()
+    assert err <= (TOL_FP8 if fp8 else TOL_BF16)
+    # the rows themselves
+    ws = moe.workspace(cfg, T)
+    ids2, w2 = moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ws=ws)
+    _, offsets, r2p, _ = moe.moe_permute(cfg, ids2, ws=ws)
+    y = moe.moe_grouped_swiglu(cfg, inp["x"], offsets, r2p, inp["w13"], inp["w2"], w13_scale=inp.get("w13_scale"),
+                               w2_scale=inp.get("w2_scale"), ws=ws)
+    torch.cuda.synchronize()
+    vals = y[:, :2 * H].cpu().contiguous().view(torch.float16).float().abs().numpy()
+    gmax = vals.reshape(vals.shape[0], -1, 128).max(axis=2)
+    nz = gmax > 0
+    assert np.all((gmax[nz] >= 2.0 ** 14) & (gmax[nz] <= 2.0 ** 15))   # rounding may carry to 2^15
+    assert np.abs(decode_rows(y, H)).max() > 65504.0
+
+
+def test_layer_tiny_outputs():
+    """Inputs scaled by 1e-4 (expert outputs around 1e-8, below fp16's
+    smallest normal number): the layer against the oracle within the usual
+    tolerance of its (tiny) RMS."""
+    wl = mi.workload("tiny", x_scale=1e-4, T=96)
+    say("[tiny_outputs]")
+    inp = gpu_inputs(wl)
+    out, ids, w, counts = run_layer(wl, inp)
+    h = host(inp)
+    ref = orc.layer(wl.cfg, h)
+    _, _, _, corr = orc.route(wl.cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ex = check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], corr, wl.cfg.top_k)
+    err, rms = max_err_over_rms(out.float().cpu().numpy()[~ex], ref["out"][~ex])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------------------
+# prefill-sized token counts with small dimensions: the whole-layer call
+# equals its separate entry points bit for bit (the shared expert as group E
+# of the routed launches, or in launches of its own when its width differs)
+
+PREFILL_SMALL_DIMS = {
+    # 8192 pairs over 352 experts (23 per expert): 64-row tiles at T = 1024
+    "t1024_64_row_tiles": dict(T=1024, hidden_size=128, num_experts=352, top_k=8, moe_intermediate_size=128,
+                               share_expert_dim=128),
+    # 256-row tiles, the shared expert of another width in launches of its own
+    "t2048_shared_width_differs": dict(T=2048, hidden_size=256, num_experts=8, top_k=2, moe_intermediate_size=256,
+                                       share_expert_dim=128),
+    # 256-row tiles, the shared expert as group E
+    "t2048_shared_as_group": dict(T=2048, hidden_size=256, num_experts=8, top_k=2, moe_intermediate_size=256,
+                                  share_expert_dim=256),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_SMALL_DIMS))
+def test_prefill_sizes_layer_equals_steps(name):
+    wl = mi.workload("tiny", **PREFILL_SMALL_DIMS[name])
+    cfg, T, k, E = wl.cfg, wl.T, wl.cfg.top_k, wl.cfg.num_experts
+    say(f"[prefill_sizes_layer_equals_steps] {name}")
+    inp = gpu_inputs(wl)
+    out, ids, w, counts = run_layer(wl, inp)
+    ws = moe.workspace(cfg, T)
+    ids2, w2 = moe.moe_route(cfg, inp["x"], inp["w_router"], inp["router_bias"], ws=ws)
+    counts2, offsets, r2p, p2r = moe.moe_permute(cfg, ids2, ws=ws)
+    if moe.binding.shared_fusable(cfg):
+        hb = moe.moe_expert_up(cfg, inp["x"], offsets, r2p, inp["w13"], ws=ws, ws13=inp["ws13"])
+        y = moe.moe_expert_down(cfg, T, hb, offsets, inp["w2"], ws=ws, ws2=inp["ws2"])
+        out2 = moe.moe_combine(cfg, y, p2r, w2, shared_rows=y[T * k:])
+    else:
+        y = moe.moe_grouped_swiglu(cfg, inp["x"], offsets, r2p, inp["w13"], inp["w2"], ws=ws)
+        ysh = moe.moe_shared_ffn(cfg, inp["x"], inp["ws13"], inp["ws2"], ws=ws)
+        out2 = moe.moe_combine(cfg, y, p2r, w2, ysh)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2) and torch.equal(counts, counts2)
+    assert torch.equal(out, out2)
+    h = host(inp)
+    ref = orc.layer(cfg, h)
+    _, _, _, corr = orc.route(cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
+    ex = check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], corr, k)
+    err, rms = max_err_over_rms(out.cpu().numpy()[~ex], ref["out"][~ex])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= TOL_BF16
