@@ -217,6 +217,26 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
                                int32_t* expert_counts_out,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer_forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments less (ws, ws_bytes), the same kernels and results.  Its
+ * workspace is a device array inside the library, moe_noalloc_max_bytes()
+ * (64 MiB) per GPU, held until the process ends; a call whose
+ * moe_workspace_size() exceeds it returns MOE_ERR_WORKSPACE before
+ * anything is launched (at the Step-5 shapes with bf16 experts that is
+ * above 609 tokens).  The call allocates nothing.  All calls on one GPU share that
+ * array: calls that overlap on one GPU (other streams, other threads)
+ * race; order them on one stream. */
+moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, int64_t T, const void* x,
+                                       const void* w_router, const float* router_bias,
+                                       const void* w13, const float* w13_scale,
+                                       const void* w2, const float* w2_scale,
+                                       const void* ws13, const void* ws2, void* out,
+                                       int32_t* topk_ids_out, float* topk_w_out,
+                                       int32_t* expert_counts_out, hipStream_t stream);
+/* Bytes of the array moe_layer_forward_noalloc works in. */
+size_t moe_noalloc_max_bytes(void);
+
 /* The MoE sub-block of a decoder layer (MAX page: each layer has a norm in
  * front of the MLP/MoE and a residual connection around it; AutoModel page,
  * benchmark table: FP32 norms and residual stream):

@@ -25,7 +25,7 @@ EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swigl
             "moe_expert_down", "moe_hidden_bytes", "moe_expert_rows_bytes", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
             "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_rmsnorm", "moe_block_forward",
             "moe_saved_bytes", "moe_backward_workspace_size", "moe_layer_forward_train", "moe_layer_backward",
-            "moe_status_string")
+            "moe_layer_forward_noalloc", "moe_noalloc_max_bytes", "moe_status_string")
 
 
 class MoEError(RuntimeError):
@@ -76,6 +76,7 @@ def load(path: Optional[str] = None):
         "moe_layer_backward": [C, I64, P, P, P, P, P, P, P, SZ, P, P, P, P, P, P, P, P, SZ, P],
         "moe_block_forward": [C, I64, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_layer_forward": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_layer_forward_noalloc": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P],
         "moe_route_replay": [C, I64, P, P, P, P, P, SZ, P],
         "moe_balanced_ids": [C, I64, P, P],
         "moe_layer_forward_routed": [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -84,6 +85,8 @@ def load(path: Optional[str] = None):
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    L.moe_noalloc_max_bytes.argtypes = []
+    L.moe_noalloc_max_bytes.restype = ctypes.c_size_t
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -383,6 +386,41 @@ def moe_layer_forward(cfg, inp: dict, out=None, ws=None, topk_ids=None, topk_w=N
         _ptr(expert_counts, torch.int32, (E,), "expert_counts"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check(st, "moe_layer_forward")
+    return out
+
+
+def moe_noalloc_max_bytes() -> int:
+    """Size of the per-GPU scratch array that moe_layer_forward_noalloc uses."""
+    return int(load().moe_noalloc_max_bytes())
+
+
+def moe_layer_forward_noalloc(cfg, inp: dict, out=None, topk_ids=None, topk_w=None, expert_counts=None,
+                              stream=None):
+    """moe_layer_forward without a workspace argument: the library's own
+    per-GPU scratch array serves as the workspace and nothing is allocated
+    (the output is allocated here when ``out`` is None).  Raises MoeError
+    (MOE_ERR_WORKSPACE) when the batch needs more scratch than the array has."""
+    x = inp["x"]
+    T, H, E, k, I, Is = (x.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k, cfg.moe_intermediate_size,
+                         cfg.share_expert_dim)
+    wdt = _weights_dtype(cfg)
+    fp8 = cfg.expert_dtype == "fp8"
+    out = out if out is not None else torch.empty((T, H), dtype=_out_dtype(cfg), device=x.device)
+    c = make_config(cfg)
+    st = load().moe_layer_forward_noalloc(
+        ctypes.byref(c), T, _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(inp["w_router"], torch.bfloat16, (E, H), "w_router"),
+        _ptr(inp["router_bias"], torch.float32, (E,), "router_bias"),
+        _ptr(inp["w13"], wdt, (E, 2 * I, H), "w13"),
+        _ptr(inp.get("w13_scale"), torch.float32, (E, 2 * I // 128, H // 128) if fp8 else None, "w13_scale"),
+        _ptr(inp["w2"], wdt, (E, H, I), "w2"),
+        _ptr(inp.get("w2_scale"), torch.float32, (E, H // 128, I // 128) if fp8 else None, "w2_scale"),
+        _ptr(inp.get("ws13") if Is else None, torch.bfloat16, (2 * Is, H), "ws13"),
+        _ptr(inp.get("ws2") if Is else None, torch.bfloat16, (H, Is), "ws2"),
+        _ptr(out, _out_dtype(cfg), (T, H), "out"),
+        _ptr(topk_ids, torch.int32, (T, k), "topk_ids"), _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+        _ptr(expert_counts, torch.int32, (E,), "expert_counts"), _stream(stream))
+    _check(st, "moe_layer_forward_noalloc")
     return out
 
 

@@ -6,6 +6,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
 
@@ -391,6 +393,39 @@ int bwd_max_tiles(const Dims& d) {
     return (int)((d.P + 255) / 256) + d.E + (d.Is > 0 ? (int)((d.T + 255) / 256) + 1 : 0);
 }
 
+// ---- the allocation-free entry point's scratch -----------------------------
+// A file-scope device array that moe_layer_forward_noalloc uses as its
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel: the
+// name is a host-side stand-in, not a device address.  The device address
+// is looked up once per device (with that device current) and kept.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// the scratch array's address on the device `stream` belongs to
+moe_status_t noalloc_scratch(hipStream_t stream, char** out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) return MOE_ERR_HIP;
+        // the same address whichever thread stores it
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = (char*)p;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -527,6 +562,22 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x
     MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
     return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
                          expert_counts_out, stream);
+}
+
+size_t moe_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                                       const float* router_bias, const void* w13, const float* w13_scale,
+                                       const void* w2, const float* w2_scale, const void* ws13, const void* ws2,
+                                       void* out, int32_t* topk_ids_out, float* topk_w_out,
+                                       int32_t* expert_counts_out, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (T == 0) return MOE_OK;
+    if (layer_ws(dims(cfg, T)).total > kNoallocScratchBytes) return MOE_ERR_WORKSPACE;
+    char* base = nullptr;
+    MOE_TRY(noalloc_scratch(stream, &base));
+    return moe_layer_forward(cfg, T, x, w_router, router_bias, w13, w13_scale, w2, w2_scale, ws13, ws2, out,
+                             topk_ids_out, topk_w_out, expert_counts_out, base, kNoallocScratchBytes, stream);
 }
 
 moe_status_t moe_route_replay(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,

@@ -24,7 +24,7 @@ def lib():
 
 def header_functions():
     text = open(os.path.join(ROOT, "include", "moe.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:moe_status_t|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|const char\*|size_t)\s+(moe_\w+)\s*\(", text, re.M)))
 
 
 def test_header_symbols_are_exported(lib):
