@@ -108,7 +108,7 @@ def up_kernel_flops(wl):
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "routed_up_bf16_step5_prefill_hbm_counters.md")
+                            "routed_gemms_bf16_step5_prefill_counters.md")
 KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_layer_route_amd", "csrc",
                           "grouped_gemm.hip")
 
@@ -288,9 +288,10 @@ def up_roofline(wl, r, peaks, traffic):
 
 
 def measure_peaks(torch):
-    """Attainable peaks on this chip: a device-to-device copy of 2 GiB (bytes
-    read + written per second, the median of 10) and the vendor library's
-    bf16 GEMM of 8192 x 8192 x 8192 (hipBLASLt through torch.matmul)."""
+    """Attainable peaks on this chip: HBM as the faster of a device-to-device
+    copy of 2 GiB (bytes read + written per second) and a sum over 2 GiB
+    (bytes read per second), and the vendor library's bf16 GEMM of 8192 x
+    8192 x 8192 (hipBLASLt through torch.matmul); medians of 10."""
     note("measuring attainable peaks (device copy, vendor bf16 GEMM)")
     n = 2 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -304,8 +305,21 @@ def measure_peaks(torch):
         torch.cuda.synchronize()
         if i >= 3:
             ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
-    hbm = 2 * n / median(ts)
-    del src, dst
+    copy = 2 * n / median(ts)
+    del dst
+    # read-only stream: a sum over the same 2 GiB (bytes read per second)
+    f = src.view(torch.float32)
+    ts = []
+    for i in range(13):
+        ev[0].record()
+        f.sum()
+        ev[1].record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+    read = n / median(ts)
+    del src, f
+    hbm = max(copy, read)
     a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
     b = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
     ts = []
@@ -319,7 +333,10 @@ def measure_peaks(torch):
     gemm = 2 * 8192 ** 3 / median(ts)
     del a, b
     torch.cuda.empty_cache()
-    return {"hbm_gbs": hbm / 1e9, "hbm_how": "device-to-device copy of 2 GiB, read + written bytes, median of 10",
+    return {"hbm_gbs": hbm / 1e9,
+            "hbm_how": "the faster of a 2 GiB device-to-device copy (read + written bytes) and a sum over 2 GiB "
+                       "(read bytes), medians of 10",
+            "hbm_copy_gbs": copy / 1e9, "hbm_read_gbs": read / 1e9,
             "bf16_tflops": gemm / 1e12, "bf16_how": "torch.matmul (hipBLASLt) 8192^3 bf16, median of 10"}
 
 
