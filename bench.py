@@ -447,36 +447,48 @@ def time_balanced(args, wl, moe, torch, mi):
 
 def time_block(args, wl, moe, torch, mi):
     """moe_block_forward (zero-centred RMSNorm, the layer, fp32 residual add
-    in the combine) and the RMSNorm kernel alone, each over args.steps
-    launches bracketed by HIP events on the stream."""
+    in the combine), then its front end both ways: the RMSNorm kernel and
+    moe_route as two steps, and moe_rmsnorm_route (one fused pass from 512
+    tokens); each over args.steps launches bracketed by HIP events on the
+    stream."""
     cfg, T, H = wl.cfg, wl.T, wl.cfg.hidden_size
     inp = dict(mi.make_inputs(wl, "cuda", seed=0), **mi.block_inputs(wl, "cuda", seed=0))
     ws = moe.workspace(cfg, T)
     stream = torch.cuda.current_stream()
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
     x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    norm = lambda: moe.moe_rmsnorm(cfg, inp["resid"], inp["norm_weight"], inp["eps"], x=x, stream=stream)
+    route = lambda: moe.moe_route(cfg, x, inp["w_router"], inp["router_bias"], topk_ids=ids, topk_w=w, ws=ws,
+                                  stream=stream)
+    fused = lambda: moe.moe_rmsnorm_route(cfg, inp["resid"], inp["norm_weight"], inp["eps"], inp["w_router"],
+                                          inp["router_bias"], x=x, topk_ids=ids, topk_w=w, ws=ws, stream=stream)
+    block = lambda: moe.moe_block_forward(cfg, inp, resid_out=out, ws=ws, stream=stream)
+    regions = [block, norm, route, fused]
     for _ in range(args.warmup):
-        moe.moe_block_forward(cfg, inp, resid_out=out, ws=ws, stream=stream)
-        moe.moe_rmsnorm(cfg, inp["resid"], inp["norm_weight"], inp["eps"], x=x, stream=stream)
+        for f in regions:
+            f()
     torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(args.steps):
-        moe.moe_block_forward(cfg, inp, resid_out=out, ws=ws, stream=stream)
-    ev[1].record(stream)
-    ev[2].record(stream)
-    for _ in range(args.steps):
-        moe.moe_rmsnorm(cfg, inp["resid"], inp["norm_weight"], inp["eps"], x=x, stream=stream)
-    ev[3].record(stream)
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / args.steps
-    norm_us = ev[2].elapsed_time(ev[3]) * 1e3 / args.steps
+    us = []
+    for f in regions:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            f()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        us.append(ev[0].elapsed_time(ev[1]) * 1e3 / args.steps)
+    block_us, norm_us, route_us, fused_us = us
+    ms = block_us * 1e-3
     norm_bytes = T * H * 4 + T * H * 2 + H * 4          # fp32 rows in, bf16 rows out, the weight
-    del inp, ws, out, x
+    del inp, ws, out, x, ids, w
     torch.cuda.empty_cache()
     return {"workload": wl.name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "rmsnorm_us": norm_us,
             "rmsnorm_gbs": norm_bytes / (norm_us * 1e-6) / 1e9,
-            "rmsnorm_hbm_frac": norm_bytes / (norm_us * 1e-6) / HBM_PEAK}
+            "rmsnorm_hbm_frac": norm_bytes / (norm_us * 1e-6) / HBM_PEAK,
+            "route_us": route_us, "norm_route_two_steps_us": norm_us + route_us,
+            "norm_route_fused_us": fused_us}
 
 
 def time_train(args, wl, moe, torch, mi):

@@ -201,6 +201,20 @@ moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* y_rows,
 moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const float* resid, const float* norm_weight,
                          float eps, void* x, hipStream_t stream);
 
+/* moe_rmsnorm followed by moe_route on its output, as one pass where it
+ * pays (MAX page, model overview: the norm feeds the MoE block's router):
+ * x [T,H] bf16 as moe_rmsnorm writes it, topk_ids / topk_w as moe_route
+ * gives for that x, bit for bit.  From 512 tokens (H <= 4096, H % 256 == 0,
+ * E <= 384) the norm and the router logits run in one kernel that feeds the
+ * normalised rows to the router from on-chip memory; otherwise the two steps
+ * run in turn (moe_block_forward always takes the two steps).  Uses ws for the
+ * logits (moe_workspace_size covers it); errors as for moe_route and
+ * moe_rmsnorm. */
+moe_status_t moe_rmsnorm_route(const moe_config_t* cfg, int64_t T, const float* resid, const float* norm_weight,
+                               float eps, const void* w_router, const float* router_bias, void* x,
+                               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* The whole layer: route, permute, routed experts, shared expert, combine.
  * Inputs as above (ws13/ws2 may be NULL when share_expert_dim == 0).  With
  * bf16 experts and share_expert_dim == moe_intermediate_size the shared

@@ -23,7 +23,8 @@ MOE_BF16, MOE_FP32, MOE_FP8_E4M3_B128 = range(3)
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_expert_up",
             "moe_expert_down", "moe_hidden_bytes", "moe_expert_rows_bytes", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
-            "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_rmsnorm", "moe_block_forward",
+            "moe_route_replay", "moe_balanced_ids", "moe_layer_forward_routed", "moe_rmsnorm", "moe_rmsnorm_route",
+            "moe_block_forward",
             "moe_saved_bytes", "moe_backward_workspace_size", "moe_layer_forward_train", "moe_layer_backward",
             "moe_layer_forward_noalloc", "moe_noalloc_max_bytes", "moe_status_string")
 
@@ -70,6 +71,7 @@ def load(path: Optional[str] = None):
         "moe_shared_ffn": [C, I64, P, P, P, P, P, SZ, P],
         "moe_combine": [C, I64, P, P, P, P, P, P, P, P],
         "moe_rmsnorm": [C, I64, P, P, ctypes.c_float, P, P],
+        "moe_rmsnorm_route": [C, I64, P, P, ctypes.c_float, P, P, P, P, P, P, SZ, P],
         "moe_saved_bytes": [C, I64, ctypes.POINTER(SZ)],
         "moe_backward_workspace_size": [C, I64, ctypes.POINTER(SZ)],
         "moe_layer_forward_train": [C, I64, P, P, P, P, P, P, P, P, P, P, SZ, P, SZ, P],
@@ -467,6 +469,29 @@ def moe_rmsnorm(cfg, resid, norm_weight, eps, x=None, stream=None):
                             _ptr(x, torch.bfloat16, (T, H), "x"), _stream(stream))
     _check(st, "moe_rmsnorm")
     return x
+
+
+def moe_rmsnorm_route(cfg, resid, norm_weight, eps, w_router, router_bias, x=None, topk_ids=None, topk_w=None,
+                      ws=None, stream=None):
+    """moe_rmsnorm then moe_route on its output (one fused pass from 512
+    tokens): returns x [T,H] bf16, topk_ids [T,k] int32, topk_w [T,k] fp32."""
+    T, H, E, k = resid.shape[0], cfg.hidden_size, cfg.num_experts, cfg.top_k
+    dev = resid.device
+    x = x if x is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    topk_ids = topk_ids if topk_ids is not None else torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_w = topk_w if topk_w is not None else torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws = ws if ws is not None else workspace(cfg, T, dev)
+    c = make_config(cfg)
+    st = load().moe_rmsnorm_route(ctypes.byref(c), T, _ptr(resid, torch.float32, (T, H), "resid"),
+                                  _ptr(norm_weight, torch.float32, (H,), "norm_weight"), float(eps),
+                                  _ptr(w_router, torch.bfloat16, (E, H), "w_router"),
+                                  _ptr(router_bias, torch.float32, (E,), "router_bias"),
+                                  _ptr(x, torch.bfloat16, (T, H), "x"),
+                                  _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+                                  _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+                                  _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "moe_rmsnorm_route")
+    return x, topk_ids, topk_w
 
 
 def moe_block_forward(cfg, inp: dict, resid_out=None, ws=None, topk_ids=None, topk_w=None, expert_counts=None,

@@ -120,7 +120,8 @@ struct Params {
     const int4* items;          // grouped (optional): per work item {group, first row, rows, n-tile}
     int64_t c_row_bytes;        // OUT_F16: bytes per output row (scaled fp16 rows)
     int rot_group;              // dense (>= 0): take the K rotation of group rot_group, so a dense
-                                // launch adds in the order of that group's grouped launch
+                                // launch adds in the order of that group's grouped launch;
+                                // -2: the router's order (router_chunk_rot by 64-row tile)
 };
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -239,7 +240,11 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     // blocks that share an A tile (grouped) or a weight panel (dense) in step.
     // K slices: 64 (128 B of a row) for 256-row tiles, 32 for 64-row tiles
     const int nk = K / (BM == 256 ? BK2 : BK);   // K % 64 == 0
-    const int rot = (GROUPED ? (g + 1) * 37 : ((p.rot_group >= 0 ? p.rot_group : n_tile) + 1) * 37) % nk;
+    // (the router's dense launch, rot_group -2, takes the chunk order of
+    // router_chunk_rot by 64-row tile: 8 slices of 32 per chunk)
+    const int rot = GROUPED ? (g + 1) * 37 % nk
+                    : (p.rot_group == -2 && nk % 8 == 0) ? 8 * router_chunk_rot(m_tile, nk / 8)
+                    : ((p.rot_group >= 0 ? p.rot_group : n_tile) + 1) * 37 % nk;
 
     // valid 16-row tiles of this wave: tiles wm + WM i with 16 (wm + WM i) < valid
     const int ntile_valid = (valid + 15) >> 4;

@@ -144,6 +144,23 @@ moe_status_t do_route(const moe_config_t* c, const Dims& d, const void* x, const
     return MOE_OK;
 }
 
+// the RMSNorm, then the routing of its output; with `fused`, where the shape
+// allows, the norm and the router logits in one pass (the same bits as the
+// two steps)
+moe_status_t do_norm_route(const moe_config_t* c, const Dims& d, const float* resid, const float* g, float eps,
+                           const void* wr, const float* b, void* x, int32_t* ids, float* w, char* ws,
+                           bool fused, hipStream_t s) {
+    if (!fused || !moe::rmsnorm_router_fusable(d.T, d.H, d.E)) {
+        HIP_TRY(moe::launch_rmsnorm(resid, g, eps, x, (int)d.T, d.H, s));
+        return do_route(c, d, x, wr, b, ids, w, ws, s);
+    }
+    float* logits = (float*)ws;
+    HIP_TRY(moe::launch_rmsnorm_router(resid, g, eps, wr, x, logits, (int)d.T, d.E, d.H, s));
+    HIP_TRY(moe::launch_topk(logits, 1, b, (int)d.T, d.E, d.k, c->router_scaling_factor, c->norm_expert_weight,
+                             ids, w, s));
+    return MOE_OK;
+}
+
 // router logits, then the weights of caller-supplied ids
 moe_status_t do_replay(const moe_config_t* c, const Dims& d, const void* x, const void* wr, const int32_t* ids,
                        float* w, char* ws, hipStream_t s) {
@@ -546,6 +563,20 @@ moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const float* resid,
     return hip_status(moe::launch_rmsnorm(resid, norm_weight, eps, x, (int)T, cfg->hidden_size, stream));
 }
 
+moe_status_t moe_rmsnorm_route(const moe_config_t* cfg, int64_t T, const float* resid, const float* norm_weight,
+                               float eps, const void* w_router, const float* router_bias, void* x,
+                               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_config(cfg, T));
+    if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!resid || !norm_weight || !w_router || !router_bias || !x || !topk_ids || !topk_w || !ws)
+        return MOE_ERR_INVALID_ARGUMENT;
+    Dims d = dims(cfg, T);
+    if (ws_bytes < route_ws(d)) return MOE_ERR_WORKSPACE;
+    return do_norm_route(cfg, d, resid, norm_weight, eps, w_router, router_bias, x, topk_ids, topk_w, (char*)ws,
+                         true, stream);
+}
+
 moe_status_t moe_layer_forward(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
                                const float* router_bias, const void* w13, const float* w13_scale, const void* w2,
                                const float* w2_scale, const void* ws13, const void* ws2, void* out,
@@ -630,10 +661,12 @@ moe_status_t moe_block_forward(const moe_config_t* cfg, int64_t T, const float* 
     LayerWs L = layer_ws(d);
     char* base = (char*)ws;
     void* x = base + L.x;
-    HIP_TRY(moe::launch_rmsnorm(resid_in, norm_weight, eps, x, (int)T, d.H, stream));
     int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
     float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
-    MOE_TRY(do_route(cfg, d, x, w_router, router_bias, ids, w, base + L.step, stream));
+    // the norm and the routing as two steps: faster here than the fused pass
+    // of moe_rmsnorm_route at the Step-5 prefill shape, with the same bits
+    MOE_TRY(do_norm_route(cfg, d, resid_in, norm_weight, eps, w_router, router_bias, x, ids, w, base + L.step,
+                          false, stream));
     return layer_experts(cfg, d, L, base, x, ids, w, w13, w13_scale, w2, w2_scale, ws13, ws2, resid_out,
                          expert_counts_out, stream, resid_in);
 }

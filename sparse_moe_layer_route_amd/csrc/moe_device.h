@@ -56,6 +56,14 @@ __device__ __forceinline__ void yrow_zero_pad(char* row, int H) {
 // 2^e for e in [-126, 127]
 __device__ __forceinline__ float exp2_int(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
+// The router's K order from 512 tokens: the 64-token tile m adds its K
+// chunks of 256 (8 slices of 32) starting at chunk router_chunk_rot(m, nc)
+// of nc, wrapping around, slices in order inside a chunk.  Tiles start at
+// different chunks (their rows' reads spread over the HBM channels); every
+// expert column of a tile uses the same order, which the fused RMSNorm +
+// router pass repeats chunk by chunk.
+__host__ __device__ __forceinline__ int router_chunk_rot(int m, int nc) { return (m * 5 + 3) % nc; }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }

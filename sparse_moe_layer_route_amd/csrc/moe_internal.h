@@ -101,6 +101,12 @@ hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows,
 // zero-centred RMSNorm of fp32 rows -> bf16 rows (H % 4 == 0)
 hipError_t launch_rmsnorm(const float* resid, const float* norm_weight, float eps, void* x, int T, int H,
                           hipStream_t s);
+// the same RMSNorm fused with the router logits (logits [T][E] fp32, the same
+// bits as launch_router_logits on the normalised rows); for T >= 512, H <= 4096,
+// H % 256 == 0, E <= 384 (rmsnorm_router_fusable)
+bool rmsnorm_router_fusable(int64_t T, int H, int E);
+hipError_t launch_rmsnorm_router(const float* resid, const float* norm_weight, float eps, const void* w_router,
+                                 void* x, float* logits, int T, int E, int H, hipStream_t s);
 // resid (optional, fp32 [T,H]) is added last; out may be the same buffer
 hipError_t launch_combine(const void* y_rows, const int32_t* pair_to_row, const float* topk_w,
                           const float* y_shared, const void* shared_rows, const float* resid, void* out,

@@ -104,6 +104,7 @@ hipError_t launch_router_logits(const void* x, const void* w_router, float* logi
         a.N = E;
         a.K = H;
         a.bm = 64;
+        a.rot_group = -2;           // the K order the fused RMSNorm + router pass repeats
         return launch_grouped_down(a, true, s);
     }
     dim3 grid((T + 15) / 16, (E + 63) / 64, nsplit);   // wave: 16 tokens x 16 experts x H/nsplit

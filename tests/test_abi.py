@@ -266,3 +266,23 @@ def test_training_entry_points_rules(lib):
                                   1 << 30, None) == 3
     assert lib.moe_layer_backward(cr, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, *grads, FAKE,
                                   16, None) == 3
+
+
+def test_rmsnorm_route_argument_checks(lib):
+    c = ctypes.byref(cfg_of())
+    eps = ctypes.c_float(1e-5)
+    # null x, a bad eps, a small workspace, zero tokens
+    assert lib.moe_rmsnorm_route(c, 4, FAKE, FAKE, eps, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_rmsnorm_route(c, 4, FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 30, None) == 1
+    assert lib.moe_rmsnorm_route(c, 600, FAKE, FAKE, eps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    assert lib.moe_rmsnorm_route(c, 0, None, None, eps, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_noalloc_limit_is_exported(lib):
+    assert B.moe_noalloc_max_bytes() == 64 << 20
+    # a batch whose workspace exceeds the array is refused before any launch
+    c = cfg_of(hidden_size=4096, num_experts=352, top_k=8, moe_intermediate_size=1536, share_expert_dim=1536)
+    assert ws_size(c, 1024)[1] > B.moe_noalloc_max_bytes()
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(c), 1024, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                                         FAKE, FAKE, None, None, None, None) == 3

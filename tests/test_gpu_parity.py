@@ -462,6 +462,39 @@ def test_rmsnorm_vs_oracle(T, H):
         assert (x[1].float() == 0).all()
 
 
+NORM_ROUTE = {
+    "tiny_64_tokens_two_steps": ("tiny", dict(T=64)),
+    "tiny_600_tokens_fused": ("tiny", dict(T=600)),
+    "ragged_777_tokens_fused": ("tiny", dict(T=777, num_experts=20, top_k=3)),
+    "step35_prefill_fused": ("step35_prefill", {}),
+    "step5_prefill_fused": ("step5_prefill", {}),
+}
+
+
+@pytest.mark.parametrize("name", list(NORM_ROUTE))
+def test_rmsnorm_route_equals_its_steps(name):
+    """moe_rmsnorm_route = moe_rmsnorm then moe_route, bit for bit (x, ids,
+    weights), whether it runs fused (from 512 tokens) or as two steps; the
+    routing itself is checked against the oracle's routing of those rows."""
+    base, over = NORM_ROUTE[name]
+    wl = mi.workload(base, **over)
+    cfg = wl.cfg
+    say(f"[norm_route] {name} T={wl.T}")
+    inp = dict(gpu_inputs(wl), **mi.block_inputs(wl, DEV))
+    x, ids, w = moe.moe_rmsnorm_route(cfg, inp["resid"], inp["norm_weight"], inp["eps"], inp["w_router"],
+                                      inp["router_bias"])
+    x2 = moe.moe_rmsnorm(cfg, inp["resid"], inp["norm_weight"], inp["eps"])
+    ids2, w2 = moe.moe_route(cfg, x2, inp["w_router"], inp["router_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(x, x2)
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w, w2)
+    if wl.T <= 1024:
+        h = host(inp)
+        o_ids, o_w, _, corr = orc.route(cfg, x.cpu(), h["w_router"], h["router_bias"], want_scores=True)
+        check_routing(ids.cpu().numpy(), w.cpu().numpy(), o_ids, o_w, corr, cfg.top_k)
+
+
 BLOCK_SMALL = ["tiny", "ragged_130_tokens_20_experts", "no_shared", "shared_width_differs", "top1",
                "small_tiles_multi_tile"]
 
@@ -529,12 +562,21 @@ def test_block_small(name):
     assert torch.equal(r, out)
 
 
-@pytest.mark.parametrize("name", ["tiny", "step5_decode"])
+BLOCK_STEPS = {
+    "tiny": ("tiny", {}),
+    "step5_decode": ("step5_decode", {}),
+    "tiny_600_tokens": ("tiny", dict(T=600)),          # the dense router instance from 512 tokens
+    "step35_prefill": ("step35_prefill", {}),
+}
+
+
+@pytest.mark.parametrize("name", list(BLOCK_STEPS))
 def test_block_equals_its_steps(name):
     """moe_block_forward = resid + moe_layer_forward(moe_rmsnorm(resid)),
     bit for bit (the residual add is the combine's last fp32 add), and so is
     the split path ending in moe_combine with the residual as its output."""
-    wl = mi.WORKLOADS[name]
+    base, over = BLOCK_STEPS[name]
+    wl = mi.workload(base, **over)
     cfg, T, k = wl.cfg, wl.T, wl.cfg.top_k
     say(f"[block_steps] {name}")
     inp = dict(gpu_inputs(wl), **mi.block_inputs(wl, DEV))
