@@ -118,6 +118,7 @@ struct Params {
     float limit_extra;
     uint16_t* gu_out;           // SWIGLU (optional): the pre-activations [rows][2N] bf16, gate then up
     const int4* items;          // grouped (optional): per work item {group, first row, rows, n-tile}
+    const int* xcd_start;       // with items: XCD x runs routed items xcd_start[x] .. xcd_start[x + 1] - 1
     int64_t c_row_bytes;        // OUT_F16: bytes per output row (scaled fp16 rows)
     int rot_group;              // dense (>= 0): take the K rotation of group rot_group, so a dense
                                 // launch adds in the order of that group's grouped launch;
@@ -155,12 +156,13 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// Work items: grouped, (group, m-tile, n-tile) with n fastest, from the
-// tile plan; dense, (n-tile, m-tile).  The routed items and the extra
-// group's are two segments; each is cut into 8 contiguous ranges, one per XCD
-// (block b runs on XCD b % 8), so every XCD gets an equal share of both and
-// the blocks that share a tile run on one L2.  An XCD runs its extra-group
-// items (full tiles) first, then its routed ones.
+// Work items: grouped, (group, n-tile, m-tile) with m fastest, from the tile
+// plan; dense, (n-tile, m-tile).  The routed items and the extra group's are
+// two segments, each cut into 8 contiguous ranges, one per XCD (block b runs
+// on XCD b % 8), so the blocks that share a weight panel run on one L2: the
+// extra group's in equal shares, the routed ones by the item table's
+// cost-balanced ranges (equal shares of the count without a table).  An XCD
+// runs its extra-group items (full tiles) first, then its routed ones.
 struct Segments {
     int total1, per1, total2, per2;           // routed / extra items, per-XCD range lengths
 };
@@ -790,14 +792,21 @@ __global__ __launch_bounds__((Shape<BM, BN>::NT), 1) void kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
     const Segments sg = segments<GROUPED, BM>(p);
     const int xcd = blockIdx.x % NXCD, slots = gridDim.x / NXCD;
-    for (int s = blockIdx.x / NXCD; s < sg.per1 + sg.per2; s += slots) {
+    // routed items of this XCD: a contiguous range of the list, from the
+    // item table's cost-balanced split or an equal split of the count
+    int r0 = xcd * sg.per1, rn = sg.per1;
+    if (GROUPED && p.xcd_start) {
+        r0 = __builtin_amdgcn_readfirstlane(p.xcd_start[xcd]);
+        rn = __builtin_amdgcn_readfirstlane(p.xcd_start[xcd + 1]) - r0;
+    }
+    for (int s = blockIdx.x / NXCD; s < sg.per2 + rn; s += slots) {
         int w;
         if (s < sg.per2) {
             w = xcd * sg.per2 + s;
             if (w >= sg.total2) continue;
             w += sg.total1;
         } else {
-            w = xcd * sg.per1 + (s - sg.per2);
+            w = r0 + (s - sg.per2);
             if (w >= sg.total1) continue;
         }
         run_item<MODE, GROUPED, BM, BN>(p, w, smem);
@@ -812,22 +821,92 @@ static int grid_blocks(int64_t work) {
     return (int)(per * NXCD);
 }
 
-// The work items of a grouped launch, {group, first row, rows, n-tile}, in
-// the kernel's order: group-major, then n-tile, then m-tile.  A group's rows
-// are split evenly over its m-tiles (each at most bm rows, as the tile plan
-// counts ceil(rows / bm) of them), so the m-tiles that share a weight panel
-// do the same work at the same pace.  One block of 1024 threads; each thread
-// takes m-tiles (its group found by a binary search of the tile plan in LDS)
-// and writes their n_tiles items.
+// The work items of a grouped launch, {group, first row, rows, n-tile}.  A
+// group's rows are split evenly over its m-tiles (each at most bm rows, as
+// the tile plan counts ceil(rows / bm) of them), so the m-tiles that share a
+// weight panel do the same work at the same pace; a group's items are
+// n-tile-major, m-tile fastest.  The routed groups are dealt to the 8 XCDs
+// by cost, so that every XCD gets about the same work: ranked by cost (an
+// item costs ITEM_COST0 + its rows, the weight panel's stream counted in
+// rows' worth of time), they go to XCDs 0..7, 7..0, 0..7, ... in rank order,
+// and each XCD's groups lie contiguous in the list (xcd_start gives the
+// ranges), heavy and light alternating.  Without `balance` the items stay
+// in group order.  The extra group's items follow the routed ones; the
+// kernel splits them evenly over the XCDs.  One block of 1024 threads.
+constexpr int ITEM_COST0 = 224;
+
 __global__ __launch_bounds__(1024) void item_table_kernel(const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ tile_start, int groups,
-                                                         int extra_rows, int n_tiles, int4* __restrict__ items) {
+                                                         int extra_rows, int n_tiles, int balance,
+                                                         int* __restrict__ xcd_start, int4* __restrict__ items) {
     __shared__ int32_t ts[1026];
+    __shared__ int32_t cost[1024], rank_of[1024], by_rank[1024];
+    __shared__ int32_t cnt_at[NXCD][128], off_at[NXCD][128];
+    __shared__ int32_t xs[NXCD + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ng = groups + (extra_rows > 0 ? 1 : 0);
-    for (int g = threadIdx.x; g <= ng; g += blockDim.x) ts[g] = tile_start[g];
+    for (int g = tid; g <= ng; g += blockDim.x) ts[g] = tile_start[g];
+    for (int i = tid; i < NXCD * 128; i += blockDim.x) cnt_at[i / 128][i % 128] = 0;
+    // rank i goes to XCD x(i) as its (i / 8)-th heaviest group; an XCD's k
+    // groups run heaviest, lightest, second heaviest, second lightest, ...,
+    // so that items bound by the MFMAs and items bound by the weight stream
+    // overlap in time on every XCD
+    auto xcd_of = [](int i) { const int pos = i % NXCD; return ((i / NXCD) & 1) ? NXCD - 1 - pos : pos; };
+    const int last = groups > 0 ? (groups - 1) / NXCD : 0;         // the last round
+    auto groups_of = [&](int x) {
+        const int pos = (last & 1) ? NXCD - 1 - x : x;
+        return groups > 0 ? last + (pos <= (groups - 1) % NXCD ? 1 : 0) : 0;
+    };
+    auto slot_of = [&](int i) {
+        const int j = i / NXCD, k = groups_of(xcd_of(i));
+        return j < (k + 1) / 2 ? 2 * j : 2 * (k - 1 - j) + 1;
+    };
     __syncthreads();
+    if (balance) {                              // (uniform over the block)
+    for (int g = tid; g < groups; g += blockDim.x)
+        cost[g] = n_tiles * ((ts[g + 1] - ts[g]) * ITEM_COST0 + (offsets[g + 1] - offsets[g]));
+    __syncthreads();
+    // rank: descending cost, ties to the lower group
+    for (int g = tid; g < groups; g += blockDim.x) {
+        const int c = cost[g];
+        int r = 0;
+        for (int h = 0; h < groups; ++h) {
+            const int ch = cost[h];
+            r += (ch > c || (ch == c && h < g)) ? 1 : 0;
+        }
+        rank_of[g] = r;
+        by_rank[r] = g;
+    }
+    __syncthreads();
+    for (int i = tid; i < groups; i += blockDim.x) {
+        const int g = by_rank[i];
+        cnt_at[xcd_of(i)][slot_of(i)] = (ts[g + 1] - ts[g]) * n_tiles;
+    }
+    __syncthreads();
+    // exclusive scan of each XCD's item counts over its groups (wave x, two per lane)
+    if (wave < NXCD) {
+        const int a = cnt_at[wave][2 * lane], b = cnt_at[wave][2 * lane + 1];
+        int incl = a + b;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        const int excl = incl - a - b;
+        off_at[wave][2 * lane] = excl;
+        off_at[wave][2 * lane + 1] = excl + a;
+        if (lane == 63) xs[wave + 1] = incl;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        xs[0] = 0;
+        for (int x = 0; x < NXCD; ++x) xs[x + 1] += xs[x];
+    }
+    __syncthreads();
+    if (tid <= NXCD) xcd_start[tid] = xs[tid];
+    }
     const int total = ts[ng];
-    for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    for (int i = tid; i < total; i += blockDim.x) {
         int lo = 0, hi = ng - 1;                // the group g with ts[g] <= i < ts[g + 1]
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -837,7 +916,14 @@ __global__ __launch_bounds__(1024) void item_table_kernel(const int32_t* __restr
         const int base = offsets[min(g, groups)];
         const int cnt = (g < groups ? offsets[g + 1] : base + extra_rows) - base;
         const int a = (int)(((int64_t)m * cnt) / mt), b = (int)(((int64_t)(m + 1) * cnt) / mt);
-        int4* out = items + (int64_t)t0 * n_tiles + m;
+        int64_t first;
+        if (g < groups && balance) {
+            const int r = rank_of[g], x = xcd_of(r);
+            first = (int64_t)xs[x] + off_at[x][slot_of(r)];
+        } else {
+            first = (int64_t)t0 * n_tiles;      // in group order (the extra group after all routed items)
+        }
+        int4* out = items + first + m;
         for (int n = 0; n < n_tiles; ++n) out[n * mt] = make_int4(g, base + a, b - a, n);
     }
 }
@@ -846,8 +932,14 @@ template <int MODE, int BM, int BN>
 void launch(Params p, int64_t tiles, hipStream_t s) {
     p.n_tiles = is_swiglu(MODE) ? (2 * p.N + BN - 1) / BN : (p.N + BN - 1) / BN;
     if (p.items) {
-        item_table_kernel<<<1, 1024, 0, s>>>(p.offsets, p.tile_start, p.groups, p.extra_rows, p.n_tiles,
-                                             (int4*)p.items);
+        // the first projection's routed groups are dealt to the XCDs by cost
+        // (measured: 2.18 -> 2.16 ms at the Step-5 prefill); the second
+        // projection keeps them in group order, equal shares of the count
+        // (dealt by cost it ran slower)
+        const int balance = is_swiglu(MODE) ? 1 : 0;
+        item_table_kernel<<<1, 1024, 0, s>>>(p.offsets, p.tile_start, p.groups, p.extra_rows, p.n_tiles, balance,
+                                             (int*)p.xcd_start, (int4*)p.items);
+        if (!balance) p.xcd_start = nullptr;
     }
     const int nb = grid_blocks(tiles * p.n_tiles);
     if (p.offsets) kernel<MODE, true, BM, BN><<<nb, Shape<BM, BN>::NT, 0, s>>>(p);
@@ -856,7 +948,8 @@ void launch(Params p, int64_t tiles, hipStream_t s) {
 
 }  // namespace gg
 
-size_t grouped_item_bytes(int64_t max_tiles, int n_tiles) { return (size_t)max_tiles * n_tiles * 16; }
+// the XCD ranges (16 ints), then the items
+size_t grouped_item_bytes(int64_t max_tiles, int n_tiles) { return 64 + (size_t)max_tiles * n_tiles * 16; }
 int64_t expert_row_bytes(int H) { return yrow_bytes(H); }
 
 int grouped_tile_m(int64_t rows, int groups) {
@@ -886,7 +979,8 @@ hipError_t launch_grouped_up(const GroupedArgs& a, hipStream_t s) {
     p.limit_extra = a.limit_extra;
     p.gu_out = (uint16_t*)a.gu_out;
     p.rot_group = a.rot_group;
-    p.items = (a.bm == 256 && a.offsets) ? (const int4*)a.items : nullptr;
+    p.items = (a.bm == 256 && a.offsets && a.items) ? (const int4*)((const char*)a.items + 64) : nullptr;
+    p.xcd_start = p.items ? (const int*)a.items : nullptr;
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
     // 256-row tiles address gathered A rows and one group's weights by 32-bit
@@ -922,7 +1016,8 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s)
     p.extra_rows = a.extra_rows;
     p.W_extra = (const uint16_t*)a.W_extra;
     p.rot_group = a.rot_group;
-    p.items = (a.bm == 256 && a.offsets) ? (const int4*)a.items : nullptr;
+    p.items = (a.bm == 256 && a.offsets && a.items) ? (const int4*)((const char*)a.items + 64) : nullptr;
+    p.xcd_start = p.items ? (const int*)a.items : nullptr;
     p.c_row_bytes = yrow_bytes(a.N);
     const int64_t tiles = a.offsets ? a.max_tiles : (a.M + a.bm - 1) / a.bm;
     if (tiles <= 0) return hipSuccess;
