@@ -75,6 +75,8 @@ struct Params {
     const int32_t* tile_start;
     int groups;
     int n_tiles;
+    const int4* items;          // optional: per work item {group, first row, rows, n-tile}
+    const int* xcd_start;       // with items: XCD x runs items xcd_start[x] .. xcd_start[x + 1] - 1
 };
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -109,7 +111,18 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
 
     // ---- work item: (expert, n-tile, m-tile), m fastest, per-XCD ranges
     int g, n_tile, row0, row_end;
-    {
+    if (p.items) {
+        // one load from the item table (written by a one-block launch first)
+        const int b = blockIdx.x;
+        const int xcd = b % NXCD, slot = b / NXCD;
+        const int r0 = __builtin_amdgcn_readfirstlane(p.xcd_start[xcd]);
+        if (slot >= __builtin_amdgcn_readfirstlane(p.xcd_start[xcd + 1]) - r0) return;
+        const int4 d = p.items[r0 + slot];
+        g = __builtin_amdgcn_readfirstlane(d.x);
+        row0 = __builtin_amdgcn_readfirstlane(d.y);
+        row_end = row0 + __builtin_amdgcn_readfirstlane(d.z);
+        n_tile = __builtin_amdgcn_readfirstlane(d.w);
+    } else {
         const int b = blockIdx.x;
         const int xcd = b % NXCD, slot = b / NXCD;
         const int ntiles = p.tile_start[p.groups];
@@ -456,7 +469,7 @@ static int f8_grid(int64_t work) { return (int)((work + f8::NXCD - 1) / f8::NXCD
 hipError_t launch_fp8_up(const void* xq, const float* xs, int xs_ld, const int32_t* a_rows, int a_div,
                          int a_nrows, const void* w13, const float* w13s, void* hq, float* hs, int hs_ld, int N,
                          int K, float limit, const int32_t* offsets, const int32_t* tile_start, int groups,
-                         int max_tiles, hipStream_t s) {
+                         int max_tiles, void* items, hipStream_t s) {
     f8::Params p{};
     p.A = (const uint8_t*)xq;
     p.a_rows = a_rows;
@@ -479,13 +492,19 @@ hipError_t launch_fp8_up(const void* xq, const float* xs, int xs_ld, const int32
     p.groups = groups;
     p.n_tiles = (2 * N) / f8::BN;
     if (max_tiles <= 0) return hipSuccess;
+    if (items) {
+        const hipError_t e = launch_item_table(offsets, tile_start, groups, 0, p.n_tiles, false, items, s);
+        if (e != hipSuccess) return e;
+        p.xcd_start = (const int*)items;
+        p.items = (const int4*)((const char*)items + 64);
+    }
     f8::kernel<f8::SWIGLU><<<f8_grid((int64_t)max_tiles * p.n_tiles), f8::NT, 0, s>>>(p);
     return hipGetLastError();
 }
 
 hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows, const void* w2, const float* w2s,
                            void* y, int N, int K, const int32_t* offsets, const int32_t* tile_start, int groups,
-                           int max_tiles, hipStream_t s) {
+                           int max_tiles, void* items, hipStream_t s) {
     f8::Params p{};
     p.A = (const uint8_t*)hq;
     p.a_rows = nullptr;
@@ -506,6 +525,12 @@ hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows,
     p.groups = groups;
     p.n_tiles = (N + f8::BN - 1) / f8::BN;
     if (max_tiles <= 0) return hipSuccess;
+    if (items) {
+        const hipError_t e = launch_item_table(offsets, tile_start, groups, 0, p.n_tiles, false, items, s);
+        if (e != hipSuccess) return e;
+        p.xcd_start = (const int*)items;
+        p.items = (const int4*)((const char*)items + 64);
+    }
     f8::kernel<f8::OUT_F16><<<f8_grid((int64_t)max_tiles * p.n_tiles), f8::NT, 0, s>>>(p);
     return hipGetLastError();
 }

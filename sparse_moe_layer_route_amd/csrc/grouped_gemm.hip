@@ -831,7 +831,7 @@ static int grid_blocks(int64_t work) {
 // rows' worth of time), they go to XCDs 0..7, 7..0, 0..7, ... in rank order,
 // and each XCD's groups lie contiguous in the list (xcd_start gives the
 // ranges), heavy and light alternating.  Without `balance` the items stay
-// in group order.  The extra group's items follow the routed ones; the
+// in group order and the ranges are equal shares of their count.  The extra group's items follow the routed ones; the
 // kernel splits them evenly over the XCDs.  One block of 1024 threads.
 constexpr int ITEM_COST0 = 224;
 
@@ -904,6 +904,10 @@ __global__ __launch_bounds__(1024) void item_table_kernel(const int32_t* __restr
     }
     __syncthreads();
     if (tid <= NXCD) xcd_start[tid] = xs[tid];
+    } else if (tid <= NXCD) {
+        // group order: equal shares of the routed items' count
+        const int total1 = ts[groups] * n_tiles, per = (total1 + NXCD - 1) / NXCD;
+        xcd_start[tid] = min(tid * per, total1);
     }
     const int total = ts[ng];
     for (int i = tid; i < total; i += blockDim.x) {
@@ -950,6 +954,13 @@ void launch(Params p, int64_t tiles, hipStream_t s) {
 
 // the XCD ranges (16 ints), then the items
 size_t grouped_item_bytes(int64_t max_tiles, int n_tiles) { return 64 + (size_t)max_tiles * n_tiles * 16; }
+
+hipError_t launch_item_table(const int32_t* offsets, const int32_t* tile_start, int groups, int extra_rows,
+                             int n_tiles, bool balance, void* buf, hipStream_t s) {
+    gg::item_table_kernel<<<1, 1024, 0, s>>>(offsets, tile_start, groups, extra_rows, n_tiles, balance ? 1 : 0,
+                                             (int*)buf, (int4*)((char*)buf + 64));
+    return hipGetLastError();
+}
 int64_t expert_row_bytes(int H) { return yrow_bytes(H); }
 
 int grouped_tile_m(int64_t rows, int groups) {

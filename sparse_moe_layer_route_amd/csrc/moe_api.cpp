@@ -249,7 +249,8 @@ moe_status_t do_up(const moe_config_t* c, const Dims& d, const void* x, const in
         float* hs = (float*)((char*)h + hcode_bytes(d));
         HIP_TRY(moe::launch_quant_rows(x, (int)d.T, d.H, xq, xs, (int)d.T, s));
         HIP_TRY(moe::launch_fp8_up(xq, xs, (int)d.T, r2p, d.k, (int)d.T, w13, w13s, h, hs, (int)d.P, d.I, d.H,
-                                   c->swiglu_limit, offsets, tile_start, d.E, (int)max_tiles(d, false), s));
+                                   c->swiglu_limit, offsets, tile_start, d.E, (int)max_tiles(d, false),
+                                   item_table(d, tile_start), s));
         return MOE_OK;
     }
     HIP_TRY(moe::launch_grouped_up(up_args(c, d, x, offsets, r2p, w13, h, tile_start, ws13), s));
@@ -266,7 +267,7 @@ moe_status_t do_down(const moe_config_t* c, const Dims& d, const void* h, const 
     if (d.fp8) {
         const float* hs = (const float*)((const char*)h + hcode_bytes(d));
         HIP_TRY(moe::launch_fp8_down(h, hs, (int)d.P, (int)d.P, w2, w2s, y_rows, d.H, d.I, offsets, tile_start,
-                                     d.E, (int)max_tiles(d, false), s));
+                                     d.E, (int)max_tiles(d, false), item_table(d, tile_start), s));
         return MOE_OK;
     }
     HIP_TRY(moe::launch_grouped_down(down_args(d, h, offsets, w2, y_rows, tile_start, ws2), false, s));

@@ -72,6 +72,11 @@ struct GroupedArgs {
 // bytes of the work-item table of a grouped 256-row launch with max_tiles
 // tiles over n_tiles column tiles
 size_t grouped_item_bytes(int64_t max_tiles, int n_tiles);
+// the work-item table of a grouped launch ({group, first row, rows, n-tile}
+// per item after a 64-byte header of 9 XCD range starts), from the tile plan;
+// `balance` deals the routed groups to the XCDs by cost
+hipError_t launch_item_table(const int32_t* offsets, const int32_t* tile_start, int groups, int extra_rows,
+                             int n_tiles, bool balance, void* buf, hipStream_t s);
 // bytes of one expert output row of H columns: H fp16 values, then one int8
 // exponent per 128 columns (padded to 16 bytes); value = fp16 * 2^exponent
 int64_t expert_row_bytes(int H);
@@ -88,13 +93,14 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s)
 // K % 128 == 0, N % 128 == 0.
 int fp8_tile_m();
 hipError_t launch_quant_rows(const void* x, int rows, int H, void* xq, float* xs, int ld, hipStream_t s);
+// items (optional): grouped_item_bytes(max_tiles, n-tiles) of scratch for the work-item table
 hipError_t launch_fp8_up(const void* xq, const float* xs, int xs_ld, const int32_t* a_rows, int a_div,
                          int a_nrows, const void* w13, const float* w13s, void* hq, float* hs, int hs_ld, int N,
                          int K, float limit, const int32_t* offsets, const int32_t* tile_start, int groups,
-                         int max_tiles, hipStream_t s);
+                         int max_tiles, void* items, hipStream_t s);
 hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows, const void* w2, const float* w2s,
                            void* y, int N, int K, const int32_t* offsets, const int32_t* tile_start, int groups,
-                           int max_tiles, hipStream_t s);
+                           int max_tiles, void* items, hipStream_t s);
 
 // ---- combine --------------------------------------------------------------
 // shared expert output: y_shared fp32 [T, H], or shared_rows (scaled fp16 rows), or neither
