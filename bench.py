@@ -288,10 +288,11 @@ def up_roofline(wl, r, peaks, traffic):
 
 
 def measure_peaks(torch):
-    """Attainable peaks on this chip: HBM as the faster of a device-to-device
-    copy of 2 GiB (bytes read + written per second) and a sum over 2 GiB
-    (bytes read per second), and the vendor library's bf16 GEMM of 8192 x
-    8192 x 8192 (hipBLASLt through torch.matmul); medians of 10."""
+    """Attainable peaks on this chip: HBM as the fastest of a device-to-device
+    copy of 2 GiB (bytes read + written per second) and two read-only
+    streams over 2 GiB, an int64 sum and a bf16 matrix-vector product (bytes
+    read per second), and the vendor library's bf16 GEMM of 8192 x 8192 x
+    8192 (hipBLASLt through torch.matmul); medians of 10."""
     note("measuring attainable peaks (device copy, vendor bf16 GEMM)")
     n = 2 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -307,18 +308,24 @@ def measure_peaks(torch):
             ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
     copy = 2 * n / median(ts)
     del dst
-    # read-only stream: a sum over the same 2 GiB (bytes read per second)
-    f = src.view(torch.float32)
-    ts = []
-    for i in range(13):
-        ev[0].record()
-        f.sum()
-        ev[1].record()
-        torch.cuda.synchronize()
-        if i >= 3:
-            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
-    read = n / median(ts)
-    del src, f
+    # read-only streams over the same 2 GiB (bytes read per second): an int64
+    # sum and a bf16 matrix-vector product (the vendor library's GEMV)
+    i64 = src.view(torch.int64)
+    mat = src.view(torch.bfloat16).view(32768, 32768)
+    vec = torch.ones(32768, device="cuda", dtype=torch.bfloat16)
+    reads = []
+    for f in (lambda: i64.sum(), lambda: torch.mv(mat, vec)):
+        ts = []
+        for i in range(13):
+            ev[0].record()
+            f()
+            ev[1].record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        reads.append(n / median(ts))
+    read = max(reads)
+    del src, i64, mat, vec
     hbm = max(copy, read)
     a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
     b = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
@@ -334,8 +341,8 @@ def measure_peaks(torch):
     del a, b
     torch.cuda.empty_cache()
     return {"hbm_gbs": hbm / 1e9,
-            "hbm_how": "the faster of a 2 GiB device-to-device copy (read + written bytes) and a sum over 2 GiB "
-                       "(read bytes), medians of 10",
+            "hbm_how": "the fastest of a 2 GiB device-to-device copy (read + written bytes), an int64 sum over "
+                       "2 GiB and a bf16 matrix-vector product over a 2 GiB matrix (read bytes), medians of 10",
             "hbm_copy_gbs": copy / 1e9, "hbm_read_gbs": read / 1e9,
             "bf16_tflops": gemm / 1e12, "bf16_how": "torch.matmul (hipBLASLt) 8192^3 bf16, median of 10"}
 
