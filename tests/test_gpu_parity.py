@@ -863,6 +863,12 @@ PREFILL_SMALL_DIMS = {
     # 256-row tiles, the shared expert as group E
     "t2048_shared_as_group": dict(T=2048, hidden_size=256, num_experts=8, top_k=2, moe_intermediate_size=256,
                                   share_expert_dim=256),
+    # 256-row tiles over 1024 expert groups: the item table deals 128 rounds of groups to the XCDs
+    "t1536_1024_experts": dict(T=1536, hidden_size=128, num_experts=1024, top_k=32, moe_intermediate_size=128,
+                               share_expert_dim=128),
+    # 37 groups (a ragged last round of the deal) and a ragged shared group of 3000 rows
+    "t3000_37_experts": dict(T=3000, hidden_size=256, num_experts=37, top_k=4, moe_intermediate_size=256,
+                             share_expert_dim=256),
 }
 
 
