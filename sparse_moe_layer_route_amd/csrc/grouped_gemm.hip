@@ -628,10 +628,52 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                 }
             }
         }
-        if (!is_swiglu(MODE)) {
-            // plain output: through LDS, EPI_ROWS rows at a time (16-byte
+        if constexpr (MODE == OUT_F16) {
+            // scaled fp16 rows straight from the registers: a wave's 128
+            // columns are one exponent group, so a row's largest magnitude
+            // is the max over the lane's 32 values and its 3 sibling lanes
+            // (staged through LDS as the fp32 output is, with its bank
+            // conflicts, the second projection took 1.33 ms against 1.21 ms
+            // at the Step-5 prefill)
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if (i >= n_i) continue;
+                const int lr = 16 * (wm + S::WM * i) + lrow;
+                float m = 0.f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n_tile * BN + S::GW * wn + 16 * j + lcol;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (col + v < p.N) m = fmaxf(m, fabsf(acc[i][j][v]));
+                }
+                m = fmaxf(m, __shfl_xor(m, 16, kWave));
+                m = fmaxf(m, __shfl_xor(m, 32, kWave));
+                if (lr >= valid) continue;
+                const int ex = yrow_exp(m);
+                const float sc = exp2_int(-ex);
+                char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n_tile * BN + S::GW * wn + 16 * j + lcol;
+                    if (col < p.N) {
+                        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+                        f16x4 h4;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) h4[v] = (_Float16)(acc[i][j][v] * sc);
+                        *(f16x4*)(row + 2 * col) = h4;
+                    }
+                }
+                const int c0 = n_tile * BN + S::GW * wn;
+                if (lcol == 0 && c0 < p.N) {
+                    row[2 * p.N + (c0 >> 7)] = (char)ex;
+                    if (c0 == 0) yrow_zero_pad(row, p.N);
+                }
+            }
+        } else if (!is_swiglu(MODE)) {
+            // plain fp32 output: through LDS, EPI_ROWS rows at a time (16-byte
             // writes of each lane's 4 columns), then whole rows, 16 bytes per
-            // lane (fp32) or per 8 values (fp16)
+            // lane
             constexpr int PITCH = BN + 4;
             constexpr int EPI_ROWS = S::EPI_ROWS;
             constexpr int IPP = EPI_ROWS / 16 / S::WM;
@@ -648,42 +690,15 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                         *(f32x4*)&stage[pr * PITCH + S::GW * wn + 16 * j + lcol] = acc[i][j];
                 }
                 __syncthreads();
-                constexpr int CHUNK = MODE == OUT_F32 ? 4 : 8;
-                constexpr int PER_ROW = BN / CHUNK;
-                const int c = (tid % PER_ROW) * CHUNK;
+                constexpr int PER_ROW = BN / 4;
+                const int c = (tid % PER_ROW) * 4;
                 const int col = n_tile * BN + c;
 #pragma unroll 4
                 for (int q = 0; q < EPI_ROWS * PER_ROW / NT; ++q) {
                     const int pr = tid / PER_ROW + (NT / PER_ROW) * q;
                     const int lr = EPI_ROWS * pass + pr;
-                    const bool ok = lr < valid && col < p.N;
-                    const float* sv = &stage[pr * PITCH + c];
-                    const int64_t r = row0 + lr;
-                    if (MODE == OUT_F32) {
-                        if (ok) *(float4*)((float*)p.C + r * p.N + col) = *(const float4*)sv;
-                    } else {
-                        // scaled fp16 row: the 16 lanes of one 128-column group
-                        // agree on its exponent
-                        float m = 0.f;
-                        if (ok) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(sv[e]));
-                        }
-#pragma unroll
-                        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-                        const int ex = yrow_exp(m);
-                        const float sc = exp2_int(-ex);
-                        if (ok) {
-                            typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-                            f16x8 h8;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) h8[e] = (_Float16)(sv[e] * sc);
-                            char* row = (char*)p.C + r * p.c_row_bytes;
-                            *(f16x8*)(row + 2 * col) = h8;
-                            if ((col & 127) == 0) row[2 * p.N + (col >> 7)] = (char)ex;
-                            if (col == 0) yrow_zero_pad(row, p.N);
-                        }
-                    }
+                    if (lr < valid && col < p.N)
+                        *(float4*)((float*)p.C + (int64_t)(row0 + lr) * p.N + col) = *(const float4*)&stage[pr * PITCH + c];
                 }
                 __syncthreads();
             }
