@@ -586,10 +586,11 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     if (BM == 256) {
         // SwiGLU: each lane stores its 4 h values (and, when kept, the 4
         // gate and 4 up values) as 8 contiguous bytes straight from
-        // registers.  Plain output goes through LDS (below): its rows of 256
-        // columns are then written as whole rows, which measured faster for
-        // them (1.32 against 1.37-1.40 ms for the Step-5 second projection);
-        // for the first projection the direct stores are (2.36 against 2.42).
+        // registers (2.36 against 2.42 ms staged, Step-5 first projection);
+        // so do the scaled fp16 rows (below).  The fp32 output goes through
+        // LDS and is written as whole rows of 256 columns, which measured
+        // faster for it (105 against 108 us for the dense 8192-row second
+        // projection).
         const int lrow = lane & 15, lcol = 4 * (lane >> 4);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
