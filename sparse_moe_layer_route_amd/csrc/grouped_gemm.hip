@@ -341,7 +341,11 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         };
         // lane's byte offset in a 16-row tile for K chunk 4 sub + (lane >> 4)
         const int fr = lane & 15, sw = swz(fr);
-        const unsigned off0 = 128 * fr + 16 * ((lane >> 4) ^ sw);
+        unsigned off0 = 128 * fr + 16 * ((lane >> 4) ^ sw);
+        // opaque to the compiler: otherwise it keeps 128 fr apart through the
+        // item loop, spills it, and its reload after the prologue barrier
+        // waits for every DMA in flight (vmcnt 0)
+        asm volatile("" : "+v"(off0));
         const unsigned off1 = off0 ^ 64u;         // chunk 4 + c: (c ^ sw) ^ 4
         bf16x8 xa[TM], xb[TN], ya[TM], yb[TN];
         auto read_frags = [&](int kt, unsigned off, bf16x8* a, bf16x8* b) {
