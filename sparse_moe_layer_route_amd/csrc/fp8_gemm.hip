@@ -13,19 +13,21 @@
 // output tile, so each MFMA result is scaled and added to the fp32
 // accumulator straight away.
 //
-// Layout and staging (the bf16 kernel's choices, with bytes for elements):
+// Layout and staging (the bf16 256-row tiles' choices, with bytes for elements):
 //   * x is quantised once per token (quant_rows_kernel); the first projection
 //     gathers the code rows of its permuted rows (token = pair / k) as the
 //     bf16 kernel gathers x; activation scales are stored K-block-major,
 //     s_a[kb][row], and gathered per row into LDS by 4-byte DMA;
 //   * block tile 128 rows x 256 weight rows, K slices of 128 bytes (one
-//     scale block), 3-stage LDS ring filled by direct global->LDS DMA from
-//     inline asm with explicit vmcnt waits (see grouped_gemm.hip);
-//   * each DMA instruction moves 16 rows x 64 B with every 4 lanes reading
-//     64 contiguous bytes of one row, and LDS blocks sit at offsets that keep
-//     the MFMA fragment reads free of bank conflicts (as in grouped_gemm.hip);
+//     scale block, one whole line of every row), 3-stage LDS ring filled by
+//     direct global->LDS DMA from inline asm with explicit vmcnt waits;
+//   * each DMA instruction moves 8 rows x 128 B, the 16-byte chunks of a
+//     row swizzled by line_swz so that the fragment reads are free of bank
+//     conflicts (the layout of grouped_gemm.hip's 256-row tiles);
 //   * 8 waves as 2 along M x 4 along N, each 64 rows (16-row tiles wm + 2i)
-//     x 64 columns; weight-block scales are wave-uniform scalar loads.
+//     x 64 columns; weight-block scales are wave-uniform scalar loads;
+//   * the fragments of the next slice are read while this slice's MFMAs
+//     run, each into its register as soon as the register is free.
 // The first projection's epilogue applies the clipped SwiGLU, takes each
 // row's amax over the block's 128 h columns (one K block of the second
 // projection) across the 4 N waves through LDS, and writes the E4M3 codes of
@@ -41,16 +43,10 @@ constexpr int BM = 128, BN = 256, BKB = 128;      // K slice = 128 bytes = one s
 constexpr int NW = 8, NT = NW * 64;
 constexpr int TM = 4, TN = 4;
 constexpr int STAGES = 3;
-// A DMA block is 16 rows x 64 B (half of a 128-byte K slice).  The 4 blocks
-// of one (64-row group, half) start at these byte offsets: 16-byte bank
-// groups 0, 1, 16, 17 (mod 32), which keeps both 16-byte reads of every
-// 32-lane fragment pass free of bank conflicts.
-__device__ constexpr int BOFF[4] = {0, 1024 + 16, 2048 + 256, 3072 + 272};
-constexpr int GROUP = 3072 + 272 + 1024;
-constexpr int A_BYTES = 4 * GROUP;                 // 128 rows: 2 row groups x 2 halves
-constexpr int B_BYTES = 8 * GROUP;                 // 256 weight rows
+constexpr int A_BYTES = BM * BKB;                  // 128 rows of 128 B
+constexpr int B_BYTES = BN * BKB;                  // 256 weight rows of 128 B
 constexpr int SA_OFF = A_BYTES + B_BYTES;          // 128 row scales (two 256-byte DMAs)
-constexpr int STAGE_BYTES = SA_OFF + 512;
+constexpr int STAGE_BYTES = SA_OFF + 1024;         // (1 KiB aligned)
 constexpr int NXCD = 8;
 
 enum { SWIGLU = 0, OUT_F16 = 1 };
@@ -81,9 +77,12 @@ struct Params {
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void dma16(const void* g, unsigned lds_off) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g) : "memory");
+// one 1 KiB block: lane l's 16 bytes from base + off land at LDS byte
+// lds_off + 16 l (base wave-uniform, off this lane's 32-bit byte offset)
+__device__ __forceinline__ void dma16s(const void* base, unsigned off, unsigned lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(off), "s"(base) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* g, unsigned lds_off) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_off), "v"(g) : "memory");
@@ -93,6 +92,18 @@ template <int n>
 __device__ __forceinline__ void wait_vm() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// clipped SwiGLU with silu(g) = g * rcp(1 + exp(-g)), the hardware
+// reciprocal (1 ulp) in place of a division: the epilogue's VALU work is
+// most of its time
+__device__ __forceinline__ float swiglu_clip_fast(float g, float u, float L) {
+    float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+    if (L > 0.0f) {
+        sg = fminf(sg, L);
+        u = fminf(fmaxf(u, -L), L);
+    }
+    return sg * u;
 }
 
 // fp32 -> E4M3FN byte, round to nearest even (|v| <= 448 by construction)
@@ -159,29 +170,23 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         return min(max(sr, 0), p.a_nrows - 1);
     };
 
-    // ---- DMA sources (at k = 0).  Every 4 lanes read 64 contiguous bytes
-    // of one row (lane l: row quad l >> 2, 16 bytes at (l & 3) * 16 of the
-    // block's half); block b of row group g holds rows 64g + 16t + 4b + i
-    // for quad 4t + i.  Wave w moves A blocks 2w, 2w+1 and B blocks
-    // 4w .. 4w+3 of every slice; waves 0 and 1 also move the scales of tile
-    // rows 64w + lane.
-    const int quad = lane >> 2, chunk = lane & 3;
-    auto block_row = [&](int blk) { return 64 * (blk >> 3) + 16 * (quad >> 2) + 4 * (blk & 3) + (quad & 3); };
-    auto block_lds = [&](int blk) { return (blk >> 2) * GROUP + BOFF[blk & 3]; };
-    const uint8_t* a_src[2];
-    unsigned a_lds[2];
+    // ---- DMA sources.  One DMA instruction moves 8 rows x 128 B: lanes
+    // 8q .. 8q+7 read the whole 128-byte line of row q; lane l reads chunk
+    // (l & 7) ^ line_swz(row) and lands at LDS byte 16 l, so LDS chunk c of
+    // a row holds global chunk c ^ line_swz(row).  Wave w moves A rows
+    // 16w .. 16w+15 and W rows 32w .. 32w+31 of every slice.  Offsets are
+    // 32-bit from wave-uniform bases (the launch checks the ranges).
+    const int dq = lane >> 3;
+    unsigned a_off[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int blk = 2 * wave + q;                           // 0..15: (row group, half, block)
-        a_src[q] = p.A + (int64_t)src_row(block_row(blk)) * K + 64 * ((blk >> 2) & 1) + 16 * chunk;
-        a_lds[q] = block_lds(blk);
+        const int r = 16 * wave + 8 * q + dq;
+        a_off[q] = (unsigned)src_row(r) * (unsigned)K + 16u * ((lane & 7) ^ line_swz(r & 15));
     }
-    const uint8_t* b_src[4];
-    unsigned b_lds[4];
+    unsigned b_off[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int blk = 4 * wave + q;                           // 0..31
-        const int r = block_row(blk);                           // tile column 0..255
+        const int r = 32 * wave + 8 * q + dq;                   // tile column 0..255
         int wrow;
         if (MODE == SWIGLU) {
             // 64-column wave groups: 32 gate columns, then the matching 32 up columns
@@ -191,8 +196,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         } else {
             wrow = min(n_tile * BN + r, p.N - 1);
         }
-        b_src[q] = Wg + (int64_t)wrow * K + 64 * ((blk >> 2) & 1) + 16 * chunk;
-        b_lds[q] = A_BYTES + block_lds(blk);
+        b_off[q] = (unsigned)wrow * (unsigned)K + 16u * ((lane & 7) ^ line_swz(r & 15));
     }
     const float* sa_src = p.As + src_row(64 * (wave & 1) + lane);
 
@@ -202,16 +206,18 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
     auto issue_q = [&](int kt, int stage, int q) {
         const int k0 = kt * BKB;
         const unsigned sb = lds_base + stage * STAGE_BYTES;
-        if (q < 2) dma16(a_src[q] + k0, __builtin_amdgcn_readfirstlane(sb + a_lds[q]));
-        else if (q < 6) dma16(b_src[q - 2] + k0, __builtin_amdgcn_readfirstlane(sb + b_lds[q - 2]));
+        if (q < 2) dma16s(p.A + k0, a_off[q], __builtin_amdgcn_readfirstlane(sb + 1024 * (2 * wave + q)));
+        else if (q < 6) dma16s(Wg + k0, b_off[q - 2], __builtin_amdgcn_readfirstlane(sb + A_BYTES + 1024 * (4 * wave + q - 2)));
         else if (wave < 2) dma4(sa_src + (int64_t)kt * p.a_ld, __builtin_amdgcn_readfirstlane(sb + SA_OFF + 256 * wave));
     };
-    // LDS offset of this lane's 32 bytes (two 16-byte reads, +0 and +16) in
-    // 16-row tile tau = 4g + t: row r = lane & 15 from block r >> 2 of
-    // half (lane >> 5), bytes 32 * ((lane >> 4) & 1) of that half
+    // A lane's 32 bytes of a fragment (row lane & 15 of a 16-row tile) are
+    // global chunks (lane >> 4) and 4 + (lane >> 4) of the row: the same K
+    // order in both operands, so the MFMA still sums the slice's 128 products
+    // of every (row, column); the two reads hit distinct bank groups
+    // (line_swz).  off0 is opaque so that no part of it is kept apart.
     const int fr = lane & 15;
-    const unsigned lane_off = (lane >> 5) * GROUP + BOFF[fr >> 2] + 64 * (fr & 3) + 32 * ((lane >> 4) & 1);
-    auto tile_off = [&](int tau) { return (unsigned)((tau >> 2) * 2 * GROUP + 256 * (tau & 3)) + lane_off; };
+    unsigned off0 = 128 * fr + 16 * ((lane >> 4) ^ line_swz(fr));
+    asm volatile("" : "+v"(off0));
 
     const int ntile_valid = (valid + 15) >> 4;
     int n_i = 0;
@@ -246,46 +252,47 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // fragments and row scales of one slice
+    // Fragments and row scales of one slice.  The MFMAs take the W fragment
+    // as their first operand, so the tile comes out transposed: lane l holds
+    // row l & 15 of its 16-row tile and 4 consecutive columns 4 (l >> 4) + v,
+    // and one activation scale per tile covers all four.
     i32x8 bfr[TN], afr[TM];
-    f32x4 sa[TM];
-    const int crow = (lane >> 4) * 4;
-    auto read_frags = [&](int stage) {
-        const unsigned char* st = smem + stage * STAGE_BYTES;
-        const float* sa_l = (const float*)(st + SA_OFF);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const unsigned char* f = st + A_BYTES + tile_off(4 * wn + j);
-            const u32x4 lo = *(const u32x4*)f, hi = *(const u32x4*)(f + 16);
-            bfr[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i < n_i) {
-                const int tile = wm + 2 * i;
-                const unsigned char* f = st + tile_off(tile);
-                const u32x4 lo = *(const u32x4*)f, hi = *(const u32x4*)(f + 16);
-                afr[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sa[i] = *(const f32x4*)(sa_l + 16 * tile + crow);
-            }
-        }
+    float sa[TM];
+    const int quad4 = 4 * (lane >> 4);
+    auto read_frag = [&](const unsigned char* f) {
+        const u32x4 lo = *(const u32x4*)(f + off0), hi = *(const u32x4*)(f + (off0 ^ 64u));
+        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
+    auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * STAGE_BYTES; };
+    auto read_a = [&](int kt, int i) { afr[i] = read_frag(stage_ptr(kt) + 2048 * (wm + 2 * i)); };
+    auto read_sa = [&](int kt, int i) {
+        sa[i] = ((const float*)(stage_ptr(kt) + SA_OFF))[16 * (wm + 2 * i) + fr];
+    };
+    auto read_b = [&](int kt, int j) { bfr[j] = read_frag(stage_ptr(kt) + A_BYTES + 2048 * (4 * wn + j)); };
 
     // Slice s sits in stage s % STAGES.  Step kt multiplies slice kt from
     // registers; its stage then takes slice kt + STAGES (its fragments were
-    // read during step kt-1), and the fragments of slice kt+1 are read into
-    // the same registers once this step's MFMAs have been issued, so the LDS
-    // latency overlaps the MFMAs.  The DMAs sit between the MFMA groups:
-    // issued in one burst after the barrier they queue at the wave's issue
-    // and hold back its MFMAs.  Clamped re-reads past the end keep the DMA
-    // count per step fixed, which the waits rely on.
+    // read during step kt-1).  Slice kt+1 has landed when step kt starts, so
+    // its fragments are read during step kt, each as soon as its register
+    // is free: a tile's A fragment right after the tile's MFMAs are issued,
+    // its row scale after its products are scaled, and the W fragments after
+    // the last tile's MFMAs (reading them all after the MFMAs, as a block,
+    // serialised the LDS reads with the MFMAs: 1.72 against 1.38 ms for the
+    // first projection at the Step-5 prefill).
+    // The DMAs sit between the MFMA groups: issued in one burst after the
+    // barrier they queue at the wave's issue and hold back its MFMAs.
+    // Clamped re-reads past the end keep the DMA count per step fixed, which
+    // the waits rely on.
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
 #pragma unroll
         for (int q = 0; q < 7; ++q) issue_q(min(s, KB - 1), s, q);
     if (wave < 2) wait_vm<7 * (STAGES - 1)>(); else wait_vm<6 * (STAGES - 1)>();
     __builtin_amdgcn_s_barrier();
-    read_frags(0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) read_b(0, j);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) { read_a(0, i); read_sa(0, i); }
 
     for (int kt = 0; kt < KB; ++kt) {
         // slice kt+1 has landed (at most slice kt+2's DMAs outstanding), and
@@ -294,6 +301,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0), vmcnt/expcnt untouched
         __builtin_amdgcn_s_barrier();
         const int kn = min(kt + STAGES, KB - 1), sn = kt % STAGES;
+        const int kt1 = min(kt + 1, KB - 1);      // (the last step re-reads its own slice; unused)
 
         if ((kt & 63) == 0 && kt > 0) {
             swa_v = kt + lane < KB ? swa_p[kt + lane] : 0.f;
@@ -304,16 +312,14 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         const float swb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swb_v), kt & 63));
         // The MFMAs of 16-row tile i go to temporaries; tile i-1's results
         // are scaled and added while they run (so no MFMA result is consumed
-        // right after issue), and the DMAs sit between the groups.  The next
-        // slice's fragments are read after the last group is issued; the last
-        // tile's results are scaled after that, with its row scales kept.
+        // right after issue).  The reads are unconditional (a branch around
+        // them costs more than the LDS bytes of tiles past the valid rows).
         f32x4 r[2][TN];
-        f32x4 sa_last = sa[TM - 1];
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        auto scale_add = [&](int i, const f32x4* ri, f32x4 sai) {
-            const f32x4 sga = sai * swa, sgb = sai * swb;
+        auto scale_add = [&](int i) {
+            const float sga = sa[i] * swa, sgb = sa[i] * swb;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] += ri[j] * ((MODE == SWIGLU && j >= TN / 2) ? sgb : sga);
+            for (int j = 0; j < TN; ++j) acc[i][j] += r[i & 1][j] * ((MODE == SWIGLU && j >= TN / 2) ? sgb : sga);
         };
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -323,55 +329,61 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     // E8M0 scale 127 = 1.0 on both operands; the fp32 block scales follow
-                    r[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr[i], bfr[j], z, 0, 0, 0, 127, 0, 127);
+                    r[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr[i], z, 0, 0, 0, 127, 0, 127);
             }
-            if (i > 0 && i - 1 < n_i) scale_add(i - 1, r[(i - 1) & 1], sa[i - 1]);
+            read_a(kt1, i);
+            if (i == TM - 1) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) read_b(kt1, j);
+            }
+            if (i > 0 && i - 1 < n_i) scale_add(i - 1);
+            if (i > 0) read_sa(kt1, i - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < KB) read_frags((kt + 1) % STAGES);
-        if (TM - 1 < n_i) scale_add(TM - 1, r[(TM - 1) & 1], sa_last);
+        if (TM - 1 < n_i) scale_add(TM - 1);
+        read_sa(kt1, TM - 1);
     }
     wait_vm<0>();
 
-    const int ccol = lane & 15;
     if (MODE == SWIGLU) {
-        // this wave's h: rows of tiles wm + 2i, h columns 32 wn + 16 j + ccol (j < 2)
+        // this wave's h: rows 16 (wm + 2i) + fr, h columns 32 wn + 16 j + quad4 + v (j < 2)
         float hv[TM][2][4];
         float* amax_l = (float*)smem;                          // [128 rows][4 waves along N]
         __syncthreads();                                       // every wave is done with the ring
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            float m = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float m = 0.f;
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    hv[i][j][v] = swiglu_clip(acc[i][j][v], acc[i][j + 2][v], p.limit);
+                for (int v = 0; v < 4; ++v) {
+                    hv[i][j][v] = swiglu_clip_fast(acc[i][j][v], acc[i][j + 2][v], p.limit);
                     m = fmaxf(m, fabsf(hv[i][j][v]));
                 }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));   // the row's 16 lanes
-                if (ccol == 0) amax_l[(16 * (wm + 2 * i) + crow + v) * 4 + wn] = m;
-            }
+            m = fmaxf(m, __shfl_xor(m, 16, kWave));             // the row's 4 lanes
+            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            if (quad4 == 0) amax_l[(16 * (wm + 2 * i) + fr) * 4 + wn] = m;
+        }
         __syncthreads();
         uint8_t* Hq = (uint8_t*)p.C;
         const int kb = n_tile;                                  // K block of the second projection
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if (i >= n_i) continue;
+            const int lr = 16 * (wm + 2 * i) + fr;
+            const f32x4 m4 = *(const f32x4*)(amax_l + lr * 4);
+            const float amax = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
+            const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+            const float rs = 1.0f / s;
+            if (lr < valid) {
+                if (wn == 0 && quad4 == 0) p.Cs[(int64_t)kb * p.c_ld + row0 + lr] = s;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int lr = 16 * (wm + 2 * i) + crow + v;
-                const f32x4 m4 = *(const f32x4*)(amax_l + lr * 4);
-                const float amax = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
-                const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-                if (lr < valid) {
-                    if (wn == 0 && ccol == 0) p.Cs[(int64_t)kb * p.c_ld + row0 + lr] = s;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int hcol = n_tile * (BN / 2) + 32 * wn + 16 * j + ccol;
-                        if (hcol < p.N) Hq[(int64_t)(row0 + lr) * p.N + hcol] = (uint8_t)to_e4m3(hv[i][j][v] / s);
-                    }
+                for (int j = 0; j < 2; ++j) {
+                    const int hcol = n_tile * (BN / 2) + 32 * wn + 16 * j + quad4;
+                    if (hcol < p.N)
+                        *(uint32_t*)(Hq + (int64_t)(row0 + lr) * p.N + hcol) =
+                            to_e4m3(hv[i][j][0] * rs) | (to_e4m3(hv[i][j][1] * rs) << 8) |
+                            (to_e4m3(hv[i][j][2] * rs) << 16) | (to_e4m3(hv[i][j][3] * rs) << 24);
                 }
             }
         }
@@ -382,42 +394,43 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
         float* red = (float*)smem;                              // [128 rows][4 waves along N]
         __syncthreads();                                       // every wave is done with the ring
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            const int lr = 16 * (wm + 2 * i) + fr;
+            float m = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int lr = 16 * (wm + 2 * i) + crow + v;
-                float m = 0.f;
+            for (int j = 0; j < TN; ++j) {
+                const int col = n_tile * BN + 64 * wn + 16 * j + quad4;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = n_tile * BN + 64 * wn + 16 * j + ccol;
+                for (int v = 0; v < 4; ++v)
                     if (i < n_i && lr < valid && col < p.N) m = fmaxf(m, fabsf(acc[i][j][v]));
-                }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));   // the row's 16 lanes
-                if (ccol == 0) red[lr * 4 + wn] = m;
             }
+            m = fmaxf(m, __shfl_xor(m, 16, kWave));             // the row's 4 lanes
+            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            if (quad4 == 0) red[lr * 4 + wn] = m;
+        }
         __syncthreads();
         const int gw = wn & ~1;                                 // first wave of this wave's group
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if (i >= n_i) continue;
+            const int lr = 16 * (wm + 2 * i) + fr;
+            if (lr >= valid) continue;
+            const int ex = yrow_exp(fmaxf(red[lr * 4 + gw], red[lr * 4 + gw + 1]));
+            const float sc = exp2_int(-ex);
+            char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int lr = 16 * (wm + 2 * i) + crow + v;
-                if (lr >= valid) continue;
-                const int ex = yrow_exp(fmaxf(red[lr * 4 + gw], red[lr * 4 + gw + 1]));
-                const float sc = exp2_int(-ex);
-                char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = n_tile * BN + 64 * wn + 16 * j + ccol;
-                    if (col < p.N) *(_Float16*)(row + 2 * col) = (_Float16)(acc[i][j][v] * sc);
+            for (int j = 0; j < TN; ++j) {
+                const int col = n_tile * BN + 64 * wn + 16 * j + quad4;
+                if (col < p.N) {
+                    const f16x4 o = {(_Float16)(acc[i][j][0] * sc), (_Float16)(acc[i][j][1] * sc),
+                                     (_Float16)(acc[i][j][2] * sc), (_Float16)(acc[i][j][3] * sc)};
+                    *(f16x4*)(row + 2 * col) = o;
                 }
-                const int gcol = n_tile * BN + 64 * gw;
-                if (wn == gw && ccol == 0 && gcol < p.N) {
-                    row[2 * p.N + (gcol >> 7)] = (char)ex;
-                    if (gcol == 0) yrow_zero_pad(row, p.N);
-                }
+            }
+            const int gcol = n_tile * BN + 64 * gw;
+            if (wn == gw && quad4 == 0 && gcol < p.N) {
+                row[2 * p.N + (gcol >> 7)] = (char)ex;
+                if (gcol == 0) yrow_zero_pad(row, p.N);
             }
         }
     }
@@ -492,6 +505,7 @@ hipError_t launch_fp8_up(const void* xq, const float* xs, int xs_ld, const int32
     p.groups = groups;
     p.n_tiles = (2 * N) / f8::BN;
     if (max_tiles <= 0) return hipSuccess;
+    if ((int64_t)a_nrows * K > UINT32_MAX || (int64_t)2 * N * K > UINT32_MAX) return hipErrorInvalidValue;
     if (items) {
         const hipError_t e = launch_item_table(offsets, tile_start, groups, 0, p.n_tiles, false, items, s);
         if (e != hipSuccess) return e;
@@ -525,6 +539,7 @@ hipError_t launch_fp8_down(const void* hq, const float* hs, int hs_ld, int rows,
     p.groups = groups;
     p.n_tiles = (N + f8::BN - 1) / f8::BN;
     if (max_tiles <= 0) return hipSuccess;
+    if ((int64_t)rows * K > UINT32_MAX || (int64_t)N * K > UINT32_MAX) return hipErrorInvalidValue;
     if (items) {
         const hipError_t e = launch_item_table(offsets, tile_start, groups, 0, p.n_tiles, false, items, s);
         if (e != hipSuccess) return e;

@@ -56,6 +56,19 @@ __device__ __forceinline__ void yrow_zero_pad(char* row, int H) {
 // 2^e for e in [-126, 127]
 __device__ __forceinline__ float exp2_int(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
+// 16-byte chunk swizzle of row r (r & 15) of a tile held as 128-byte LDS
+// rows (one K slice per row, a DMA of whole lines): LDS chunk p holds global
+// chunk p ^ line_swz(r).  Chosen by search so that the fragment reads (lane
+// l: row l & 15, chunk (l >> 4) or 4 + (l >> 4)) hit distinct 16-byte bank
+// groups under every LDS service order that fits the bank-conflict
+// counter's readings on both this and the 64-row layout of the bf16 tiles
+// (8 lanes per cycle over 256 bytes; lanes l, l+16, l+32, l+48 together over
+// 128 or 256 bytes; 32 lanes over 512 bytes).  The simpler 2 ((r & 15) >> 2)
+// is conflict-free only under the last and measured 2-way.
+__device__ __forceinline__ int line_swz(int r) {
+    return ((((r ^ (r >> 1) ^ (r >> 3)) & 1) << 2) | (((r >> 2) & 1) << 1));
+}
+
 // The router's K order from 512 tokens: the 64-token tile m adds its K
 // chunks of 256 (8 slices of 32) starting at chunk router_chunk_rot(m, nc)
 // of nc, wrapping around, slices in order inside a chunk.  Tiles start at
