@@ -44,6 +44,7 @@
 //     list.  256-row launches read each item's (expert, first row, rows,
 //     n-tile) from a table a one-block launch writes first (one load instead
 //     of a binary search over the tile plan: 2.10 -> 2.02 ms).
+#include <type_traits>
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -135,6 +136,14 @@ __device__ __forceinline__ void dma_frag(const void* g, unsigned lds_off) {
 // the same from a wave-uniform 64-bit base plus this lane's 32-bit byte offset
 __device__ __forceinline__ void dma_frag_s(const void* base, unsigned off, unsigned lds_off) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(off), "s"(base) : "memory");
+}
+
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (two lane-swap moves, VALU only)
+__device__ __forceinline__ float max_lanes_xor16_32(float m) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding
@@ -625,44 +634,48 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
             // scaled fp16 rows straight from the registers: a wave's 128
             // columns are one exponent group, so a row's largest magnitude
             // is the max over the lane's 32 values and its 3 sibling lanes
-            // (staged through LDS as the fp32 output is, with its bank
-            // conflicts, the second projection took 1.33 ms against 1.21 ms
-            // at the Step-5 prefill)
+            // (lane swaps, no LDS).  Staged through LDS as the fp32 output
+            // is, with its bank conflicts, the second projection took
+            // 1.33 ms against 1.21 ms at the Step-5 prefill.  A wave whose
+            // columns all lie inside N stores without per-column checks.
+            const int c0 = n_tile * BN + S::GW * wn;
+            auto epi = [&](auto full_tag) {
+                constexpr bool full = decltype(full_tag)::value;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (i >= n_i) continue;
-                const int lr = 16 * (wm + S::WM * i) + lrow;
-                float m = 0.f;
+                for (int i = 0; i < TM; ++i) {
+                    if (i >= n_i) continue;
+                    const int lr = 16 * (wm + S::WM * i) + lrow;
+                    float m = 0.f;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = n_tile * BN + S::GW * wn + 16 * j + lcol;
+                    for (int j = 0; j < TN; ++j) {
+                        const int col = c0 + 16 * j + lcol;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (col + v < p.N) m = fmaxf(m, fabsf(acc[i][j][v]));
-                }
-                m = fmaxf(m, __shfl_xor(m, 16, kWave));
-                m = fmaxf(m, __shfl_xor(m, 32, kWave));
-                if (lr >= valid) continue;
-                const int ex = yrow_exp(m);
-                const float sc = exp2_int(-ex);
-                char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
+                        for (int v = 0; v < 4; ++v)
+                            if (full || col + v < p.N) m = fmaxf(m, fabsf(acc[i][j][v]));
+                    }
+                    m = max_lanes_xor16_32(m);
+                    if (lr >= valid) continue;
+                    const int ex = yrow_exp(m);
+                    const float sc = exp2_int(-ex);
+                    char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = n_tile * BN + S::GW * wn + 16 * j + lcol;
-                    if (col < p.N) {
-                        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-                        f16x4 h4;
+                    for (int j = 0; j < TN; ++j) {
+                        const int col = c0 + 16 * j + lcol;
+                        if (full || col < p.N) {
+                            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+                            f16x4 h4;
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) h4[v] = (_Float16)(acc[i][j][v] * sc);
-                        *(f16x4*)(row + 2 * col) = h4;
+                            for (int v = 0; v < 4; ++v) h4[v] = (_Float16)(acc[i][j][v] * sc);
+                            *(f16x4*)(row + 2 * col) = h4;
+                        }
+                    }
+                    if (lcol == 0 && c0 < p.N) {
+                        row[2 * p.N + (c0 >> 7)] = (char)ex;
+                        if (c0 == 0) yrow_zero_pad(row, p.N);
                     }
                 }
-                const int c0 = n_tile * BN + S::GW * wn;
-                if (lcol == 0 && c0 < p.N) {
-                    row[2 * p.N + (c0 >> 7)] = (char)ex;
-                    if (c0 == 0) yrow_zero_pad(row, p.N);
-                }
-            }
+            };
+            if (c0 + S::GW <= p.N) epi(std::true_type{}); else epi(std::false_type{});
         } else if (!is_swiglu(MODE)) {
             // plain fp32 output: through LDS, EPI_ROWS rows at a time (16-byte
             // writes of each lane's 4 columns), then whole rows, 16 bytes per
