@@ -360,8 +360,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
                     hv[i][j][v] = swiglu_clip_fast(acc[i][j][v], acc[i][j + 2][v], p.limit);
                     m = fmaxf(m, fabsf(hv[i][j][v]));
                 }
-            m = fmaxf(m, __shfl_xor(m, 16, kWave));             // the row's 4 lanes
-            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            m = max_lanes_xor16_32(m);                          // the row's 4 lanes
             if (quad4 == 0) amax_l[(16 * (wm + 2 * i) + fr) * 4 + wn] = m;
         }
         __syncthreads();
@@ -404,8 +403,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
                 for (int v = 0; v < 4; ++v)
                     if (i < n_i && lr < valid && col < p.N) m = fmaxf(m, fabsf(acc[i][j][v]));
             }
-            m = fmaxf(m, __shfl_xor(m, 16, kWave));             // the row's 4 lanes
-            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            m = max_lanes_xor16_32(m);                          // the row's 4 lanes
             if (quad4 == 0) red[lr * 4 + wn] = m;
         }
         __syncthreads();

@@ -138,14 +138,6 @@ __device__ __forceinline__ void dma_frag_s(const void* base, unsigned off, unsig
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(off), "s"(base) : "memory");
 }
 
-// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (two lane-swap moves, VALU only)
-__device__ __forceinline__ float max_lanes_xor16_32(float m) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 // wait until at most n vector-memory operations of this wave are outstanding
 template <int n>
 __device__ __forceinline__ void wait_vm() {

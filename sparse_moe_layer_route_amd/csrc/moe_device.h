@@ -110,6 +110,14 @@ __device__ __forceinline__ void swiglu_clip_grad(float g, float u, float L, floa
     }
 }
 
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (two lane-swap moves, VALU only)
+__device__ __forceinline__ float max_lanes_xor16_32(float m) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
