@@ -107,27 +107,34 @@ def up_kernel_flops(wl):
     return 2 * rows * 2 * c.moe_intermediate_size * c.hidden_size
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "routed_gemms_bf16_step5_prefill_counters.md")
-KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_layer_route_amd", "csrc",
-                          "grouped_gemm.hip")
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# workload -> (counter summary under profiles/, source of the kernel it measures)
+TRAFFIC_FILES = {
+    "step5_prefill": (os.path.join(_HERE, "profiles", "routed_gemms_bf16_step5_prefill_counters.md"),
+                      os.path.join(_HERE, "sparse_moe_layer_route_amd", "csrc", "grouped_gemm.hip")),
+    "step5_fp8_prefill": (os.path.join(_HERE, "profiles", "routed_gemms_fp8_step5_prefill_counters.md"),
+                          os.path.join(_HERE, "sparse_moe_layer_route_amd", "csrc", "fp8_gemm.hip")),
+}
 
 
 def counter_traffic(wl):
     """HBM bytes per launch of the first projection from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a plain copy's
-    counts), or None when the summary is for another workload or the kernel
+    counts), or None when there is no summary for the workload or the kernel
     source has changed since the counters were taken."""
     import hashlib
     import re
-    if wl.name != "step5_prefill" or not os.path.exists(TRAFFIC_FILE):
+    if wl.name not in TRAFFIC_FILES:
         return None
-    text = open(TRAFFIC_FILE).read()
+    summary, src = TRAFFIC_FILES[wl.name]
+    if not os.path.exists(summary):
+        return None
+    text = open(summary).read()
     t = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
     h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})", text, re.M)
     if not t or not h:
         return None
-    if hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest() != h.group(1):
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != h.group(1):
         return None
     return int(t.group(1))
 
@@ -202,7 +209,7 @@ def main():
         fl = layer_flops(wf, rf["touched"])
         rep["fp8_mfma_frac"] = fl / (rf["ms_step"] * 1e-3) / FP8_PEAK
         res["fp8"] = dict(rep, workload=wf.name, experts_touched=rf["touched"],
-                          first_projection=up_roofline(wf, rf, peaks, None))
+                          first_projection=up_roofline(wf, rf, peaks, counter_traffic(wf)))
 
     if not args.no_balanced:
         note(f"{wl.name} with the static balanced routing")

@@ -73,3 +73,18 @@ def test_fp8_layer_bytes_count_block_scales():
     scales = touched * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)) * 4
     want = touched * 18 * MIB + scales + 36 * MIB + E * H * 2 + E * 4 + T * H * 2 + T * H * 4
     assert bench.layer_bytes(wl, touched) == want
+
+
+def test_counter_summaries_carry_traffic_and_source_hash():
+    """Each committed counter summary that bench.py reads for `traffic` names
+    the bytes per launch and the SHA-256 of the kernel source it was taken
+    on (bench.py reports the bytes only while that source is unchanged)."""
+    import re
+    for name, (summary, src) in bench.TRAFFIC_FILES.items():
+        assert name in mi.WORKLOADS
+        text = open(summary).read()
+        t = re.search(r"^traffic_bytes_per_launch:\s*(\d+)$", text, re.M)
+        h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})$", text, re.M)
+        assert t and h, summary
+        assert 1e9 < int(t.group(1)) < 2e10
+        assert os.path.exists(src)
