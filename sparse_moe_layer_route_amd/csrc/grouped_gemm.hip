@@ -336,102 +336,121 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         // waits for every DMA in flight (vmcnt 0)
         asm volatile("" : "+v"(off0));
         const unsigned off1 = off0 ^ 64u;         // chunk 4 + c: (c ^ sw) ^ 4
-        bf16x8 xa[TM], xb[TN], ya[TM], yb[TN];
-        auto read_frags = [&](int kt, unsigned off, bf16x8* a, bf16x8* b) {
-            const unsigned char* sa = smem + (kt & 1) * A_BYTES;
-            const unsigned char* sb = smem + 2 * A_BYTES + (kt % 3) * B_BYTES;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8*)(sb + 2048 * (wn * TN + j) + off);
-#pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off);
-        };
-        // Slice kt's A sits in stage kt % 2, its W in stage kt % 3.  Step kt
-        // multiplies the slice's two K halves; between them (its reads done,
-        // slice kt+1 landed) the barrier frees its stages, which take A of
-        // kt+2 and W of kt+3 (clamped re-reads past the end keep the DMA count
-        // per step fixed, which the waits rely on).  DMAs complete in order and
-        // the last ones issued before step kt's wait are the previous step's
-        // A of kt+1, then W of kt+2: at most NQB outstanding means A and W of
-        // slice kt+1 have landed.
-        issue_a(0, 0);
-        issue_b(0, 0);
-        issue_a(min(1, nk - 1), 1);
-        issue_b(min(1, nk - 1), 1);
-        issue_b(min(2, nk - 1), 2);
-        if (a_mine) wait_vm<2 * NQB + NQA>(); else wait_vm<2 * NQB>();
-        __builtin_amdgcn_s_barrier();
-        read_frags(0, off0, xa, xb);
-        // The MFMAs take the W fragment as their first operand, so the tile
-        // comes out transposed: lane l holds row l & 15 and 4 consecutive
-        // columns, which the epilogue stores as whole 8- or 16-byte pieces.
-        // Each half step runs its MFMAs in TM groups (one 16-row tile each)
-        // and puts this wave's memory instructions between the groups: the
-        // LDS reads of the other half's fragments, and after the barrier two
-        // DMAs per group (A in the first half of the groups, W in the
-        // second).  Issued in one burst they queue at the wave's issue (the
-        // address and LDS units take one instruction at a time from all
-        // waves) and hold back its MFMAs.
-        static_assert(TM == NQA && TM == NQB && TM % 2 == 0 && TN % TM == 0, "two DMAs per 16-row tile group");
-        constexpr int JG = TN / TM;               // W fragments read per group
-        for (int kt = 0; kt < nk; ++kt) {
-            {
+        // The loop is compiled once per count of this wave's valid 16-row
+        // tiles (0..TM): a wave reads only the fragments its MFMAs use,
+        // with no branch inside the loop (a branch around the reads breaks
+        // the interleaved schedule).
+        auto kloop = [&](auto ni_tag) {
+            constexpr int NI = decltype(ni_tag)::value;
+            bf16x8 xa[TM], xb[TN], ya[TM], yb[TN];
+            auto read_frags = [&](int kt, unsigned off, bf16x8* a, bf16x8* b) {
                 const unsigned char* sa = smem + (kt & 1) * A_BYTES;
                 const unsigned char* sb = smem + 2 * A_BYTES + (kt % 3) * B_BYTES;
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    ya[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off1);
+                for (int j = 0; j < TN; ++j)
+                    if (NI > 0) b[j] = *(const bf16x8*)(sb + 2048 * (wn * TN + j) + off);
 #pragma unroll
-                    for (int jj = 0; jj < JG; ++jj)
-                        yb[JG * i + jj] = *(const bf16x8*)(sb + 2048 * (wn * TN + JG * i + jj) + off1);
-                    if (i < n_i) {
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], xa[i], acc[i][j], 0, 0, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            wait_vm<NQB>();                       // slice kt+1 has landed
-            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's reads of slice kt are done
+                for (int i = 0; i < TM; ++i)
+                    if (i < NI) a[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off);
+            };
+            // Slice kt's A sits in stage kt % 2, its W in stage kt % 3.  Step kt
+            // multiplies the slice's two K halves; between them (its reads done,
+            // slice kt+1 landed) the barrier frees its stages, which take A of
+            // kt+2 and W of kt+3 (clamped re-reads past the end keep the DMA count
+            // per step fixed, which the waits rely on).  DMAs complete in order and
+            // the last ones issued before step kt's wait are the previous step's
+            // A of kt+1, then W of kt+2: at most NQB outstanding means A and W of
+            // slice kt+1 have landed.
+            issue_a(0, 0);
+            issue_b(0, 0);
+            issue_a(min(1, nk - 1), 1);
+            issue_b(min(1, nk - 1), 1);
+            issue_b(min(2, nk - 1), 2);
+            if (a_mine) wait_vm<2 * NQB + NQA>(); else wait_vm<2 * NQB>();
             __builtin_amdgcn_s_barrier();
-            {
-                const int ka = min(kt + 2, nk - 1), kb = min(kt + 3, nk - 1);
-                const int ksa = ka + rot < nk ? ka + rot : ka + rot - nk;
-                const int ksb = kb + rot < nk ? kb + rot : kb + rot - nk;
-                const unsigned da = lds_base + (kt & 1) * A_BYTES + NQA * wave * 1024;
-                const unsigned db = lds_base + 2 * A_BYTES + (kt % 3) * B_BYTES + NQB * wave * 1024;
-                const unsigned char* sa = smem + ((kt + 1) & 1) * A_BYTES;
-                const unsigned char* sb = smem + 2 * A_BYTES + ((kt + 1) % 3) * B_BYTES;
-                const bool more = kt + 1 < nk;
+            read_frags(0, off0, xa, xb);
+            // The MFMAs take the W fragment as their first operand, so the tile
+            // comes out transposed: lane l holds row l & 15 and 4 consecutive
+            // columns, which the epilogue stores as whole 8- or 16-byte pieces.
+            // Each half step runs its MFMAs in TM groups (one 16-row tile each)
+            // and puts this wave's memory instructions between the groups: the
+            // LDS reads of the other half's fragments, and after the barrier two
+            // DMAs per group (A in the first half of the groups, W in the
+            // second).  Issued in one burst they queue at the wave's issue (the
+            // address and LDS units take one instruction at a time from all
+            // waves) and hold back its MFMAs.
+            static_assert(TM == NQA && TM == NQB && TM % 2 == 0 && TN % TM == 0, "two DMAs per 16-row tile group");
+            constexpr int JG = TN / TM;               // W fragments read per group
+            for (int kt = 0; kt < nk; ++kt) {
+                {
+                    const unsigned char* sa = smem + (kt & 1) * A_BYTES;
+                    const unsigned char* sb = smem + 2 * A_BYTES + (kt % 3) * B_BYTES;
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    // all A DMAs of the step before all W DMAs: the wait
-                    // above relies on W being the last NQB issued
-                    if (i < TM / 2) {
-                        if (a_mine) {
-                            dma_frag_s(a_base + ksa * BK2, a_off[2 * i], __builtin_amdgcn_readfirstlane(da + 2048 * i));
-                            dma_frag_s(a_base + ksa * BK2, a_off[2 * i + 1],
-                                       __builtin_amdgcn_readfirstlane(da + 2048 * i + 1024));
-                        }
-                    } else {
-                        const int q = 2 * (i - TM / 2);
-                        dma_frag_s(Wg + ksb * BK2, b_off(q), __builtin_amdgcn_readfirstlane(db + 1024 * q));
-                        dma_frag_s(Wg + ksb * BK2, b_off(q + 1), __builtin_amdgcn_readfirstlane(db + 1024 * (q + 1)));
-                    }
-                    if (more) {
-                        xa[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off0);
+                    for (int i = 0; i < TM; ++i) {
+                        if (i < NI) ya[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off1);
 #pragma unroll
                         for (int jj = 0; jj < JG; ++jj)
-                            xb[JG * i + jj] = *(const bf16x8*)(sb + 2048 * (wn * TN + JG * i + jj) + off0);
-                    }
-                    if (i < n_i) {
+                            if (NI > 0) yb[JG * i + jj] = *(const bf16x8*)(sb + 2048 * (wn * TN + JG * i + jj) + off1);
+                        if (i < NI) {
 #pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb[j], ya[i], acc[i][j], 0, 0, 0);
+                            for (int j = 0; j < TN; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], xa[i], acc[i][j], 0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+                }
+                wait_vm<NQB>();                       // slice kt+1 has landed
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's reads of slice kt are done
+                __builtin_amdgcn_s_barrier();
+                {
+                    const int ka = min(kt + 2, nk - 1), kb = min(kt + 3, nk - 1);
+                    const int ksa = ka + rot < nk ? ka + rot : ka + rot - nk;
+                    const int ksb = kb + rot < nk ? kb + rot : kb + rot - nk;
+                    const unsigned da = lds_base + (kt & 1) * A_BYTES + NQA * wave * 1024;
+                    const unsigned db = lds_base + 2 * A_BYTES + (kt % 3) * B_BYTES + NQB * wave * 1024;
+                    const unsigned char* sa = smem + ((kt + 1) & 1) * A_BYTES;
+                    const unsigned char* sb = smem + 2 * A_BYTES + ((kt + 1) % 3) * B_BYTES;
+                    const bool more = kt + 1 < nk;
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        // all A DMAs of the step before all W DMAs: the wait
+                        // above relies on W being the last NQB issued
+                        if (i < TM / 2) {
+                            if (a_mine) {
+                                dma_frag_s(a_base + ksa * BK2, a_off[2 * i],
+                                           __builtin_amdgcn_readfirstlane(da + 2048 * i));
+                                dma_frag_s(a_base + ksa * BK2, a_off[2 * i + 1],
+                                           __builtin_amdgcn_readfirstlane(da + 2048 * i + 1024));
+                            }
+                        } else {
+                            const int q = 2 * (i - TM / 2);
+                            dma_frag_s(Wg + ksb * BK2, b_off(q), __builtin_amdgcn_readfirstlane(db + 1024 * q));
+                            dma_frag_s(Wg + ksb * BK2, b_off(q + 1),
+                                       __builtin_amdgcn_readfirstlane(db + 1024 * (q + 1)));
+                        }
+                        if (more) {
+                            if (i < NI) xa[i] = *(const bf16x8*)(sa + 2048 * (wm + S::WM * i) + off0);
+#pragma unroll
+                            for (int jj = 0; jj < JG; ++jj)
+                                if (NI > 0)
+                                    xb[JG * i + jj] = *(const bf16x8*)(sb + 2048 * (wn * TN + JG * i + jj) + off0);
+                        }
+                        if (i < NI) {
+#pragma unroll
+                            for (int j = 0; j < TN; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb[j], ya[i], acc[i][j], 0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
+        };
+        switch (n_i) {
+            case 0: kloop(std::integral_constant<int, 0>{}); break;
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            default: kloop(std::integral_constant<int, TM>{}); break;
         }
         wait_vm<0>();
     } else {
