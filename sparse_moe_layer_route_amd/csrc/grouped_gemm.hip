@@ -138,6 +138,15 @@ __device__ __forceinline__ void dma_frag_s(const void* base, unsigned off, unsig
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(off), "s"(base) : "memory");
 }
 
+// two fp32 -> packed bf16 by the gfx950 conversion instruction (one
+// v_cvt_pk_bf16_f32, round to nearest even like f32_to_bf16; NaN stays NaN)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+    const bf16x2_t b = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
 // wait until at most n vector-memory operations of this wave are outstanding
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -635,7 +644,7 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                         float hh[4];
 #pragma unroll
                         for (int v = 0; v < 4; ++v) hh[v] = swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit);
-                        hv = make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
+                        hv = make_uint2(pack_bf16x2_hw(hh[0], hh[1]), pack_bf16x2_hw(hh[2], hh[3]));
                     }
                     *(uint2*)((uint16_t*)p.C + r * p.N + hcol) = hv;
                 }
