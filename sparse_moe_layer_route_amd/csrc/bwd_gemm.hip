@@ -337,7 +337,9 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
     // straight from registers, each instruction would write 64-byte pieces of
     // 4 rows.  Instead the tile goes to LDS EPI_ROWS rows at a time (the
     // operand stages are free by now), and each wave then writes whole rows
-    // with 16 bytes per lane.
+    // with 16 bytes per lane.  (The weight gradients written straight from a
+    // transposed tile, 16 bytes per lane in 64-byte row pieces, took the
+    // Step-5 prefill backward from 14.0 to 16.8 ms.)
     constexpr int EPI_ROWS = S::EPI_ROWS;
     constexpr int IPP = EPI_ROWS / 16 / WM;        // 16-row tiles of a wave per pass
     const int ccol = lane & 15, crow = (lane >> 4) * 4;
