@@ -265,11 +265,12 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         // 128-byte line of row q, so every request is a whole line (half the
         // L2 requests of 64-byte pieces for the same bytes).  A block lands at
         // LDS byte 16 l per lane l, i.e. rows of 128 B back to back; lane l
-        // reads the line's 16-byte chunk (l & 7) ^ line_swz(row), so LDS chunk p of
-        // a row holds global chunk p ^ line_swz(row).  A fragment read (lane l: row
-        // l & 15 of a 16-row tile, K chunk 4 sub + (l >> 4)) is then free of
-        // bank conflicts (see line_swz).  LDS: A in 2 stages, W in 3 (W is the operand
-        // that streams from HBM, so it gets the longer lead), 160 KiB.
+        // reads the line's 16-byte chunk (l & 7) ^ line_swz(row), so LDS
+        // chunk p of a row holds global chunk p ^ line_swz(row).  A fragment
+        // read (lane l: row l & 15 of a 16-row tile, K chunk 4 sub + (l >> 4))
+        // is then free of bank conflicts (see line_swz).  LDS: A in 2 stages,
+        // W in 3 (W is the operand that streams from HBM, so it gets the
+        // longer lead), 160 KiB.
         // Wave w moves A blocks 4w .. 4w+3 (rows 32w .. 32w+31) and W blocks
         // 4w .. 4w+3 of every slice.
         constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
@@ -315,7 +316,8 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
         }
         static_assert(NQB == 4 && S::GW == 128, "the W row formula assumes 32 columns per wave and slice");
         // chunk of even / odd q (tile column 8 (4 wave + q) + dq: row 8 (q & 1) + dq of its 16)
-        const unsigned b_chunk0 = 16u * ((lane & 7) ^ line_swz(dq)), b_chunk1 = 16u * ((lane & 7) ^ line_swz(8 + dq));
+        const unsigned b_chunk0 = 16u * ((lane & 7) ^ line_swz(dq));
+        const unsigned b_chunk1 = 16u * ((lane & 7) ^ line_swz(8 + dq));
         auto b_off = [&](int q) {
             const int wrow = w_add + min(w_base + 8 * q + dq, w_last);
             return (unsigned)wrow * (unsigned)(2 * K) + ((q & 1) ? b_chunk1 : b_chunk0);
