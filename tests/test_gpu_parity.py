@@ -355,6 +355,45 @@ def test_layer_rows_per_expert_at_tile_boundaries():
     assert err <= TOL_BF16
 
 
+# rows per expert at the boundaries of the 256-row tiles' per-wave counts of
+# valid 16-row tiles (wave wm holds tiles wm, wm+4, wm+8, wm+12: 1..4 of them,
+# or none), of the FP8 kernel's 128-row tiles, and of two and three m-tiles
+ROWS_AT_WAVE_TILE_BOUNDARIES = [1, 16, 17, 48, 49, 64, 65, 112, 128, 129, 192, 193, 240, 241, 255, 256, 257, 300,
+                                511, 512, 513, 1, 0, 0]
+
+
+@pytest.mark.parametrize("expert_dtype", ["bf16", "fp8"])
+def test_layer_rows_per_expert_at_wave_tile_boundaries(expert_dtype):
+    """Prefill-sized tiles (256 rows bf16, 128 rows FP8) with experts given
+    row counts at every boundary of a wave's valid 16-row tiles, through the
+    routed entry point; every token against the oracle with the same
+    choice."""
+    counts_want = ROWS_AT_WAVE_TILE_BOUNDARIES
+    E, k = len(counts_want), 4
+    T = sum(counts_want) // k
+    assert T * k == sum(counts_want) and max(counts_want) < T
+    kw = dict(T=T, num_experts=E, top_k=k, hidden_size=256, moe_intermediate_size=128 if expert_dtype == "fp8" else 256)
+    if expert_dtype == "fp8":
+        kw["expert_dtype"] = "fp8"
+    wl = mi.workload("tiny", **kw)
+    cfg = wl.cfg
+    flat = np.repeat(np.arange(E), counts_want)
+    ids_np = np.empty((T, k), dtype=np.int32)
+    for p_, e in enumerate(flat):
+        ids_np[p_ % T, p_ // T] = e
+    assert all(len(set(r)) == k for r in ids_np.tolist())
+    say(f"[layer_rows_per_expert_at_wave_tile_boundaries] {expert_dtype} T={T} E={E}")
+    inp = gpu_inputs(wl)
+    ids = torch.from_numpy(ids_np)
+    out, w, counts = run_routed(wl, inp, ids.to(DEV))
+    assert counts.cpu().tolist() == counts_want
+    ref = orc.layer(cfg, host(inp), ids_in=ids)
+    check_weights(w.cpu().numpy(), ref["w"])
+    err, rms = max_err_over_rms(out.float().cpu().numpy(), ref["out"])
+    say(f"  max_err/rms = {err:.3e} (rms {rms:.3e})")
+    assert err <= (TOL_FP8 if expert_dtype == "fp8" else TOL_BF16)
+
+
 @pytest.mark.parametrize("name", REPLAY_SMALL)
 def test_layer_replay_small(name):
     """A replayed choice that is not the router's (random distinct experts;
