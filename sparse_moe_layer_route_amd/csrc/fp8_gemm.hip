@@ -376,13 +376,24 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             const float rs = 1.0f / s;
             if (lr < valid) {
                 if (wn == 0 && quad4 == 0) p.Cs[(int64_t)kb * p.c_ld + row0 + lr] = s;
+                uint32_t code[2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int hcol = n_tile * (BN / 2) + 32 * wn + 16 * j + quad4;
-                    if (hcol < p.N)
-                        *(uint32_t*)(Hq + (int64_t)(row0 + lr) * p.N + hcol) =
-                            to_e4m3(hv[i][j][0] * rs) | (to_e4m3(hv[i][j][1] * rs) << 8) |
-                            (to_e4m3(hv[i][j][2] * rs) << 16) | (to_e4m3(hv[i][j][3] * rs) << 24);
+                for (int j = 0; j < 2; ++j)
+                    code[j] = to_e4m3(hv[i][j][0] * rs) | (to_e4m3(hv[i][j][1] * rs) << 8) |
+                              (to_e4m3(hv[i][j][2] * rs) << 16) | (to_e4m3(hv[i][j][3] * rs) << 24);
+                const int hc0 = n_tile * (BN / 2) + 32 * wn;
+                if (hc0 + 32 <= p.N) {
+                    // both h tiles through one lane swap: lanes with (lane >> 4)
+                    // even take 8 codes of tile 0, the odd ones 8 of tile 1
+                    const auto sw = __builtin_amdgcn_permlane16_swap(code[0], code[1], false, false);
+                    const int hcol = hc0 + 16 * ((lane >> 4) & 1) + 4 * ((lane >> 4) & ~1);
+                    *(uint2*)(Hq + (int64_t)(row0 + lr) * p.N + hcol) = make_uint2(sw[0], sw[1]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int hcol = hc0 + 16 * j + quad4;
+                        if (hcol < p.N) *(uint32_t*)(Hq + (int64_t)(row0 + lr) * p.N + hcol) = code[j];
+                    }
                 }
             }
         }
@@ -416,13 +427,31 @@ __global__ __launch_bounds__(NT, 1) void kernel(Params p) {
             const int ex = yrow_exp(fmaxf(red[lr * 4 + gw], red[lr * 4 + gw + 1]));
             const float sc = exp2_int(-ex);
             char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
+            const int wc0 = n_tile * BN + 64 * wn;
+            if (wc0 + 64 <= p.N) {
+                // tiles j and j+1 through one lane swap, 16 bytes per lane
+                // (the grouped bf16 kernel's second projection does the same)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = n_tile * BN + 64 * wn + 16 * j + quad4;
-                if (col < p.N) {
-                    const f16x4 o = {(_Float16)(acc[i][j][0] * sc), (_Float16)(acc[i][j][1] * sc),
-                                     (_Float16)(acc[i][j][2] * sc), (_Float16)(acc[i][j][3] * sc)};
-                    *(f16x4*)(row + 2 * col) = o;
+                for (int j = 0; j < TN; j += 2) {
+                    const f16x4 a4 = {(_Float16)(acc[i][j][0] * sc), (_Float16)(acc[i][j][1] * sc),
+                                      (_Float16)(acc[i][j][2] * sc), (_Float16)(acc[i][j][3] * sc)};
+                    const f16x4 b4 = {(_Float16)(acc[i][j + 1][0] * sc), (_Float16)(acc[i][j + 1][1] * sc),
+                                      (_Float16)(acc[i][j + 1][2] * sc), (_Float16)(acc[i][j + 1][3] * sc)};
+                    const uint2 a = __builtin_bit_cast(uint2, a4), b = __builtin_bit_cast(uint2, b4);
+                    const auto s0 = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+                    const int col = wc0 + 16 * (j + ((lane >> 4) & 1)) + 4 * ((lane >> 4) & ~1);
+                    *(uint4*)(row + 2 * col) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = wc0 + 16 * j + quad4;
+                    if (col < p.N) {
+                        const f16x4 o = {(_Float16)(acc[i][j][0] * sc), (_Float16)(acc[i][j][1] * sc),
+                                         (_Float16)(acc[i][j][2] * sc), (_Float16)(acc[i][j][3] * sc)};
+                        *(f16x4*)(row + 2 * col) = o;
+                    }
                 }
             }
             const int gcol = n_tile * BN + 64 * gw;

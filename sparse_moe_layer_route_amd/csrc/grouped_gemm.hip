@@ -621,7 +621,27 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
             const int lr = 16 * (wm + S::WM * i) + lrow;
             if (lr >= valid) continue;
             const int64_t r = row0 + lr;
-            if (is_swiglu(MODE)) {
+            const int hc0 = n_tile * (BN / 2) + (S::GW / 2) * wn;
+            if (MODE == SWIGLU && hc0 + S::GW / 2 <= p.N) {
+                // the wave's h columns all inside N: h tiles j and j+1 through
+                // one lane swap (as the second projection's rows below), 16
+                // bytes per lane
+#pragma unroll
+                for (int j = 0; j < TN / 2; j += 2) {
+                    float ha[4], hb[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        ha[v] = swiglu_clip(acc[i][j][v], acc[i][j + TN / 2][v], limit);
+                        hb[v] = swiglu_clip(acc[i][j + 1][v], acc[i][j + 1 + TN / 2][v], limit);
+                    }
+                    const auto s0 = __builtin_amdgcn_permlane16_swap(pack_bf16x2_hw(ha[0], ha[1]),
+                                                                     pack_bf16x2_hw(hb[0], hb[1]), false, false);
+                    const auto s1 = __builtin_amdgcn_permlane16_swap(pack_bf16x2_hw(ha[2], ha[3]),
+                                                                     pack_bf16x2_hw(hb[2], hb[3]), false, false);
+                    const int hcol = hc0 + 16 * (j + ((lane >> 4) & 1)) + 4 * ((lane >> 4) & ~1);
+                    *(uint4*)((uint16_t*)p.C + r * p.N + hcol) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                }
+            } else if (is_swiglu(MODE)) {
 #pragma unroll
                 for (int j = 0; j < TN / 2; ++j) {
                     const int hcol = n_tile * (BN / 2) + (S::GW / 2) * wn + 16 * j + lcol;
@@ -680,15 +700,41 @@ __device__ __forceinline__ void run_item(const Params& p, int w, unsigned char* 
                     const int ex = yrow_exp(m);
                     const float sc = exp2_int(-ex);
                     char* row = (char*)p.C + (int64_t)(row0 + lr) * p.c_row_bytes;
+                    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+                    if constexpr (full) {
+                        // tiles j and j+1 through one lane swap: lanes with
+                        // (lane >> 4) even take columns 4 (lane >> 4) .. +7 of
+                        // tile j, the odd ones the same 8 columns of tile
+                        // j+1, so each lane stores 16 bytes
+                        const bool odd = (lane >> 4) & 1;
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        const int col = c0 + 16 * j + lcol;
-                        if (full || col < p.N) {
-                            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-                            f16x4 h4;
+                        for (int j = 0; j < TN; j += 2) {
+                            f16x4 a4, b4;
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) h4[v] = (_Float16)(acc[i][j][v] * sc);
-                            *(f16x4*)(row + 2 * col) = h4;
+                            for (int v = 0; v < 4; ++v) {
+                                a4[v] = (_Float16)(acc[i][j][v] * sc);
+                                b4[v] = (_Float16)(acc[i][j + 1][v] * sc);
+                            }
+                            const uint2 a = __builtin_bit_cast(uint2, a4), b = __builtin_bit_cast(uint2, b4);
+                            const auto s0 = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+                            const auto s1 = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+                            // even rows of lanes keep their tile-j columns and take the
+                            // partner's next 4; odd rows take the partner's tile-(j+1)
+                            // columns before their own
+                            const uint4 q = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                            const int col = c0 + 16 * (j + (odd ? 1 : 0)) + 4 * ((lane >> 4) & ~1);
+                            *(uint4*)(row + 2 * col) = q;
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) {
+                            const int col = c0 + 16 * j + lcol;
+                            if (col < p.N) {
+                                f16x4 h4;
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) h4[v] = (_Float16)(acc[i][j][v] * sc);
+                                *(f16x4*)(row + 2 * col) = h4;
+                            }
                         }
                     }
                     if (lcol == 0 && c0 < p.N) {
