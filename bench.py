@@ -589,10 +589,13 @@ def calibrate_hot_bias(wl, moe, torch, mi, target=0.5, tol=0.02):
 
 def bench_decode(args, wl, moe, torch, peaks):
     """The decode layer call, one at a time: before each timed call an
-    untimed write of 1 GiB flushes the 256 MiB memory-side cache, so the
-    call streams its expert weights from HBM; the median of the per-call
-    HIP-event times.  The same for the call captured once in a HIP graph and
-    replayed."""
+    untimed read of a 1 GiB buffer fills the 256 MiB memory-side cache with
+    clean lines of other data (as the previous layer's weight reads would),
+    so the call streams its expert weights from HBM; the median of the
+    per-call HIP-event times.  The same for the call captured once in a HIP
+    graph and replayed.  Also reported: the median after a 1 GiB write
+    instead, which leaves the cache full of dirty lines whose write-back to
+    HBM then runs inside the timed call."""
     import moe_inputs as mi
     inp = mi.make_inputs(wl, "cuda", seed=0)
     T, k, E, H = wl.T, wl.cfg.top_k, wl.cfg.num_experts, wl.cfg.hidden_size
@@ -600,18 +603,22 @@ def bench_decode(args, wl, moe, torch, peaks):
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
     counts = torch.empty((E,), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_sum = torch.empty((), dtype=torch.float32, device="cuda")
     for _ in range(max(args.warmup, 3)):
         moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, expert_counts=counts, stream=stream)
     torch.cuda.synchronize()
     touched = int((counts > 0).sum().item())
     n = max(args.steps, 20)
 
-    def timed(fn):
+    def timed(fn, dirty=False):
         ts = []
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for _ in range(n):
-            flush.fill_(1)
+            if dirty:
+                flush.fill_(1.0)
+            else:
+                torch.sum(flush, dim=0, out=flush_sum)
             ev[0].record(stream)
             fn()
             ev[1].record(stream)
@@ -620,6 +627,7 @@ def bench_decode(args, wl, moe, torch, peaks):
         return median(ts)
 
     us = timed(lambda: moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, stream=stream))
+    us_dirty = timed(lambda: moe.moe_layer_forward(wl.cfg, inp, out=out, ws=ws, stream=stream), dirty=True)
     by = layer_bytes(wl, touched)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -633,12 +641,14 @@ def bench_decode(args, wl, moe, torch, peaks):
     g.replay()
     torch.cuda.synchronize()
     us_graph = timed(g.replay)
-    del g, inp, ws, flush
+    del g, inp, ws, flush, flush_sum
     torch.cuda.empty_cache()
     rep = {"workload": wl.name, "tokens": T, "experts_touched": touched, "us_per_step": us,
            "tokens_per_s": T / (us * 1e-6), "gbs": by / (us * 1e-6) / 1e9, "hbm_frac": by / (us * 1e-6) / HBM_PEAK,
            "us_per_step_graph": us_graph, "hbm_frac_graph": by / (us_graph * 1e-6) / HBM_PEAK,
-           "algorithmic_bytes": by, "timing": "median of %d calls, 1 GiB written before each (untimed)" % n}
+           "us_per_step_after_write_flush": us_dirty,
+           "algorithmic_bytes": by,
+           "timing": "median of %d calls, 1 GiB of other data read before each (untimed)" % n}
     if peaks:
         rep["hbm_frac_attainable"] = by / (us * 1e-6) / (peaks["hbm_gbs"] * 1e9)
     return rep
