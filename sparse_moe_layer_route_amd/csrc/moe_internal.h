@@ -93,7 +93,8 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool c_fp32, hipStream_t s)
 // K % 128 == 0, N % 128 == 0.
 int fp8_tile_m();
 hipError_t launch_quant_rows(const void* x, int rows, int H, void* xq, float* xs, int ld, hipStream_t s);
-// items (optional): grouped_item_bytes(max_tiles, n-tiles) of scratch for the work-item table
+// items (required; hipErrorInvalidValue when null): grouped_item_bytes(max_tiles, n-tiles) of
+// scratch for the work-item table, which the persistent grid walks
 hipError_t launch_fp8_up(const void* xq, const float* xs, int xs_ld, const int32_t* a_rows, int a_div,
                          int a_nrows, const void* w13, const float* w13s, void* hq, float* hs, int hs_ld, int N,
                          int K, float limit, const int32_t* offsets, const int32_t* tile_start, int groups,
