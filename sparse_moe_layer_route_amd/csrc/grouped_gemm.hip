@@ -1034,7 +1034,12 @@ void launch(Params p, int64_t tiles, hipStream_t s) {
                                              (int*)p.xcd_start, (int4*)p.items);
         if (!balance) p.xcd_start = nullptr;
     }
-    const int nb = grid_blocks(tiles * p.n_tiles);
+    // the second projection's 256-row items run on a persistent grid, one
+    // block per CU walking a stride of its XCD's items (1,150 -> 1,133 us at
+    // the Step-5 prefill: no block launch per item); the first projection's
+    // items differ too much in cost for a fixed stride and keep one block each
+    int nb = grid_blocks(tiles * p.n_tiles);
+    if (MODE == OUT_F16 && BM == 256 && p.offsets && nb > 256) nb = 256;
     if (p.offsets) kernel<MODE, true, BM, BN><<<nb, Shape<BM, BN>::NT, 0, s>>>(p);
     else kernel<MODE, false, BM, BN><<<nb, Shape<BM, BN>::NT, 0, s>>>(p);
 }
