@@ -725,7 +725,28 @@ FP8_SMALL = {
     "fp8_deep_k_66_blocks": dict(hidden_size=128 * 66, moe_intermediate_size=128, share_expert_dim=64, T=24,
                                  num_experts=4, top_k=2),
     "fp8_no_shared_bf16_out": dict(share_expert_dim=0, out_dtype="bf16", T=96),
+    # more work items than blocks, so blocks walk several: with 8 K blocks in
+    # both projections each item fetches the next one's first slices during
+    # its last steps (about 640 and 320 items)
+    "fp8_pipelined_items_k1024": dict(hidden_size=1024, moe_intermediate_size=1024, share_expert_dim=256, T=2400,
+                                      num_experts=16, top_k=4),
+    # the second projection's 4 K blocks are too few for that: its blocks
+    # walk about 1000 items one after the other, each with its own prologue
+    "fp8_unpipelined_items_k512": dict(hidden_size=2048, moe_intermediate_size=512, share_expert_dim=256, T=4000,
+                                       num_experts=8, top_k=4),
 }
+
+
+# cases whose launches must hold more 128-row work items than the 256 blocks
+# of the persistent grid (checked from the GPU's own expert counts)
+FP8_MULTI_ITEM = {"fp8_pipelined_items_k1024", "fp8_unpipelined_items_k512"}
+
+
+def fp8_items(cfg, counts):
+    """Work items of the FP8 first and second projections: 128-row m-tiles
+    times 256-column n-tiles (first: 2I gate/up columns, second: H)."""
+    tiles = int(sum((int(c) + 127) // 128 for c in counts))
+    return tiles * (2 * cfg.moe_intermediate_size // 256), tiles * ((cfg.hidden_size + 255) // 256)
 
 
 def fp8_workload(name):
@@ -741,6 +762,10 @@ def test_layer_fp8_small(name):
     inp = gpu_inputs(wl)
     inp["x"][0] = 0.0                               # an all-zero row: every group's scale is 1
     out, ids, w, counts = run_layer(wl, inp)
+    if name in FP8_MULTI_ITEM:
+        up_items, down_items = fp8_items(wl.cfg, counts.cpu().numpy())
+        say(f"  work items: {up_items} first projection, {down_items} second")
+        assert min(up_items, down_items) > 256
     h = host(inp)
     ref = orc.layer(wl.cfg, h)
     _, _, _, corr = orc.route(wl.cfg, h["x"], h["w_router"], h["router_bias"], want_scores=True)
